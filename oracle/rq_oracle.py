@@ -1,0 +1,287 @@
+"""Plain CPU oracle for the online rotate + INT4 + W4A4 hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+kernels, their headers or the Python binding; the two sides meet only through
+seeded input arrays.
+
+Pages cited (each function names the passage it follows):
+  [QuaRot]    aicassindra.com, QuaRot explainer ("Why architecture matters
+              here" / "The architecture: every piece explained" /
+              "End-to-end flow").
+  [RQ]        llms.blog, "Rotational Quantization: How Orthogonal Transforms
+              and Hadamard Incoherence Enable Outlier-Free Low-Bit Inference".
+  [SpinQuant] aicassindra.com, SpinQuant explainer (same three sections as
+              [QuaRot]).
+
+Notation (row vectors, [RQ] "The Principle of Computational Invariance"):
+  X is m x d (one token per row), W is d x k, Y = X W.
+  R = diag(s) . H_n / sqrt(n) with H_n the +-1 Sylvester matrix and s a
+  Rademacher sign vector.  Rotated activation  X~ = X R  (each row
+  x -> (x * s) H_n / sqrt(n));  folded weight  W~ = R^T W, stored as
+  W~^T = W^T R, i.e. the same row transform applied to each row of W^T.
+
+Two precisions:
+  "f64"  truth mode: every floating-point step in float64.
+  "f32"  mirror mode: the same steps in float32 (IEEE add/sub, no fused
+         multiply-add), butterflies in ascending-stride order, and the single
+         global scale applied as one multiply by fp32(1/sqrt(n)).  A GPU
+         kernel that keeps this stage order can be compared bit for bit on the
+         rotated activations, and its INT4 decisions are taken in the same
+         (fp32) precision.
+
+Quantizer (symmetric per row, codes in [-8, 7], nibble packed):
+  a = max_j |x~_j|;  scale = fp16_rne(a / 7);  q_j = clamp(rne(x~_j / scale),
+  -8, 7) with rne = round half to even; scale == 0 gives all-zero codes.
+  The scale that is stored (fp16) is the one that divides, so dequantisation
+  q * scale uses exactly the stored value.  Packing: byte i holds code 2i in
+  its low nibble and code 2i+1 in its high nibble, two's complement.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(explicit Sylvester matrices, scipy.linalg.hadamard, closed forms, brute force
+on tiny inputs, worked examples from the pages).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "hadamard_transform",
+    "rotate",
+    "fp16_rne",
+    "quantize_rows",
+    "pack_int4",
+    "unpack_int4",
+    "fwht_quant",
+    "fold_weights",
+    "w4a4_gemm",
+    "kv_rotate_quant",
+    "dequantize",
+]
+
+QMIN, QMAX = -8, 7
+
+
+def _check_pow2(n: int) -> None:
+    if n < 1 or (n & (n - 1)) != 0:
+        raise ValueError(f"rotation length must be a power of two, got {n}")
+
+
+def hadamard_transform(u: np.ndarray) -> np.ndarray:
+    """Unnormalised fast Walsh-Hadamard transform along the last axis.
+
+    [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms",
+    part 2 (online FWHT): the butterfly exploits the recursive Kronecker
+    structure of the Sylvester matrix, costs O(n log2 n) and uses only
+    additions and subtractions.  [RQ] "Incoherence Processing via Randomized
+    Hadamard Transforms", recursion H_2k = [[H_k, H_k], [H_k, -H_k]] (here
+    without the 1/sqrt(2) per level; the one global scale is applied by the
+    caller).  Natural (Sylvester) ordering: output j = sum_i (-1)^popcount(i&j)
+    u_i.  Stages run in ascending stride h = 1, 2, ..., n/2; at each stage the
+    pair (a, b) at positions (i, i + h), bit h of i clear, becomes
+    (a + b, a - b).  The dtype of ``u`` is kept, so float32 input is computed
+    with float32 rounding after every add/sub.
+    """
+    out = np.array(u, copy=True)
+    n = out.shape[-1]
+    _check_pow2(n)
+    lead = out.shape[:-1]
+    h = 1
+    while h < n:
+        v = out.reshape(lead + (n // (2 * h), 2, h))
+        a = v[..., 0, :].copy()
+        b = v[..., 1, :].copy()
+        v[..., 0, :] = a + b
+        v[..., 1, :] = a - b
+        h *= 2
+    return out
+
+
+def _inv_sqrt_f32(n: int) -> np.float32:
+    """fp32(1/sqrt(n)): the float64 value rounded once to float32."""
+    return np.float32(1.0 / np.sqrt(np.float64(n)))
+
+
+def rotate(x: np.ndarray, signs: np.ndarray | None, precision: str = "f64") -> np.ndarray:
+    """Row-wise randomized Hadamard rotation x -> (x * s) H_n / sqrt(n).
+
+    [RQ] "Incoherence Processing via Randomized Hadamard Transforms": the
+    randomized Hadamard transform multiplies by a Rademacher sign diagonal and
+    the Sylvester matrix; the normalised matrix has entries +-1/sqrt(n).
+    [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms": the
+    butterflies use only add/sub and one global scalar multiplication at the
+    end.  The sign diagonal comes first (x * s, then H), the order in which
+    the rotated linear layer is specified; the fold below uses the same R.
+    ``signs=None`` means s = 1 (plain H_n / sqrt(n)).
+    """
+    x = np.asarray(x)
+    n = x.shape[-1]
+    _check_pow2(n)
+    if precision == "f64":
+        u = x.astype(np.float64)
+        if signs is not None:
+            u = u * np.asarray(signs).astype(np.float64)
+        return hadamard_transform(u) / np.sqrt(np.float64(n))
+    if precision == "f32":
+        u = x.astype(np.float32)
+        if signs is not None:
+            u = u * np.asarray(signs).astype(np.float32)  # exact: s = +-1
+        y = hadamard_transform(u)
+        return (y * _inv_sqrt_f32(n)).astype(np.float32)
+    raise ValueError(f"precision must be 'f64' or 'f32', got {precision!r}")
+
+
+def fp16_rne(v) -> np.ndarray:
+    """Round float64 values to IEEE binary16, once, half to even.
+
+    numpy's float64 -> float16 cast rounds directly from the double value
+    (no detour through float32); the pins check that against hand-built
+    midpoint cases, subnormals and overflow to infinity.
+    """
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16)
+
+
+def quantize_rows(xt: np.ndarray):
+    """Symmetric per-row INT4 quantisation of rotated rows.
+
+    [QuaRot] "End-to-end flow" (runtime: the rotated activation is quantised
+    to INT4) and [RQ] "The Activation Outlier Bottleneck in Low-Bit Serving"
+    (a uniform grid of 2^4 = 16 levels whose range is set by the extremes).
+    Symmetric form: scale = fp16_rne(max|x~| / 7), q = clamp(rne(x~/scale),
+    -8, 7); a zero scale (zero row, or a/7 below half the smallest fp16
+    subnormal) gives all-zero codes.  The division runs in float64 on the
+    given values, so for float32 input it is the exact quotient up to
+    2^-53 relative.
+
+    Returns (q int8 [..., n], scales float16 [...], v float64 [..., n]) where v
+    is the pre-round value x~/scale (0 where the scale is 0).
+    """
+    xt64 = np.asarray(xt).astype(np.float64)
+    a = np.max(np.abs(xt64), axis=-1)
+    scales = fp16_rne(a / 7.0)
+    s = scales.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s > 0, xt64 / np.where(s > 0, s, 1.0), 0.0)
+    q = np.clip(np.rint(v), QMIN, QMAX).astype(np.int8)  # np.rint: half to even
+    return q, scales, v
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two's-complement nibble packing: low nibble = even index."""
+    q = np.asarray(q).astype(np.int16)
+    if q.shape[-1] % 2:
+        raise ValueError("packing needs an even number of codes per row")
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(codes: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_int4` (sign-extends each nibble)."""
+    c = np.asarray(codes).astype(np.int16)
+    lo = c & 0xF
+    hi = (c >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """q * scale in float64 (the value a code stands for)."""
+    return np.asarray(q).astype(np.float64) * np.asarray(scales).astype(np.float64)[..., None]
+
+
+def fwht_quant(x: np.ndarray, signs: np.ndarray | None, precision: str = "f64") -> dict:
+    """Online rotation fused with per-token INT4 quantisation and packing.
+
+    [QuaRot] "End-to-end flow" (runtime): an online Hadamard rotates the
+    activation, which is then quantised to INT4.  [RQ] "Weight Absorption and
+    Online Fast Walsh-Hadamard Transforms", part 2: the online rotation is an
+    FWHT.  Returns codes uint8 [m, n/2], scales float16 [m], x_rot [m, n]
+    (float64 or float32), q int8 [m, n] and v (pre-round values).
+    """
+    xt = rotate(x, signs, precision)
+    q, scales, v = quantize_rows(xt)
+    return {"codes": pack_int4(q), "scales": scales, "x_rot": xt, "q": q, "v": v}
+
+
+def fold_weights(wt: np.ndarray, signs: np.ndarray | None, precision: str = "f64") -> dict:
+    """Offline fold W~ = R^T W followed by per-output-channel INT4.
+
+    [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms",
+    part 1: an input projection's weight is pre-multiplied by R^T once,
+    offline.  [QuaRot] "End-to-end flow" (offline: quantize): the folded
+    weights are quantised to INT4.  [SpinQuant] "The architecture: every
+    piece explained": INT4 weights with per-channel scales.
+
+    ``wt`` is W^T stored [k][d] (output channel major).  Row j of W~^T is
+    w_j R = (w_j * s) H_d / sqrt(d): exactly :func:`rotate` applied to each
+    row of W^T, then :func:`quantize_rows` along d (one scale per output
+    channel).
+    """
+    return fwht_quant(wt, signs, precision)
+
+
+def _int_matmul_nt(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """Exact integer product qa @ qw.T for int4 codes (int64 result).
+
+    Uses a float64 matrix product as the library primitive: every product
+    is an integer of magnitude <= 64 and every partial sum an integer of
+    magnitude <= 64 * d <= 2^20, all exactly representable in float64 (53-bit
+    significand), so the result is exact whatever the summation order.
+    """
+    d = qa.shape[-1]
+    if 64 * d >= 2 ** 53:
+        raise ValueError("d too large for an exact float64 accumulation")
+    acc = qa.astype(np.float64) @ qw.astype(np.float64).T
+    return acc.astype(np.int64)
+
+
+def w4a4_gemm(a_codes: np.ndarray, a_scales: np.ndarray, w_codes: np.ndarray,
+              w_scales: np.ndarray):
+    """W4A4 linear on packed codes: integer accumulation then fp16 epilogue.
+
+    [RQ] "Hardware Execution and Serving Economics", part 1: a rotated W4A4
+    layer runs as an integer GEMM.  [QuaRot] "End-to-end flow": the INT4
+    rotated activation multiplies the INT4 folded weight.
+    acc[m][j] = sum_i qa[m][i] * qw[j][i] (exact integers),
+    y[m][j] = fp16_rne(acc * sa[m] * sw[j]) with the product in float64.
+    Returns (y float16 [m, k], acc int64 [m, k]).
+    """
+    qa = unpack_int4(a_codes)
+    qw = unpack_int4(w_codes)
+    if qa.shape[-1] != qw.shape[-1]:
+        raise ValueError("inner dimensions differ")
+    acc = _int_matmul_nt(qa, qw)
+    sa = np.asarray(a_scales).astype(np.float64)[:, None]
+    sw = np.asarray(w_scales).astype(np.float64)[None, :]
+    y = fp16_rne(acc.astype(np.float64) * sa * sw)
+    return y, acc
+
+
+def kv_rotate_quant(k: np.ndarray, v: np.ndarray, signs: np.ndarray | None = None,
+                    precision: str = "f64") -> dict:
+    """Per-head rotation and INT4 packing of the key/value cache.
+
+    [QuaRot] "The architecture: every piece explained" (KV-cache rotation
+    box) and "End-to-end flow" (the KV cache): keys and values are rotated,
+    then quantised to four bits.  [RQ] "Hardware Execution and Serving
+    Economics", part 2: 4-bit KV caching after rotating K and V.
+    Each head_dim vector (last axis, 128 for the configured cache) is one
+    row: plain H/sqrt(n) unless signs are given, then per-row INT4.
+    """
+    out = {}
+    for name, t in (("k", k), ("v", v)):
+        r = fwht_quant(np.asarray(t), signs, precision)
+        out[name + "_codes"] = r["codes"]
+        out[name + "_scales"] = r["scales"]
+        out[name + "_q"] = r["q"]
+        out[name + "_v"] = r["v"]
+        out[name + "_rot"] = r["x_rot"]
+    return out

@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test fixes the oracle against a closed form, an independent library
+routine, brute force on tiny inputs, or a number the pages print.  A plausible
+slip in the oracle (wrong butterfly sign or stride, signs applied after H
+instead of before, a missing 1/sqrt(n), fp16 double rounding, ties rounded
+away from zero, swapped nibbles, a transposed GEMM operand) fails at least one
+of them.
+"""
+
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import scipy.linalg
+from hypothesis import given, settings, strategies as st
+
+from oracle import rq_oracle as O
+from rotation_w4a4_quantization_amd import datagen
+
+
+def sylvester_block(n):
+    """+-1 Sylvester matrix from the block recursion [[H, H], [H, -H]]."""
+    h = np.array([[1]], dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+# ----------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_fwht_equals_explicit_sylvester_matmul(n):
+    rng = np.random.default_rng(n)
+    u = rng.standard_normal((5, n))
+    h = sylvester_block(n).astype(np.float64)
+    ref = u @ h.T  # row vector convention: y_j = sum_i H[j][i] u_i (H symmetric)
+    got = O.hadamard_transform(u)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("n", [2, 16, 512, 2048])
+def test_fwht_equals_scipy_hadamard(n):
+    rng = np.random.default_rng(1000 + n)
+    u = rng.standard_normal((3, n))
+    ref = u @ scipy.linalg.hadamard(n).astype(np.float64)
+    np.testing.assert_allclose(O.hadamard_transform(u), ref, rtol=0, atol=1e-10 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 256, 1024])
+def test_hadamard_rows_closed_form_and_orthogonality(n):
+    # transforming the identity yields H itself; entries must be (-1)^popcount(i&j)
+    h = O.hadamard_transform(np.eye(n, dtype=np.float64))
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    pop = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    np.testing.assert_array_equal(h, np.where(pop % 2 == 0, 1.0, -1.0))
+    hi = h.astype(np.int64)
+    np.testing.assert_array_equal(hi @ hi.T, n * np.eye(n, dtype=np.int64))
+
+
+@pytest.mark.parametrize("a,b", [(2, 8), (4, 16), (8, 32)])
+def test_kronecker_structure(a, b):
+    ha = scipy.linalg.hadamard(a)
+    hb = scipy.linalg.hadamard(b)
+    h = O.hadamard_transform(np.eye(a * b)).astype(np.int64)
+    np.testing.assert_array_equal(h, np.kron(ha, hb))
+
+
+@settings(max_examples=40, deadline=None)
+@given(logn=st.integers(0, 11), seed=st.integers(0, 2**31 - 1))
+def test_involution(logn, seed):
+    n = 1 << logn
+    u = np.random.default_rng(seed).standard_normal((2, n))
+    back = O.hadamard_transform(O.hadamard_transform(u))
+    np.testing.assert_allclose(back, n * u, rtol=0, atol=1e-9 * n * max(1.0, np.abs(u).max()))
+
+
+@settings(max_examples=40, deadline=None)
+@given(logn=st.integers(1, 12), seed=st.integers(0, 2**31 - 1))
+def test_rotation_preserves_norm(logn, seed):
+    n = 1 << logn
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((3, n)) * rng.uniform(0.1, 100)
+    s = datagen.rademacher(rng, n)
+    xr = O.rotate(x, s, "f64")
+    np.testing.assert_allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+
+
+@pytest.mark.parametrize("n,i", [(256, 0), (256, 77), (4096, 598), (8192, 8191)])
+def test_one_hot_spike_spreads_to_uniform_magnitude(n, i):
+    rng = np.random.default_rng(n + i)
+    s = datagen.rademacher(rng, n)
+    m = 100.0
+    x = np.zeros((1, n))
+    x[0, i] = m
+    xr = O.rotate(x, s, "f64")[0]
+    j = np.arange(n)
+    parity = np.array([bin(i & int(v)).count("1") % 2 for v in j])
+    expected = s[i] * np.where(parity == 0, 1.0, -1.0) * m / math.sqrt(n)
+    np.testing.assert_allclose(xr, expected, rtol=1e-14, atol=0)
+
+
+def test_attenuation_factors_from_page(golden):
+    g = golden["attenuation"]
+    factors = []
+    for d in g["d"]:
+        x = np.zeros((1, d))
+        x[0, 5] = 1.0
+        xr = O.rotate(x, None, "f64")
+        factors.append(1.0 / np.abs(xr).max())
+    assert factors[0] == pytest.approx(g["factor_low"], rel=1e-12)  # sqrt(4096) = 64
+    assert g["factor_high"] <= factors[1] < g["factor_high"] + 1  # sqrt(8192) = 90.51
+
+
+def test_plain_rotation_equals_all_plus_signs():
+    x = np.random.default_rng(3).standard_normal((4, 128))
+    np.testing.assert_array_equal(O.rotate(x, None, "f64"), O.rotate(x, np.ones(128, np.int8), "f64"))
+
+
+def test_signs_applied_before_hadamard():
+    # with R = diag(s) H / sqrt(n), row e_i maps to s_i * H[i] / sqrt(n); the
+    # other order (H diag(s)) would give H[i] * s instead.
+    n = 16
+    s = np.array([1, -1] * 8, dtype=np.int8)
+    s[3] = -1
+    e = np.zeros((1, n))
+    e[0, 2] = 1.0
+    h = sylvester_block(n).astype(np.float64)
+    np.testing.assert_allclose(O.rotate(e, s, "f64")[0], s[2] * h[2] / 4.0, atol=1e-15)
+    assert not np.allclose(O.rotate(e, s, "f64")[0], h[2] * s / 4.0)
+
+
+def test_computational_invariance_tiny_linear():
+    # (X R)(R^T W) = X W in fp64; the fold and the online rotation must use the same R.
+    cfg = datagen.tiny_linear(0)
+    x = cfg["x"].astype(np.float64)
+    wt = cfg["wt"].astype(np.float64)
+    xr = O.rotate(x, cfg["signs"], "f64")
+    wr_t = O.rotate(wt, cfg["signs"], "f64")  # rows of W~^T = W^T R
+    y_rot = xr @ wr_t.T
+    y = x @ wt.T
+    err = np.abs(y_rot - y).max() / np.abs(y).max()
+    assert err < 1e-10
+    # the fold entry point is that same row transform on W^T
+    folded = O.fold_weights(cfg["wt"], cfg["signs"], "f64")
+    np.testing.assert_array_equal(folded["x_rot"], wr_t)
+
+
+@pytest.mark.parametrize("n", [2, 8, 32, 128, 512, 2048, 8192])
+def test_inv_sqrt_constant_is_correctly_rounded(n):
+    getcontext().prec = 60
+    exact = Decimal(1) / Decimal(n).sqrt()
+    c = O._inv_sqrt_f32(n)
+    below = np.nextafter(c, np.float32(0))
+    above = np.nextafter(c, np.float32(1))
+    err = abs(Decimal(float(c)) - exact)
+    assert err <= abs(Decimal(float(below)) - exact)
+    assert err <= abs(Decimal(float(above)) - exact)
+
+
+def test_f32_mirror_exact_on_small_integers_and_close_otherwise():
+    rng = np.random.default_rng(11)
+    n = 1024  # 4^5: 1/sqrt(n) is a power of two
+    x = rng.integers(-50, 50, size=(4, n)).astype(np.float32)
+    s = datagen.rademacher(rng, n)
+    np.testing.assert_array_equal(O.rotate(x, s, "f32").astype(np.float64), O.rotate(x, s, "f64"))
+    xg = rng.standard_normal((8, 4096)).astype(np.float16)
+    s = datagen.rademacher(rng, 4096)
+    r32 = O.rotate(xg, s, "f32").astype(np.float64)
+    r64 = O.rotate(xg, s, "f64")
+    rel = np.abs(r32 - r64).max(axis=1) / np.abs(r64).max(axis=1)
+    # ascending-stride fp32 butterflies: error <= log2(n) * 2^-24 * sqrt(n) * rms bound, far below 1e-5
+    assert rel.max() < 1e-5
+
+
+# ----------------------------------------------------------- fp16 rounding
+
+def test_fp16_single_rounding_pins():
+    cases = [
+        (1 + 2**-11 + 2**-40, 1 + 2**-10),  # above the midpoint: up (a float32 detour would give 1.0)
+        (1 + 2**-11, 1.0),                  # exact midpoint: tie to even
+        (1 + 3 * 2**-11, 1 + 2**-9),        # exact midpoint: tie to even (up)
+        (2**-25, 0.0),                      # half the smallest subnormal: tie to even zero
+        (3 * 2**-25, 2**-23),               # 1.5 subnormal ulps: tie to even (2 ulps)
+        (2**-25 + 2**-40, 2**-24),          # just above half an ulp
+        (65519.99, 65504.0),
+        (65520.0, np.inf),                  # midpoint to the next binade rounds to infinity
+        (-2.5 * 2**-24, -2 * 2**-24),
+    ]
+    for v, want in cases:
+        assert float(O.fp16_rne(v)) == want, (v, float(O.fp16_rne(v)), want)
+
+
+# --------------------------------------------------------------- quantizer
+
+def test_quantizer_round_half_even_table():
+    # a = 7 -> scale = fp16(1.0) = 1, so v = x exactly
+    row = np.array([7.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, 6.5, -6.5, -7.0, 0.49, -3.51])
+    q, sc, v = O.quantize_rows(row[None, :])
+    assert float(sc[0]) == 1.0
+    np.testing.assert_array_equal(q[0], [7, 2, 4, -2, 0, 0, 2, 6, -6, -7, 0, -4])
+    np.testing.assert_array_equal(v[0], row)
+
+
+def test_quantizer_scale_is_single_rounded_absmax_over_7():
+    # a/7 exactly on an fp16 midpoint -> tie to even
+    a = 7 * (1 + 2**-11)
+    q, sc, _ = O.quantize_rows(np.array([[a, -1.0, 0.0, 2.0]]))
+    assert float(sc[0]) == 1.0
+    assert q[0, 0] == 7  # v = 7.0034 -> 7, never 8
+    q, sc, _ = O.quantize_rows(np.array([[-a * (1 + 2**-30), 1.0]]))
+    assert float(sc[0]) == 1 + 2**-10
+    assert q[0, 0] == -7
+
+
+def test_quantizer_zero_and_underflow_rows():
+    q, sc, v = O.quantize_rows(np.zeros((2, 8)))
+    assert not q.any() and not sc.astype(np.float64).any()
+    tiny = np.array([[0.4 * 7 * 2**-24, -0.1 * 2**-24, 0.0, 0.0]])  # a/7 < 2^-25 -> scale 0
+    q, sc, v = O.quantize_rows(tiny)
+    assert float(sc[0]) == 0.0 and not q.any()
+
+
+def test_quantizer_clamps_when_scale_is_subnormal():
+    a = 7 * 1.4 * 2**-24  # a/7 = 1.4 subnormal ulps -> scale = 2^-24, v up to 9.8
+    q, sc, v = O.quantize_rows(np.array([[a, -a, a / 2, 0.0]]))
+    assert float(sc[0]) == 2**-24
+    np.testing.assert_array_equal(q[0], [7, -8, 5, 0])
+
+
+def test_one_hot_row_codes_are_plus_minus_seven():
+    n = 256
+    s = datagen.rademacher(np.random.default_rng(5), n)
+    x = np.zeros((1, n))
+    x[0, 17] = -3.25
+    r = O.fwht_quant(x, s, "f64")
+    assert set(np.abs(r["q"][0]).tolist()) == {7}
+
+
+def test_zero_row_codes_are_zero():
+    r = O.fwht_quant(np.zeros((3, 64), np.float16), None, "f64")
+    assert not r["codes"].any()
+    assert not r["scales"].astype(np.float64).any()
+
+
+@settings(max_examples=30, deadline=None)
+@given(logn=st.integers(1, 10), seed=st.integers(0, 2**31 - 1), mag=st.floats(1e-3, 1e4))
+def test_codes_within_range_and_reconstruct(logn, seed, mag):
+    n = 1 << logn
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((4, n)) * mag
+    r = O.fwht_quant(x, datagen.rademacher(rng, n), "f64")
+    assert r["q"].min() >= -7 and r["q"].max() <= 7  # normal fp16 scales never reach -8
+    deq = O.dequantize(r["q"], r["scales"])
+    step = r["scales"].astype(np.float64)[:, None]
+    assert np.all(np.abs(deq - r["x_rot"]) <= 0.5 * step * (1 + 1e-12) + 1e-300)
+
+
+# ------------------------------------------------------------------ packing
+
+def test_nibble_order_and_twos_complement():
+    assert O.pack_int4(np.array([[1, -1]]))[0, 0] == 0xF1
+    assert O.pack_int4(np.array([[-8, 7]]))[0, 0] == 0x78
+    assert O.pack_int4(np.array([[0, -8, 5, 3]])).tolist() == [[0x80, 0x35]]
+    allq = np.array([[a, b] for a in range(-8, 8) for b in range(-8, 8)])
+    packed = O.pack_int4(allq)
+    assert sorted(packed[:, 0].tolist()) == list(range(256))
+    np.testing.assert_array_equal(O.unpack_int4(packed), allq)
+
+
+# --------------------------------------------------------------------- GEMM
+
+def test_gemm_brute_force_tiny():
+    rng = np.random.default_rng(21)
+    m, k, d = 3, 5, 8
+    ac = datagen.random_codes(rng, m, d)
+    wc = datagen.random_codes(rng, k, d)
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k)
+    y, acc = O.w4a4_gemm(ac, sa, wc, sw)
+
+    def nib(byte, hi):
+        v = (int(byte) >> (4 if hi else 0)) & 0xF
+        return v - 16 if v >= 8 else v
+
+    for i in range(m):
+        for j in range(k):
+            ref = 0
+            for t in range(d):
+                ref += nib(ac[i, t // 2], t % 2) * nib(wc[j, t // 2], t % 2)
+            assert acc[i, j] == ref
+            want = np.float16(float(ref) * float(sa[i]) * float(sw[j]))
+            assert y[i, j] == want or (np.isnan(want) and np.isnan(y[i, j]))
+
+
+def test_gemm_closed_forms():
+    d = 8192
+    sevens = O.pack_int4(np.full((2, d), 7))
+    negs = O.pack_int4(np.full((3, d), -8))
+    ones = np.ones(3, np.float16)
+    _, acc = O.w4a4_gemm(sevens, ones[:2], sevens, ones[:2])
+    assert (acc == 49 * d).all()
+    _, acc = O.w4a4_gemm(negs, ones, negs, ones)
+    assert (acc == 64 * d).all() and acc.max() == 524288
+    _, acc = O.w4a4_gemm(sevens, ones[:2], negs, ones)
+    assert (acc == -56 * d).all()
+    # unit scales: y = fp16(acc)
+    rng = np.random.default_rng(4)
+    ac = datagen.random_codes(rng, 4, 64)
+    wc = datagen.random_codes(rng, 6, 64)
+    y, acc = O.w4a4_gemm(ac, np.ones(4, np.float16), wc, np.ones(6, np.float16))
+    np.testing.assert_array_equal(y, acc.astype(np.float16))
+
+
+def test_gemm_is_not_transposed():
+    # rows of the output follow activation rows, columns follow weight rows
+    a = O.pack_int4(np.array([[1] * 64, [2] * 64]))
+    w = O.pack_int4(np.array([[1] * 64, [0] * 64, [-1] * 64]))
+    _, acc = O.w4a4_gemm(a, np.ones(2, np.float16), w, np.ones(3, np.float16))
+    np.testing.assert_array_equal(acc, [[64, 0, -64], [128, 0, -128]])
+
+
+def test_w4a4_output_tracks_float_linear_and_rotation_helps():
+    # accuracy of the method itself is not a parity target; this checks the
+    # property the pages argue for: rotated W4A4 error << unrotated error
+    cfg = datagen.tiny_linear(0)
+    x = cfg["x"].astype(np.float64)
+    wt = cfg["wt"].astype(np.float64)
+    y = x @ wt.T
+
+    def w4a4(signs_rot):
+        if signs_rot is None:
+            a = O.quantize_rows(x)
+            w = O.quantize_rows(wt)
+            ac, sa, wc, sw = O.pack_int4(a[0]), a[1], O.pack_int4(w[0]), w[1]
+        else:
+            a = O.fwht_quant(x, signs_rot, "f64")
+            w = O.fold_weights(wt, signs_rot, "f64")
+            ac, sa, wc, sw = a["codes"], a["scales"], w["codes"], w["scales"]
+        yq, _ = O.w4a4_gemm(ac, sa, wc, sw)
+        return np.linalg.norm(yq.astype(np.float64) - y) / np.linalg.norm(y)
+
+    e_rot = w4a4(cfg["signs"])
+    e_plain = w4a4(None)
+    assert e_rot < 0.2
+    assert e_rot < 0.8 * e_plain  # weight INT4 error is common to both; activation error differs
+
+
+# ------------------------------------------------------- worked examples
+
+def test_outlier_collapses_ordinary_values_into_few_bins(golden):
+    g = golden["outlier_example"]
+    rng = np.random.default_rng(7)
+    n = 4096
+    lo, hi = g["ordinary_range"]
+    x = rng.uniform(lo, hi, size=(1, n))
+    x[0, 7] = g["outlier_value"]
+    q, _, _ = O.quantize_rows(x)
+    ordinary = np.delete(q[0], 7)
+    assert len(np.unique(ordinary)) <= golden["bins_for_ordinary_values"]["max_bins"]
+    assert 2 ** 4 == g["int4_levels"]
+    r = O.fwht_quant(x, datagen.rademacher(rng, n), "f64")
+    assert len(np.unique(r["q"][0])) >= 12
+    err_plain = np.linalg.norm(O.dequantize(q, O.quantize_rows(x)[1]) - x)
+    err_rot = np.linalg.norm(O.dequantize(r["q"], r["scales"]) - r["x_rot"])
+    assert err_rot < 0.3 * err_plain
+
+
+def test_kv_memory_formula_and_saving(golden):
+    # Memory = 2 * layers * heads * head_dim * seq * batch * bytes_per_element
+    def kv_bytes(layers, heads, head_dim, seq, batch, bits):
+        return 2 * layers * heads * head_dim * seq * batch * bits / 8
+
+    b16 = kv_bytes(1, 8, 128, 4096, 32, 16)
+    b4 = kv_bytes(1, 8, 128, 4096, 32, 4)
+    assert 1 - b4 / b16 == golden["kv_memory"]["reduction_16_to_4_bit"]
+    # this layout: 4-bit codes plus one fp16 scale per 128-element vector
+    ours = 2 * (32 * 8 * 4096) * (128 // 2 + 2)
+    assert ours == 2 * (134217728 // 2 + 2 * 32 * 8 * 4096)
+    assert ours / b16 == pytest.approx(4.125 / 16)
+    assert 1 - ours / b16 == pytest.approx(0.7421875)
+
+
+def test_weight_bytes_quartered(golden):
+    d, k = 4096, 4096
+    fp16_bytes = 2 * d * k
+    int4_bytes = d * k // 2
+    assert int4_bytes / fp16_bytes == golden["weight_bytes"]["ratio_4_over_16"]
+
+
+def test_datagen_outlier_fraction_matches_page(golden):
+    g = golden["outlier_statistics"]
+    for d, want in [(4096, 4), (8192, 8)]:
+        ch = datagen.outlier_channels(datagen.rng_for(1, 0), d, g["channel_fraction"])
+        assert len(ch) == want and len(set(ch.tolist())) == want
+
+
+def test_kv_oracle_is_rowwise_fwht_quant():
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((2, 3, 5, 128)).astype(np.float16)
+    v = rng.standard_normal((2, 3, 5, 128)).astype(np.float16)
+    out = O.kv_rotate_quant(k, v)
+    flat = O.fwht_quant(k.reshape(-1, 128), None, "f64")
+    np.testing.assert_array_equal(out["k_codes"].reshape(-1, 64), flat["codes"])
+    assert out["k_codes"].shape == (2, 3, 5, 64) and out["v_scales"].shape == (2, 3, 5)
