@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the rotate + INT4 + W4A4 hot path on one MI355X.
+
+Main workload (the JSON ``value``): rq_fwht_quant on 4096 tokens x 4096 fp16
+activations (0.1% of channels x100, randomized Hadamard n = 4096), in GB/s of
+algorithmic HBM traffic (fp16 input + packed codes + fp16 scales + int8
+signs).  One step = one call over the whole 4096 x 4096 batch; inputs and
+outputs rotate over buffer sets larger than the 256 MB Infinity Cache so that
+repeats cannot be served from it.
+
+``secondary`` reports the other rows of the path on their own workloads:
+the decode-shaped and prefill-shaped W4A4 GEMMs (TOPS and GB/s), the prefill
+activation rotation (2048 x 8192) and the KV-cache rotation
+[32, 8, 4096, 128] x {K, V}.
+
+Kernel time is measured with HIP events recorded on the stream the kernels
+are launched on (torch's current stream, which the binding passes to librq).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-secondary", action="store_true", help="time only the main workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of secondary items to run")
+    return p.parse_args()
+
+
+def fwht_bytes(m: int, n: int) -> int:
+    # fp16 input + packed int4 codes + fp16 scales + int8 signs
+    return m * n * 2 + m * n // 2 + 2 * m + n
+
+
+def gemm_bytes(m: int, k: int, d: int) -> int:
+    # weights + weight scales + activation codes + activation scales + fp16 output
+    return d * k // 2 + 2 * k + m * d // 2 + 2 * m + 2 * m * k
+
+
+def kv_bytes(rows: int) -> int:
+    return 2 * (rows * 128 * 2 + rows * 64 + rows * 2)
+
+
+def time_launches(torch, fn, sets: int, steps: int, warmup: int):
+    """Average per-call milliseconds of fn(i) over `steps` calls (events on the
+    current stream), after `warmup` untimed calls; i cycles over buffer sets."""
+    for i in range(warmup):
+        fn(i % sets)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i % sets)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    for v in ("RANK", "WORLD_SIZE"):
+        if os.environ.get(v) not in (None, "0", "1"):
+            print(json.dumps({"error": "multi-rank launch is not supported"}))
+            sys.exit(2)
+
+    import torch
+
+    import rotation_w4a4_quantization_amd as rq
+    from rotation_w4a4_quantization_amd import datagen
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    rq.load_library()
+    dev = torch.device("cuda:0")
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    # ------------------------------------------------ main: fwht_quant 4096^2
+    w = datagen.fwht_workload(0)
+    m, n = w["m"], w["d"]
+    x0 = torch.from_numpy(w["x"]).to(dev)
+    signs = torch.from_numpy(w["signs"]).to(dev)
+    per_set = m * n * 2 + m * n // 2 + 2 * m
+    sets = max(2, -(-2 * MALL_BYTES // per_set) + 1)
+    xs = [x0.clone() for _ in range(sets)]
+    outs = [(torch.empty((m, n // 2), dtype=torch.uint8, device=dev),
+             torch.empty((m,), dtype=torch.float16, device=dev)) for _ in range(sets)]
+    lib = rq.load_library()
+    from rotation_w4a4_quantization_amd.binding import RQ_F16, _ptr, _stream
+
+    def fq(i):
+        st = lib.rq_fwht_quant(_ptr(xs[i]), RQ_F16, m, n, _ptr(signs), _ptr(outs[i][0]),
+                               _ptr(outs[i][1]), None, _stream())
+        if st:
+            raise RuntimeError(rq.status_string(st))
+
+    log(f"[bench] fwht_quant {m}x{n} fp16: {sets} buffer sets, warmup {args.warmup}, steps {args.steps}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_launches(torch, fq, sets, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    nbytes = fwht_bytes(m, n)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] fwht_quant: {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% HBM)")
+    del xs, outs
+
+    result = {
+        "metric": "FWHT+quant GB/s and W4A4 GEMM TOPS (% of HBM / int8-MFMA peak), 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; N(0,1) fp16 with 0.1% of channels x100)",
+        "config": {"workload": "rq_fwht_quant 4096 tokens x 4096 fp16, n=4096 randomized Hadamard, "
+                               "per-token INT4", "tokens": m, "n": n, "input_dtype": "fp16",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "fwht_quant_kernel<__half, 4096, 64>",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "wall_s_timed_region": round(wall, 3),
+    }
+
+    # ------------------------------------------------------------ secondary
+    sec = {}
+    only = set(filter(None, args.only.split(",")))
+    want = (lambda k: (not only) or k in only)
+    if not args.no_secondary:
+        steps2 = max(10, args.steps // 4)
+        warm2 = max(3, args.warmup // 4)
+
+        if want("decode"):
+            dec = datagen.decode_linear(0)
+            s = torch.from_numpy(dec["signs"]).to(dev)
+            xa = torch.from_numpy(dec["x"]).to(dev)
+            ac, sa, _ = rq.fwht_quant(xa, s)
+            for k, wt in dec["wts"].items():
+                wc, ws, _ = rq.fold_weights(torch.from_numpy(wt).to(dev), s)
+                nsets = max(2, -(-2 * MALL_BYTES // wc.numel()) + 1)
+                wcs = [wc.clone() for _ in range(nsets)]
+                for mm in (1, 4, 16):
+                    y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+                    a_m, s_m = ac[:mm].contiguous(), sa[:mm].contiguous()
+
+                    def g(i, a_m=a_m, s_m=s_m, y=y):
+                        rq.w4a4_gemm(a_m, s_m, wcs[i], ws, out=y)
+
+                    msg = time_launches(torch, g, nsets, steps2, warm2)
+                    b = gemm_bytes(mm, k, 4096)
+                    sec[f"gemm_decode_m{mm}_k{k}"] = {
+                        "us": round(msg * 1e3, 3), "GB/s": round(b / (msg * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(b / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "TOPS": round(2 * mm * k * 4096 / (msg * 1e-3) / 1e12, 3)}
+                    log(f"[bench] decode m={mm} k={k}: {sec[f'gemm_decode_m{mm}_k{k}']}")
+                del wcs
+
+        if want("prefill"):
+            pf = datagen.prefill_linear(0)
+            s = torch.from_numpy(pf["signs"]).to(dev)
+            wc, ws, _ = rq.fold_weights(torch.from_numpy(pf["wt"]).to(dev), s)
+            del pf["wt"]
+            xa = torch.from_numpy(pf["x"]).to(dev)
+            mm, d, k = pf["m"], pf["d"], pf["k"]
+            ac = torch.empty((mm, d // 2), dtype=torch.uint8, device=dev)
+            sa = torch.empty((mm,), dtype=torch.float16, device=dev)
+
+            def f8(i):
+                st = lib.rq_fwht_quant(_ptr(xa), RQ_F16, mm, d, _ptr(s), _ptr(ac), _ptr(sa), None,
+                                       _stream())
+                assert st == 0
+
+            msf = time_launches(torch, f8, 1, steps2, warm2)
+            b = fwht_bytes(mm, d)
+            sec["fwht_quant_2048x8192"] = {"us": round(msf * 1e3, 3),
+                                           "GB/s": round(b / (msf * 1e-3) / 1e9, 1),
+                                           "hbm_frac": round(b / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] fwht_quant 2048x8192: {sec['fwht_quant_2048x8192']}")
+            y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+            wcs = [wc, wc.clone()]
+
+            def gp(i):
+                rq.w4a4_gemm(ac, sa, wcs[i], ws, out=y)
+
+            msp = time_launches(torch, gp, 2, max(5, steps2 // 2), warm2)
+            tops = 2 * mm * d * k / (msp * 1e-3) / 1e12
+            sec["gemm_prefill_2048x8192x28672"] = {"us": round(msp * 1e3, 2), "TOPS": round(tops, 1),
+                                                   "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+            log(f"[bench] prefill gemm: {sec['gemm_prefill_2048x8192x28672']}")
+
+            def lin(i):
+                f8(0)
+                rq.w4a4_gemm(ac, sa, wcs[i], ws, out=y)
+
+            msl = time_launches(torch, lin, 2, max(5, steps2 // 2), warm2)
+            sec["linear_prefill_rotate_plus_gemm"] = {"us": round(msl * 1e3, 2)}
+            del wcs, wc, y
+
+        if want("kv"):
+            kv = datagen.kv_cache(0)
+            kt = torch.from_numpy(kv["k"]).to(dev)
+            vt = torch.from_numpy(kv["v"]).to(dev)
+            del kv
+            rows = kt.numel() // 128
+            kc = torch.empty((rows, 64), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+            ks = torch.empty((rows,), dtype=torch.float16, device=dev)
+            vs = torch.empty_like(ks)
+
+            def fkv(i):
+                st = lib.rq_kv_rotate_quant(_ptr(kt), _ptr(vt), rows, 128, None, _ptr(kc), _ptr(ks),
+                                            _ptr(vc), _ptr(vs), _stream())
+                assert st == 0
+
+            mk = time_launches(torch, fkv, 1, max(5, steps2 // 2), warm2)
+            b = kv_bytes(rows)
+            sec["kv_rotate_quant_32x8x4096x128"] = {"us": round(mk * 1e3, 2),
+                                                    "GB/s": round(b / (mk * 1e-3) / 1e9, 1),
+                                                    "hbm_frac": round(b / (mk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] kv: {sec['kv_rotate_quant_32x8x4096x128']}")
+            del kt, vt
+    result["secondary"] = sec
+
+    # ------------------------------------------------------- CPU baseline
+    if not args.no_cpu_baseline:
+        from oracle import rq_oracle as O
+        rows = 1024
+        xs_ = w["x"][:rows]
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            O.fwht_quant(xs_, w["signs"], "f64")
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0 or reps >= 50:
+                break
+        cpu_gbs = reps * fwht_bytes(rows, n) / el / 1e9
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle fwht_quant on the first {rows} of the 4096 rows, "
+                      f"{reps} repetitions, {el:.1f} s (numpy, single thread)"}
+        log(f"[bench] cpu oracle: {cpu_gbs * 1e3:.3f} MB/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

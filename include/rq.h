@@ -1,0 +1,175 @@
+/*
+ * rq.h -- C ABI of librq: the online hot path of rotational W4A4
+ * quantisation on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [QuaRot]    aicassindra.com, QuaRot explainer.
+ *   [RQ]        llms.blog, "Rotational Quantization: How Orthogonal Transforms
+ *               and Hadamard Incoherence Enable Outlier-Free Low-Bit
+ *               Inference".
+ *   [SpinQuant] aicassindra.com, SpinQuant explainer.
+ *
+ * Conventions shared by every entry point
+ *   - Row vectors ([RQ] "The Principle of Computational Invariance"):
+ *     X is m x d, one token per row; W is d x k and is stored transposed,
+ *     W^T [k][d] (output channel major, the reduction dimension contiguous).
+ *   - R = diag(s) H_n / sqrt(n), H_n the +-1 Sylvester matrix in natural
+ *     order, s int8 +-1 (Rademacher).  A rotated row is (x * s) H_n / sqrt(n).
+ *   - INT4 codes are two's complement, packed two per byte: code 2i in the low
+ *     nibble of byte i, code 2i+1 in the high nibble.  A row of n codes is n/2
+ *     bytes.  Scales are IEEE binary16 bit patterns (uint16_t).
+ *   - Quantiser (symmetric, per row): a = max|x~|, scale = fp16_rne(a / 7)
+ *     rounded once from the exact quotient, q = clamp(rne(x~ / scale), -8, 7)
+ *     with round half to even; scale == 0 gives all-zero codes; a scale that
+ *     overflows fp16 is +inf and gives all-zero codes.
+ *   - All pointers are device pointers.  The caller allocates and owns every
+ *     buffer; the library allocates nothing, keeps no state between calls and
+ *     may be called from several threads.  Work is queued asynchronously on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream); the
+ *     caller keeps buffers alive until the stream has finished.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-zero rq_status is returned and nothing runs.  Row counts of 0 return
+ *     RQ_OK without launching.  Non-finite inputs are undefined behaviour.
+ *   - Optional debug outputs (x_rot, w_rot, acc) select an instantiation of the
+ *     same kernel that also stores the intermediate value; the arithmetic that
+ *     produces the primary outputs is unchanged.
+ */
+#ifndef RQ_H_
+#define RQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RQ_OK = 0,
+  RQ_ERR_NULL = 1,  /* a required pointer is NULL */
+  RQ_ERR_SHAPE = 2, /* a size is negative, not a power of two, or out of range */
+  RQ_ERR_ALIGN = 3, /* a pointer is not 16-byte aligned */
+  RQ_ERR_DTYPE = 4, /* unknown input dtype */
+  RQ_ERR_HIP = 5    /* a HIP launch failed */
+} rq_status;
+
+typedef enum { RQ_F16 = 0, RQ_F32 = 1 } rq_dtype;
+
+/* Smallest and largest supported rotation length n (both powers of two). */
+#define RQ_MIN_N 2
+#define RQ_MAX_N 8192
+
+/*
+ * rq_fwht_quant -- online rotation fused with per-token INT4 quantisation.
+ *
+ * [QuaRot] "End-to-end flow" (runtime: an online Hadamard rotates the
+ * activation, which is quantised to INT4); [RQ] "Weight Absorption and Online
+ * Fast Walsh-Hadamard Transforms", part 2 (the online rotation is a butterfly
+ * FWHT of add/sub stages followed by one global scale); [RQ] "Incoherence
+ * Processing via Randomized Hadamard Transforms" (R = sign diagonal times
+ * Sylvester matrix).
+ *
+ *   x       [m][n] activations, dtype x_dtype (RQ_F16 or RQ_F32), row major,
+ *           16-byte aligned.
+ *   m       number of rows (tokens), >= 0.
+ *   n       rotation length, power of two in [RQ_MIN_N, RQ_MAX_N].
+ *   signs   [n] int8, each +1 or -1; NULL means all +1 (plain H_n/sqrt(n)).
+ *   codes   [m][n/2] uint8 output, 16-byte aligned.
+ *   scales  [m] fp16 output (one per row).
+ *   x_rot   optional [m][n] float32 output of the rotated rows (debug), or
+ *           NULL; 16-byte aligned when given.
+ *
+ * The butterflies are fp32 additions in ascending-stride order; the rotated
+ * value is fp32(y * fp32(1/sqrt(n))).  Codes and scales depend only on x,
+ * signs and n.
+ */
+int rq_fwht_quant(const void* x, int x_dtype, int64_t m, int64_t n, const int8_t* signs,
+                  uint8_t* codes, uint16_t* scales, float* x_rot, void* stream);
+
+/*
+ * rq_fold_weights -- offline fold W~ = R^T W with per-output-channel INT4.
+ *
+ * [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms", part 1
+ * (an input projection's weight is replaced by R^T W once, offline);
+ * [QuaRot] "End-to-end flow" (offline: the folded weights are quantised to
+ * INT4); [SpinQuant] "The architecture: every piece explained" (INT4 weights
+ * with per-channel scales).
+ *
+ *   wt       W^T [k][d], dtype wt_dtype, 16-byte aligned.  Row j of the folded
+ *            W~^T is w_j R = (w_j * s) H_d / sqrt(d): the same row transform
+ *            as rq_fwht_quant, with the same signs as the activations.
+ *   k        output channels (rows of W^T), >= 0.
+ *   d        input width, power of two in [RQ_MIN_N, RQ_MAX_N].
+ *   signs    [d] int8 +-1 or NULL.
+ *   w_codes  [k][d/2] uint8 output; w_scales [k] fp16 output.
+ *   w_rot    optional [k][d] float32 output of W~^T (debug), or NULL.
+ */
+int rq_fold_weights(const void* wt, int wt_dtype, int64_t k, int64_t d, const int8_t* signs,
+                    uint8_t* w_codes, uint16_t* w_scales, float* w_rot, void* stream);
+
+/*
+ * rq_w4a4_gemm_workspace_size -- bytes of device workspace rq_w4a4_gemm needs
+ * for this shape.  The current kernels need none and return 0.
+ */
+size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d);
+
+/*
+ * rq_w4a4_gemm -- W4A4 linear: y = fp16(acc * sa[m] * sw[j]),
+ * acc[m][j] = sum_i qa[m][i] * qw[j][i] in int32.
+ *
+ * [RQ] "Hardware Execution and Serving Economics", part 1 (rotated W4A4
+ * layers run integer GEMMs end to end); [QuaRot] "End-to-end flow" (the INT4
+ * rotated activation multiplies the INT4 folded weight in a low-bit kernel).
+ * INT4 codes are widened to int8 in registers and multiplied with int8 MFMA
+ * into int32 accumulators (exact: |acc| <= 64 * d); the epilogue is
+ * fp32(acc) * sa, then * sw, rounded to fp16 half to even.
+ *
+ *   a_codes  [m][d/2] uint8 activation codes (rq_fwht_quant output), 16-byte
+ *            aligned; a_scales [m] fp16.
+ *   m        tokens, >= 0.
+ *   w_codes  [k][d/2] uint8 weight codes (rq_fold_weights output), 16-byte
+ *            aligned; w_scales [k] fp16.
+ *   k        output channels, >= 1 when m > 0.
+ *   d        reduction length, a multiple of 64 in [64, 16384].
+ *   y        [m][k] fp16 output.
+ *   acc      optional [m][k] int32 output of the accumulators (debug), or NULL.
+ *   workspace, workspace_bytes  device scratch of at least
+ *            rq_w4a4_gemm_workspace_size(m, k, d) bytes (may be NULL when 0).
+ */
+int rq_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                 const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                 uint16_t* y, int32_t* acc, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * rq_kv_rotate_quant -- per-head rotation and INT4 packing of K and V.
+ *
+ * [QuaRot] "The architecture: every piece explained" (KV-cache rotation) and
+ * "End-to-end flow" (keys and values are rotated, then stored in four bits);
+ * [RQ] "Hardware Execution and Serving Economics", part 2 (4-bit KV after
+ * rotating K and V).
+ *
+ *   k_in, v_in   fp16 [rows][head_dim]: every (batch, head, position) vector
+ *                is one row, 16-byte aligned.
+ *   rows         number of vectors in each of K and V, >= 0.
+ *   head_dim     must be 128.
+ *   signs        [head_dim] int8 +-1, or NULL for the plain H/sqrt(128)
+ *                (the same rotation for every head, for K and for V).
+ *   k_codes, v_codes    [rows][head_dim/2] uint8, 16-byte aligned.
+ *   k_scales, v_scales  [rows] fp16.
+ */
+int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows, int64_t head_dim,
+                       const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
+                       uint8_t* v_codes, uint16_t* v_scales, void* stream);
+
+/* Text for an rq_status value (static storage, never NULL). */
+const char* rq_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int rq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H_ */

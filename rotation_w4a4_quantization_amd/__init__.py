@@ -1,0 +1,21 @@
+"""MI355X (gfx950) kernels for the online hot path of rotational W4A4
+quantisation: randomized Hadamard rotation + per-token INT4, the offline
+weight fold, the W4A4 GEMM and the per-head KV-cache rotation.
+
+The compute lives in librq.so (HIP, C ABI in include/rq.h); this package only
+binds it.  ``datagen`` holds the seeded synthetic input generators.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    RQError,
+    fold_weights,
+    fwht_quant,
+    kv_rotate_quant,
+    load_library,
+    status_string,
+    version,
+    w4a4_gemm,
+    w4a4_linear,
+)
+from .build import LIB_PATH  # noqa: F401

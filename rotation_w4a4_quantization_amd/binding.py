@@ -1,0 +1,191 @@
+"""Thin ctypes binding over librq (include/rq.h).
+
+Argument marshalling only: shape/dtype/device checks, output allocation with
+torch, then one C call that queues the HIP kernels on the current torch
+stream.  Every arithmetic step runs in librq's kernels; there is no fallback.
+If the library has not been built, or HIP cannot be loaded, the first call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+RQ_OK, RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_ALIGN, RQ_ERR_DTYPE, RQ_ERR_HIP = range(6)
+RQ_F16, RQ_F32 = 0, 1
+
+EXPORTED = (
+    "rq_fwht_quant",
+    "rq_fold_weights",
+    "rq_w4a4_gemm_workspace_size",
+    "rq_w4a4_gemm",
+    "rq_kv_rotate_quant",
+    "rq_status_string",
+    "rq_version",
+)
+
+_lib = None
+
+
+class RQError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librq.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"librq.so not found at {path}; build it with "
+            "`python -m rotation_w4a4_quantization_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.rq_fwht_quant.argtypes = [p, i32, i64, i64, p, p, p, p, p]
+    lib.rq_fwht_quant.restype = i32
+    lib.rq_fold_weights.argtypes = [p, i32, i64, i64, p, p, p, p, p]
+    lib.rq_fold_weights.restype = i32
+    lib.rq_w4a4_gemm_workspace_size.argtypes = [i64, i64, i64]
+    lib.rq_w4a4_gemm_workspace_size.restype = sz
+    lib.rq_w4a4_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, p, p, sz, p]
+    lib.rq_w4a4_gemm.restype = i32
+    lib.rq_kv_rotate_quant.argtypes = [p, p, i64, i64, p, p, p, p, p, p]
+    lib.rq_kv_rotate_quant.restype = i32
+    lib.rq_status_string.argtypes = [i32]
+    lib.rq_status_string.restype = ctypes.c_char_p
+    lib.rq_version.argtypes = []
+    lib.rq_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().rq_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().rq_version())
+
+
+def _check(func: str, status: int) -> None:
+    if status != RQ_OK:
+        raise RQError(func, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_cuda(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _signs(signs, n, device):
+    if signs is None:
+        return None
+    if signs.dtype != torch.int8 or signs.numel() != n:
+        raise ValueError(f"signs must be int8 with {n} entries")
+    _need_cuda("signs", signs)
+    return signs
+
+
+def _rotate_quant(cfunc: str, x: torch.Tensor, signs, debug: bool):
+    _need_cuda("x", x)
+    if x.dtype not in (torch.float16, torch.float32):
+        raise ValueError("x must be float16 or float32")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, n]")
+    rows, n = x.shape
+    s = _signs(signs, n, x.device)
+    codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows,), dtype=torch.float16, device=x.device)
+    rot = torch.empty((rows, n), dtype=torch.float32, device=x.device) if debug else None
+    dtype = RQ_F16 if x.dtype == torch.float16 else RQ_F32
+    st = getattr(load_library(), cfunc)(_ptr(x), dtype, rows, n, _ptr(s), _ptr(codes),
+                                        _ptr(scales), _ptr(rot), _stream())
+    _check(cfunc, st)
+    return codes, scales, rot
+
+
+def fwht_quant(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+    """rq_fwht_quant: returns (codes uint8 [m, n/2], scales fp16 [m], x_rot fp32 or None)."""
+    return _rotate_quant("rq_fwht_quant", x, signs, debug)
+
+
+def fold_weights(wt: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+    """rq_fold_weights on W^T [k][d]: returns (codes [k, d/2], scales [k], w_rot or None)."""
+    return _rotate_quant("rq_fold_weights", wt, signs, debug)
+
+
+def w4a4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+              w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
+    """rq_w4a4_gemm: returns (y fp16 [m, k], acc int32 [m, k] or None)."""
+    for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes),
+                    ("w_scales", w_scales)):
+        _need_cuda(name, t)
+    if a_codes.dtype != torch.uint8 or w_codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
+    if a_scales.dtype != torch.float16 or w_scales.dtype != torch.float16:
+        raise ValueError("scales must be float16")
+    m, half_d = a_codes.shape
+    k, half_d2 = w_codes.shape
+    if half_d != half_d2:
+        raise ValueError("activation and weight codes differ in d")
+    if a_scales.numel() != m or w_scales.numel() != k:
+        raise ValueError("scale counts do not match the code rows")
+    d = 2 * half_d
+    lib = load_library()
+    ws_bytes = int(lib.rq_w4a4_gemm_workspace_size(m, k, d))
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
+    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
+    acc = torch.empty((m, k), dtype=torch.int32, device=a_codes.device) if debug else None
+    st = lib.rq_w4a4_gemm(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes), _ptr(w_scales), k, d,
+                          _ptr(y), _ptr(acc), _ptr(ws), ws_bytes, _stream())
+    _check("rq_w4a4_gemm", st)
+    return y, acc
+
+
+def kv_rotate_quant(k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor | None = None):
+    """rq_kv_rotate_quant on fp16 [..., 128] K and V.
+
+    Returns (k_codes [..., 64], k_scales [...], v_codes, v_scales)."""
+    _need_cuda("k", k)
+    _need_cuda("v", v)
+    if k.dtype != torch.float16 or v.dtype != torch.float16 or k.shape != v.shape:
+        raise ValueError("k and v must be float16 tensors of the same shape")
+    head_dim = k.shape[-1]
+    rows = k.numel() // head_dim
+    s = _signs(signs, head_dim, k.device)
+    lead = tuple(k.shape[:-1])
+    kc = torch.empty(lead + (head_dim // 2,), dtype=torch.uint8, device=k.device)
+    vc = torch.empty_like(kc)
+    ks = torch.empty(lead, dtype=torch.float16, device=k.device)
+    vs = torch.empty_like(ks)
+    st = load_library().rq_kv_rotate_quant(_ptr(k), _ptr(v), rows, head_dim, _ptr(s), _ptr(kc),
+                                           _ptr(ks), _ptr(vc), _ptr(vs), _stream())
+    _check("rq_kv_rotate_quant", st)
+    return kc, ks, vc, vs
+
+
+def w4a4_linear(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tensor,
+                w_scales: torch.Tensor) -> torch.Tensor:
+    """Online rotation + INT4 quantisation of x, then the W4A4 GEMM against
+    weights folded with the same signs.  Two launches on the current stream."""
+    codes, scales, _ = fwht_quant(x, signs)
+    y, _ = w4a4_gemm(codes, scales, w_codes, w_scales)
+    return y

@@ -1,0 +1,412 @@
+// Row-wise randomized Hadamard rotation fused with symmetric INT4
+// quantisation, for CDNA4 (gfx950).  One kernel family serves the online
+// activation rotation, the offline weight fold (the same row transform applied
+// to the rows of W^T) and the per-head KV-cache rotation.
+//
+// Pages cited:
+//   [RQ]     llms.blog, "Rotational Quantization: How Orthogonal Transforms and
+//            Hadamard Incoherence Enable Outlier-Free Low-Bit Inference".
+//   [QuaRot] aicassindra.com, QuaRot explainer.
+//
+// What a row goes through ([RQ] "Incoherence Processing via Randomized
+// Hadamard Transforms": R = sign diagonal times Sylvester matrix; [RQ] "Weight
+// Absorption and Online Fast Walsh-Hadamard Transforms", part 2: add/sub
+// butterflies and one global scale at the end; [QuaRot] "End-to-end flow":
+// the rotated activation is quantised to INT4):
+//   u = x * s                      exact (sign flip of the fp32 value)
+//   y = H_n u                      fp32 add/sub, strides 1, 2, ..., n/2
+//   x~ = fp32(y * fp32(1/sqrt n))  only stored in debug mode
+//   a = max|x~| = fp32(max|y| * c) (rounding is monotone)
+//   scale = fp16_rne(a / 7)        rounded once from the exact quotient
+//   q = rne(y * m), m = fp32(c / scale), clamped to [-8, 7] only when the
+//       scale is an fp16 subnormal (a normal scale bounds |x~/scale| by 7.004)
+//
+// Work layout.  A row of n elements is spread over LANES = n / E lanes of one
+// wavefront, E elements per lane (all of a row in one lane for n <= 128).
+//   load   : the wave's block of rows is copied global -> LDS with coalesced
+//            16-byte loads (XOR-swizzled 16-byte chunks, so the per-lane
+//            reads below hit distinct banks).
+//   phase 1: each lane reads E consecutive elements: the butterflies of the
+//            low log2(E) index bits run in registers.
+//   phase 2: (LANES > 1) an fp32 exchange through LDS gives each lane the
+//            elements whose low log2(LANES) index bits equal its lane index;
+//            the remaining butterflies (index bits log2(E) .. log2(n) - 1) run
+//            in registers.  Stage order stays ascending, so y is bit-identical
+//            to an ascending-stride fp32 FWHT.
+//   absmax : in-lane max, then an xor-shuffle across the row's lanes.
+//   codes  : fma(y, m, 2^23 + 8) leaves rne(y*m) + 8 in the low mantissa bits;
+//            bytes go through LDS and are packed into nibbles on the way out
+//            (LANES > 1), or packed in registers (LANES == 1).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+constexpr int kWave = 64;
+// fma(v, m, kMagic) = 2^23 + 8 + rne(v*m) for |v*m| < 8: the low 4 bits are
+// the offset-binary code (q + 8); bits 4..22 are zero.
+constexpr float kMagic = 8388616.0f;
+constexpr float kMagicLo = 8388608.0f;   // code -8
+constexpr float kMagicHi = 8388623.0f;   // code +7
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ __forceinline__ uint16_t f2h_rn(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// fp16_rne(xm / 7) rounded once from the exact quotient (xm >= 0, finite).
+// The fp32 quotient is correctly rounded; only when it lands exactly on an
+// fp16 rounding midpoint can a second rounding go the wrong way, and then the
+// exact residual xm - 7q (representable, computed exactly by fma) says on
+// which side of the midpoint the true quotient lies.
+__device__ __forceinline__ uint16_t scale_fp16(float xm) {
+  const float q = xm / 7.0f;
+  uint16_t hb = f2h_rn(q);
+  const float back = (hb == 0x7C00u) ? 65536.0f : h2f(hb);
+  if (q != back) {
+    const uint16_t ob = (back < q) ? (uint16_t)(hb + 1) : (uint16_t)(hb - 1);
+    const float other = (ob == 0x7C00u) ? 65536.0f : h2f(ob);
+    if (q == 0.5f * (back + other)) {
+      const float r = __builtin_fmaf(-7.0f, q, xm);
+      if (r > 0.0f) hb = hb > ob ? hb : ob;
+      else if (r < 0.0f) hb = hb < ob ? hb : ob;
+    }
+  }
+  return hb;
+}
+
+template <int N, int E, int TSIZE>
+struct Geo {
+  static constexpr int LANES = N / E;
+  static constexpr int RW = kWave / LANES;  // rows per wave
+  static constexpr int LOG_N = ilog2(N);
+  static constexpr int LOG_E = ilog2(E);
+  static constexpr int LOG_L = LOG_N - LOG_E;
+  static constexpr int SEG_BYTES = E * TSIZE;          // raw bytes owned by one lane
+  static constexpr int CPL = SEG_BYTES / 16;           // 16-byte chunks per lane (0: < 16 B)
+  static constexpr int ROW_BYTES = N * TSIZE;
+  static constexpr int BLOCK_BYTES = RW * ROW_BYTES;   // = 64 * SEG_BYTES
+  static constexpr int P = E + 4;                      // exchange pitch per lane segment (floats)
+  static constexpr int ROWP = LANES * P;               // exchange pitch per row (floats)
+  static constexpr int RAW_LDS = BLOCK_BYTES;
+  static constexpr int EXCH_LDS = LANES > 1 ? RW * ROWP * 4 : 0;
+  static constexpr int CODE_LDS = LANES > 1 ? RW * N : 0;
+  static constexpr int LDS = RAW_LDS > EXCH_LDS ? (RAW_LDS > CODE_LDS ? RAW_LDS : CODE_LDS)
+                                                 : (EXCH_LDS > CODE_LDS ? EXCH_LDS : CODE_LDS);
+  // XOR swizzle of the 16-byte chunk index inside a lane segment: the 16
+  // lanes served by one LDS pass land on 16 different 16-byte bank groups.
+  static constexpr int SW_SHIFT = CPL >= 16 ? 0 : ilog2(16 / (CPL > 0 ? CPL : 1));
+  static_assert(E >= LANES, "two register phases must cover every index bit");
+  static_assert(LANES <= kWave, "a row must fit in one wavefront");
+};
+
+template <class G>
+__device__ __forceinline__ int raw_phys(int c) {
+  if constexpr (G::CPL <= 1) {
+    return c;
+  } else {
+    const int s = c / G::CPL;
+    const int i = c % G::CPL;
+    return s * G::CPL + (i ^ ((s >> G::SW_SHIFT) & (G::CPL - 1)));
+  }
+}
+
+struct FQOut {
+  const void* x;
+  uint8_t* codes;
+  uint16_t* scales;
+  float* xrot;
+};
+
+template <typename T>
+__device__ __forceinline__ void widen16(const uint4& v, float* out);
+
+template <>
+__device__ __forceinline__ void widen16<__half>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = h2f((uint16_t)(w[i] & 0xFFFFu));
+    out[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+  }
+}
+
+template <>
+__device__ __forceinline__ void widen16<float>(const uint4& v, float* out) {
+  out[0] = u2f(v.x);
+  out[1] = u2f(v.y);
+  out[2] = u2f(v.z);
+  out[3] = u2f(v.w);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const unsigned char* p) {
+  if constexpr (sizeof(T) == 2) {
+    return h2f(*reinterpret_cast<const uint16_t*>(p));
+  } else {
+    return *reinterpret_cast<const float*>(p);
+  }
+}
+
+template <typename T, int N, int E, bool HAS_SIGNS>
+__global__ __launch_bounds__(64) void fwht_quant_kernel(FQOut o0, FQOut o1, int64_t rows,
+                                                       const int8_t* __restrict__ signs,
+                                                       float c32) {
+  using G = Geo<N, E, (int)sizeof(T)>;
+  constexpr int LANES = G::LANES;
+  constexpr int RW = G::RW;
+  __shared__ __align__(16) unsigned char smem[G::LDS];
+
+  const FQOut o = blockIdx.y ? o1 : o0;
+  const int lane = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.x * RW;
+  const int rows_valid = (int)((rows - row0) < RW ? (rows - row0) : RW);
+
+  // ---- global -> LDS, coalesced 16-byte chunks
+  {
+    const int64_t valid_bytes = (int64_t)rows_valid * G::ROW_BYTES;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(o.x) + row0 * G::ROW_BYTES;
+    constexpr int CHUNKS = G::BLOCK_BYTES / 16;
+#pragma unroll
+    for (int c = lane; c < CHUNKS; c += kWave) {
+      const int64_t off = (int64_t)c * 16;
+      if (off + 16 <= valid_bytes) {
+        *reinterpret_cast<uint4*>(smem + raw_phys<G>(c) * 16) =
+            *reinterpret_cast<const uint4*>(src + off);
+      } else if (off < valid_bytes) {
+        for (int b = 0; b < 16; ++b)
+          if (off + b < valid_bytes) smem[raw_phys<G>(c) * 16 + b] = src[off + b];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: this lane's E consecutive elements (segment = lane)
+  const int rho = lane / LANES;  // row inside the block
+  const int j = lane % LANES;    // lane inside the row
+  float u[E];
+  if constexpr (G::CPL >= 1) {
+#pragma unroll
+    for (int i = 0; i < G::CPL; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + raw_phys<G>(lane * G::CPL + i) * 16);
+      widen16<T>(v, u + i * (16 / (int)sizeof(T)));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) u[r] = load_elem<T>(smem + (lane * E + r) * (int)sizeof(T));
+  }
+
+  if constexpr (HAS_SIGNS) {
+    const int8_t* sg = signs + j * E;
+    if constexpr (E >= 16) {
+#pragma unroll
+      for (int i = 0; i < E / 16; ++i) {
+        const uint4 sv = *reinterpret_cast<const uint4*>(sg + 16 * i);
+        const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t bit = (w[r >> 2] << (24 - 8 * (r & 3))) & 0x80000000u;
+          u[16 * i + r] = u2f(f2u(u[16 * i + r]) ^ bit);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+        u[r] = u2f(f2u(u[r]) ^ (((uint32_t)(uint8_t)sg[r] & 0x80u) << 24));
+    }
+  }
+
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      if (!(r & h)) {
+        const float a = u[r], b = u[r + h];
+        u[r] = a + b;
+        u[r + h] = a - b;
+      }
+    }
+  }
+
+  // ---- phase 2: lane j now holds elements r' * LANES + j
+  if constexpr (LANES > 1) {
+    float* ex = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every raw read has completed before the region is reused
+    float* wb = ex + rho * G::ROWP + j * G::P;
+#pragma unroll
+    for (int r = 0; r < E; r += 4)
+      *reinterpret_cast<float4*>(wb + r) = make_float4(u[r], u[r + 1], u[r + 2], u[r + 3]);
+    __syncthreads();
+    const float* rb = ex + rho * G::ROWP + j;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int owner = (r * LANES) / E;
+      const int pos = (r * LANES) % E;
+      u[r] = rb[owner * G::P + pos];
+    }
+#pragma unroll
+    for (int t = G::LOG_E; t < G::LOG_N; ++t) {
+      const int h = 1 << (t - G::LOG_L);
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        if (!(r & h)) {
+          const float a = u[r], b = u[r + h];
+          u[r] = a + b;
+          u[r + h] = a - b;
+        }
+      }
+    }
+  }
+
+  // ---- absmax over the row
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < E; ++r) amax = fmaxf(amax, fabsf(u[r]));
+#pragma unroll
+  for (int off = 1; off < LANES; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+
+  const uint16_t hb = scale_fp16(amax * c32);
+  const bool subnormal = hb != 0 && hb < 0x0400u;
+  const float mult = hb == 0 ? 0.0f : c32 / h2f(hb);  // +inf scale -> 0
+  const bool row_ok = rho < rows_valid;
+  const int64_t grow = row0 + rho;
+
+  if (o.xrot != nullptr && row_ok) {
+    float* xr = o.xrot + grow * N;
+    if constexpr (LANES > 1) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) xr[r * LANES + j] = u[r] * c32;
+    } else {
+#pragma unroll
+      for (int r = 0; r < E; ++r) xr[r] = u[r] * c32;
+    }
+  }
+  if (j == 0 && row_ok) o.scales[grow] = hb;
+
+  float t[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) t[r] = __builtin_fmaf(u[r], mult, kMagic);
+  if (__ballot(subnormal) != 0) {
+    // only reachable with a subnormal fp16 scale; harmless for normal scales
+#pragma unroll
+    for (int r = 0; r < E; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
+  }
+
+  if constexpr (LANES > 1) {
+    unsigned char* cb = smem;
+    __syncthreads();  // exchange reads done
+#pragma unroll
+    for (int r = 0; r < E; ++r) cb[rho * N + r * LANES + j] = (unsigned char)f2u(t[r]);
+    __syncthreads();
+    constexpr int OUT_CHUNKS = RW * N / 32;  // 16 output bytes = 32 codes
+    const int64_t valid_bytes = (int64_t)rows_valid * (N / 2);
+    uint8_t* dst = o.codes + row0 * (N / 2);
+#pragma unroll
+    for (int c = lane; c < OUT_CHUNKS; c += kWave) {
+      if ((int64_t)c * 16 < valid_bytes) {
+        const uint4* s = reinterpret_cast<const uint4*>(cb + c * 32);
+        const uint4 lo = s[0], hi = s[1];
+        const uint32_t b[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t p0 = b[2 * i] | (b[2 * i] >> 4);
+          const uint32_t p1 = b[2 * i + 1] | (b[2 * i + 1] >> 4);
+          w[i] = __builtin_amdgcn_perm(p1, p0, 0x06040200u) ^ 0x88888888u;
+        }
+        *reinterpret_cast<uint4*>(dst + (int64_t)c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  } else {
+    if (row_ok) {
+      uint8_t* dst = o.codes + grow * (N / 2);
+      if constexpr (N >= 8) {
+        uint32_t w[N / 8];
+#pragma unroll
+        for (int g = 0; g < N / 8; ++g) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc |= ((f2u(t[8 * g + i]) & 0xFu) ^ 0x8u) << (4 * i);
+          w[g] = acc;
+        }
+        if constexpr (N / 2 >= 16) {
+#pragma unroll
+          for (int g = 0; g < N / 8; g += 4)
+            *reinterpret_cast<uint4*>(dst + 4 * g) = make_uint4(w[g], w[g + 1], w[g + 2], w[g + 3]);
+        } else if constexpr (N / 2 == 8) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = w[0];
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < N / 2; ++p) {
+          const uint32_t lo = (f2u(t[2 * p]) & 0xFu) ^ 0x8u;
+          const uint32_t hi = (f2u(t[2 * p + 1]) & 0xFu) ^ 0x8u;
+          dst[p] = (uint8_t)(lo | (hi << 4));
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int N, int E, bool HAS_SIGNS>
+hipError_t launch_one(FQOut o0, FQOut o1, int pairs, int64_t rows, const int8_t* signs,
+                      hipStream_t stream) {
+  using G = Geo<N, E, (int)sizeof(T)>;
+  const int64_t blocks = (rows + G::RW - 1) / G::RW;
+  const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
+  hipLaunchKernelGGL((fwht_quant_kernel<T, N, E, HAS_SIGNS>), dim3((unsigned)blocks, pairs),
+                     dim3(kWave), 0, stream, o0, o1, rows, signs, c32);
+  return hipGetLastError();
+}
+
+template <typename T, bool HAS_SIGNS>
+hipError_t dispatch_n(FQOut o0, FQOut o1, int pairs, int64_t rows, int n, const int8_t* signs,
+                      hipStream_t stream) {
+  switch (n) {
+    case 2: return launch_one<T, 2, 2, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 4: return launch_one<T, 4, 4, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 8: return launch_one<T, 8, 8, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 16: return launch_one<T, 16, 16, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 32: return launch_one<T, 32, 32, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 64: return launch_one<T, 64, 64, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 128: return launch_one<T, 128, 128, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 256: return launch_one<T, 256, 64, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 512: return launch_one<T, 512, 64, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 1024: return launch_one<T, 1024, 64, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 2048: return launch_one<T, 2048, 64, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 4096: return launch_one<T, 4096, 64, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    case 8192: return launch_one<T, 8192, 128, HAS_SIGNS>(o0, o1, pairs, rows, signs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, const int8_t* signs,
+                             uint8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream) {
+  const FQOut o{x, codes, scales, x_rot};
+  if (is_f32) {
+    return signs ? dispatch_n<float, true>(o, o, 1, rows, n, signs, stream)
+                 : dispatch_n<float, false>(o, o, 1, rows, n, signs, stream);
+  }
+  return signs ? dispatch_n<__half, true>(o, o, 1, rows, n, signs, stream)
+               : dispatch_n<__half, false>(o, o, 1, rows, n, signs, stream);
+}
+
+hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
+                                  const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
+                                  uint8_t* v_codes, uint16_t* v_scales, hipStream_t stream) {
+  const FQOut ok{k_in, k_codes, k_scales, nullptr};
+  const FQOut ov{v_in, v_codes, v_scales, nullptr};
+  return signs ? launch_one<__half, 128, 128, true>(ok, ov, 2, rows, signs, stream)
+               : launch_one<__half, 128, 128, false>(ok, ov, 2, rows, signs, stream);
+}
+
+}  // namespace rq

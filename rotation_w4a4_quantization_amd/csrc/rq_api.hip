@@ -1,0 +1,110 @@
+// C ABI of librq (declared in include/rq.h): argument validation on the host,
+// then one kernel launch per call.  Nothing here allocates, synchronises or
+// keeps state between calls.
+#include <hip/hip_runtime.h>
+
+#include "../../include/rq.h"
+#include "rq_internal.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Rows are limited so that every grid dimension fits its hardware limit.
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+int from_hip(hipError_t e) { return e == hipSuccess ? RQ_OK : RQ_ERR_HIP; }
+
+int check_rotation_args(const void* x, int dtype, int64_t m, int64_t n, const int8_t* signs,
+                        const void* codes, const void* scales, const void* rot) {
+  if (dtype != RQ_F16 && dtype != RQ_F32) return RQ_ERR_DTYPE;
+  if (m < 0 || m >= kMaxRows) return RQ_ERR_SHAPE;
+  if (!is_pow2(n) || n < RQ_MIN_N || n > RQ_MAX_N) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return RQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return RQ_ERR_ALIGN;
+  if (signs != nullptr && !aligned16(signs)) return RQ_ERR_ALIGN;
+  if (rot != nullptr && !aligned16(rot)) return RQ_ERR_ALIGN;
+  return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rq_fwht_quant(const void* x, int x_dtype, int64_t m, int64_t n, const int8_t* signs,
+                  uint8_t* codes, uint16_t* scales, float* x_rot, void* stream) {
+  const int st = check_rotation_args(x, x_dtype, m, n, signs, codes, scales, x_rot);
+  if (st != RQ_OK || m == 0) return st;
+  return from_hip(rq::launch_fwht_quant(x, x_dtype == RQ_F32, m, (int)n, signs, codes, scales,
+                                        x_rot, static_cast<hipStream_t>(stream)));
+}
+
+int rq_fold_weights(const void* wt, int wt_dtype, int64_t k, int64_t d, const int8_t* signs,
+                    uint8_t* w_codes, uint16_t* w_scales, float* w_rot, void* stream) {
+  const int st = check_rotation_args(wt, wt_dtype, k, d, signs, w_codes, w_scales, w_rot);
+  if (st != RQ_OK || k == 0) return st;
+  return from_hip(rq::launch_fwht_quant(wt, wt_dtype == RQ_F32, k, (int)d, signs, w_codes,
+                                        w_scales, w_rot, static_cast<hipStream_t>(stream)));
+}
+
+size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d) {
+  (void)m;
+  (void)k;
+  (void)d;
+  return 0;
+}
+
+int rq_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                 const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                 uint16_t* y, int32_t* acc, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (m < 0 || k < 0 || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if (m > 16 && (m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (k == 0) return RQ_ERR_SHAPE;
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr || w_scales == nullptr ||
+      y == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_w4a4_gemm(a_codes, a_scales, m, w_codes, w_scales, k, d, y, acc,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows, int64_t head_dim,
+                       const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
+                       uint8_t* v_codes, uint16_t* v_scales, void* stream) {
+  if (head_dim != 128) return RQ_ERR_SHAPE;
+  if (rows < 0 || rows >= kMaxRows) return RQ_ERR_SHAPE;
+  if (rows == 0) return RQ_OK;
+  if (k_in == nullptr || v_in == nullptr || k_codes == nullptr || k_scales == nullptr ||
+      v_codes == nullptr || v_scales == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(k_in) || !aligned16(v_in) || !aligned16(k_codes) || !aligned16(v_codes))
+    return RQ_ERR_ALIGN;
+  if (signs != nullptr && !aligned16(signs)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_kv_rotate_quant(k_in, v_in, rows, signs, k_codes, k_scales, v_codes,
+                                             v_scales, static_cast<hipStream_t>(stream)));
+}
+
+const char* rq_status_string(int status) {
+  switch (status) {
+    case RQ_OK: return "ok";
+    case RQ_ERR_NULL: return "a required pointer is NULL";
+    case RQ_ERR_SHAPE: return "a size is out of range or not a supported power of two";
+    case RQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case RQ_ERR_DTYPE: return "unknown input dtype";
+    case RQ_ERR_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int rq_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,26 @@
+// Internal launch interface between the C-ABI layer (rq_api.hip) and the
+// kernel translation units.  Arguments reaching these functions have been
+// validated already; they only pick a kernel instantiation and launch it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+// Row-wise (x * s) H_n / sqrt(n) fused with symmetric INT4 quantisation.
+// `is_f32` selects the element type of x (fp32 or fp16).
+hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, const int8_t* signs,
+                             uint8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream);
+
+// Same transform for the two KV tensors (fp16, n = 128) in one launch.
+hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
+                                  const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
+                                  uint8_t* v_codes, uint16_t* v_scales, hipStream_t stream);
+
+// y[m][k] = fp16(acc * sa * sw), acc = qa . qw over d.
+hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                            const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                            uint16_t* y, int32_t* acc, hipStream_t stream);
+
+}  // namespace rq
