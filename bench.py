@@ -58,19 +58,30 @@ def kv_bytes(rows: int) -> int:
 
 
 def time_launches(torch, fn, sets: int, steps: int, warmup: int):
-    """Average per-call milliseconds of fn(i) over `steps` calls (events on the
-    current stream), after `warmup` untimed calls; i cycles over buffer sets."""
+    """Average per-call milliseconds of fn(i), i cycling over buffer sets.
+
+    `warmup` eager calls, then `steps` calls are captured into one HIP graph
+    (so host launch overhead does not starve the GPU), the graph is replayed
+    once untimed, and one replay is timed with HIP events recorded on the
+    stream the kernels run on, between two device synchronisations."""
     for i in range(warmup):
         fn(i % sets)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            fn(i % sets)
+    graph.replay()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        fn(i % sets)
+    graph.replay()
     stop.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    ms = start.elapsed_time(stop) / steps
+    del graph
+    return ms
 
 
 def main():

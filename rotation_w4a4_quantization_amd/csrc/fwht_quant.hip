@@ -46,6 +46,7 @@ namespace rq {
 namespace {
 
 constexpr int kWave = 64;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // fma(v, m, kMagic) = 2^23 + 8 + rne(v*m) for |v*m| < 8: the low 4 bits are
 // the offset-binary code (q + 8); bits 4..22 are zero.
 constexpr float kMagic = 8388616.0f;
@@ -355,6 +356,253 @@ __global__ __launch_bounds__(64) void fwht_quant_kernel(FQOut o0, FQOut o1, int6
   }
 }
 
+// ------------------------------------------------------------------------
+// fp16 rows with 512 <= n <= 8192: one row per wavefront, no LDS exchange.
+//
+// Lane L loads the 16-byte chunks at elements 512*i + 8*L (fully coalesced),
+// so register index rho = 8*i + r holds element e = 512*i + 8*L + r:
+// element bits 0..2 and 9.. live in registers, bits 3..8 in the lane index.
+//   * e0: v_fma_mix_f32 widens the fp16 pair and adds/subtracts in one op
+//     (the sign flip is an xor on the packed fp16 pair before it);
+//   * e1, e2: in registers;
+//   * e3..e6 (lane bits 0..3): v_fmac_f32_dpp, u += g * u[partner], with the
+//     partner lane given by the DPP patterns xor 1, xor 2, xor 7 (row half
+//     mirror) and xor 8 (row rotate by 8).  These four masks span lane bits
+//     0..3, so the butterflies combine the same cosets as the ascending
+//     natural-order FWHT; the per-lane factor g = +-1 picks sum or difference
+//     and leaves each lane's value multiplied by a known sign sigma(L).  The
+//     products are exact, so every result is fp32(a +- b), bit-identical up
+//     to sign with the plain butterfly.  Output index bits 3..6 of lane L are
+//     j(L) = (L0^L2, L1^L2, L0^L1^L2, L3);
+//   * e7, e8 (lane bits 4, 5): v_permlane16_swap / v_permlane32_swap trade
+//     them for register bits 2 and 1 (elements e2, e1, already done), then
+//     e7, e8 and e9.. run in registers.
+// Codes: register bit 0 is still e0, so nibble pairs are formed in
+// registers; bytes are staged in LDS and leave as coalesced 16-byte stores.
+
+#define RQ_DPP8(CTRL, U, G)                                                        \
+  asm volatile("s_nop 1\n"                                                          \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"    \
+               : "+v"((U)[0]), "+v"((U)[1]), "+v"((U)[2]), "+v"((U)[3]), "+v"((U)[4]), \
+                 "+v"((U)[5]), "+v"((U)[6]), "+v"((U)[7])                           \
+               : "v"(G))
+
+// fp16 pair (lo, hi) -> lo + hi and lo - hi in fp32, one rounding each.
+__device__ __forceinline__ float mix_add(uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ __forceinline__ float mix_sub(uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// Is lane L the one receiving the sum in DPP stage k (k = 0..3)?
+__device__ __forceinline__ bool dpp_lower(int L, int k) {
+  const int b0 = L & 1, b1 = (L >> 1) & 1, b2 = (L >> 2) & 1, b3 = (L >> 3) & 1;
+  switch (k) {
+    case 0: return (b0 ^ b2) == 0;
+    case 1: return (b1 ^ b2) == 0;
+    case 2: return b2 == 0;
+    default: return b3 == 0;
+  }
+}
+__device__ __forceinline__ int dpp_partner(int L, int k) {
+  const int m = k == 0 ? 1 : k == 1 ? 2 : k == 2 ? 7 : 8;
+  return L ^ m;
+}
+// sigma after the first k DPP stages: (-1)^(number of stages where L was upper)
+__device__ __forceinline__ float dpp_sigma(int L, int k) {
+  float s = 1.0f;
+  for (int t = 0; t < k; ++t) s = dpp_lower(L, t) ? s : -s;
+  return s;
+}
+
+template <int R>
+__device__ __forceinline__ void butterfly_regs(float (&u)[R], int h) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!(r & h)) {
+      const float a = u[r], b = u[r + h];
+      u[r] = a + b;
+      u[r + h] = a - b;
+    }
+  }
+}
+
+constexpr int kRowWaves = 4;  // rows (wavefronts) per 256-thread workgroup
+
+template <int N, bool HAS_SIGNS>
+__global__ __launch_bounds__(64 * kRowWaves) void fwht_row_kernel(FQOut o, int64_t rows,
+                                                                 const int8_t* __restrict__ signs,
+                                                                 float c32) {
+  constexpr int R = N / 64;   // elements per lane
+  constexpr int NI = N / 512; // 16-byte loads per lane
+  static_assert(N >= 512 && N <= 8192, "row kernel covers 512..8192");
+  __shared__ __align__(16) unsigned char cb_all[kRowWaves][N / 2];
+
+  const int L = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  unsigned char* cb = cb_all[wave];
+  const int64_t row_id = (int64_t)blockIdx.x * kRowWaves + wave;
+  const bool row_ok = row_id < rows;
+  const int64_t row = row_ok ? row_id : rows - 1;  // tail waves recompute the last row, store nothing
+  const __half* xr = static_cast<const __half*>(o.x) + row * N;
+
+  // streaming input: nontemporal loads (read once, no reuse to keep in cache)
+  uint4 raw[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xr + 512 * i + 8 * L));
+    raw[i] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
+  uint2 sg[NI];
+  if constexpr (HAS_SIGNS) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sg[i] = *reinterpret_cast<const uint2*>(signs + 512 * i + 8 * L);
+  }
+
+  // per-lane DPP factors and the final sign of this lane's values
+  float g[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int P = dpp_partner(L & 15, k);
+    const float lo = dpp_lower(L & 15, k) ? 1.0f : -1.0f;
+    g[k] = lo * dpp_sigma(L & 15, k) * dpp_sigma(P, k);
+  }
+  const float sigma = dpp_sigma(L & 15, 4);
+
+  float u[R];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t w = w4[p];
+      if constexpr (HAS_SIGNS) {
+        const uint32_t s2 = p < 2 ? sg[i].x : sg[i].y;
+        const uint32_t b0 = (2u * p) & 3u;
+        const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
+        w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;  // sign bits of s_2p, s_2p+1
+      }
+      u[8 * i + 2 * p] = mix_add(w);
+      u[8 * i + 2 * p + 1] = mix_sub(w);
+    }
+  }
+  butterfly_regs(u, 2);  // e1
+  butterfly_regs(u, 4);  // e2
+
+#pragma unroll
+  for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[1,0,3,2]", u + b, g[0]);  // e3
+#pragma unroll
+  for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[2,3,0,1]", u + b, g[1]);  // e4
+#pragma unroll
+  for (int b = 0; b < R; b += 8) RQ_DPP8("row_half_mirror", u + b, g[2]);      // e5
+#pragma unroll
+  for (int b = 0; b < R; b += 8) RQ_DPP8("row_ror:8", u + b, g[3]);            // e6
+
+  // lane bit 4 (e7) <-> register bit 2 (e2); lane bit 5 (e8) <-> register bit 1 (e1)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!(r & 4)) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(f2u(u[r]), f2u(u[r + 4]), false, false);
+      u[r] = u2f(sw[0]);
+      u[r + 4] = u2f(sw[1]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!(r & 2)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(f2u(u[r]), f2u(u[r + 2]), false, false);
+      u[r] = u2f(sw[0]);
+      u[r + 2] = u2f(sw[1]);
+    }
+  }
+  butterfly_regs(u, 4);  // e7
+  butterfly_regs(u, 2);  // e8
+#pragma unroll
+  for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
+
+  // absmax over the row (every lane holds part of the same row)
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) amax = fmaxf(amax, fabsf(u[r]));
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+
+  const uint16_t hb = scale_fp16(amax * c32);
+  const bool subnormal = hb != 0 && hb < 0x0400u;
+  const float mult = (hb == 0 ? 0.0f : c32 / h2f(hb)) * sigma;
+  if (L == 0 && row_ok) o.scales[row] = hb;
+
+  // element index pieces of this lane
+  const int L0 = L & 1, L1 = (L >> 1) & 1, L2 = (L >> 2) & 1, L3 = (L >> 3) & 1;
+  const int j = (L0 ^ L2) | ((L1 ^ L2) << 1) | ((L0 ^ L1 ^ L2) << 2) | (L3 << 3);
+  const int lane_pair = ((L >> 5) & 1) | (((L >> 4) & 1) << 1) | (j << 2);  // byte index bits 0..5
+
+  if (o.xrot != nullptr && row_ok) {
+    float* xo = o.xrot + row * N;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = (r & 1) | (lane_pair << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8) |
+                    ((r >> 3) << 9);
+      xo[e] = (u[r] * sigma) * c32;
+    }
+  }
+
+  float t[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) t[r] = __builtin_fmaf(u[r], mult, kMagic);
+  if (__ballot(subnormal) != 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
+  }
+#pragma unroll
+  for (int r = 0; r < R; r += 2) {
+    const uint32_t byte = (f2u(t[r + 1]) << 4) | f2u(t[r]);  // low byte: (q1+8)<<4 | (q0+8)
+    const int p = lane_pair | (((r >> 2) & 1) << 6) | (((r >> 1) & 1) << 7) | ((r >> 3) << 8);
+    cb[p] = (unsigned char)byte;
+  }
+  __syncthreads();
+  uint8_t* dst = o.codes + row * (N / 2);
+#pragma unroll
+  for (int c = L; c < N / 32 && row_ok; c += 64) {
+    v4u v = *reinterpret_cast<const v4u*>(cb + 16 * c);
+    v ^= 0x88888888u;
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(dst + 16 * c));
+  }
+}
+
+template <int N, bool HAS_SIGNS>
+hipError_t launch_row(FQOut o, int64_t rows, const int8_t* signs, hipStream_t stream) {
+  const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
+  const int64_t blocks = (rows + kRowWaves - 1) / kRowWaves;
+  hipLaunchKernelGGL((fwht_row_kernel<N, HAS_SIGNS>), dim3((unsigned)blocks), dim3(kWave * kRowWaves),
+                     0, stream, o, rows, signs, c32);
+  return hipGetLastError();
+}
+
+template <bool HAS_SIGNS>
+hipError_t dispatch_row(FQOut o, int64_t rows, int n, const int8_t* signs, hipStream_t stream) {
+  switch (n) {
+    case 512: return launch_row<512, HAS_SIGNS>(o, rows, signs, stream);
+    case 1024: return launch_row<1024, HAS_SIGNS>(o, rows, signs, stream);
+    case 2048: return launch_row<2048, HAS_SIGNS>(o, rows, signs, stream);
+    case 4096: return launch_row<4096, HAS_SIGNS>(o, rows, signs, stream);
+    case 8192: return launch_row<8192, HAS_SIGNS>(o, rows, signs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int N, int E, bool HAS_SIGNS>
 hipError_t launch_one(FQOut o0, FQOut o1, int pairs, int64_t rows, const int8_t* signs,
                       hipStream_t stream) {
@@ -395,6 +643,10 @@ hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, co
   if (is_f32) {
     return signs ? dispatch_n<float, true>(o, o, 1, rows, n, signs, stream)
                  : dispatch_n<float, false>(o, o, 1, rows, n, signs, stream);
+  }
+  if (n >= 512) {
+    return signs ? dispatch_row<true>(o, rows, n, signs, stream)
+                 : dispatch_row<false>(o, rows, n, signs, stream);
   }
   return signs ? dispatch_n<__half, true>(o, o, 1, rows, n, signs, stream)
                : dispatch_n<__half, false>(o, o, 1, rows, n, signs, stream);
