@@ -582,6 +582,121 @@ __global__ __launch_bounds__(64 * kRowWaves) void fwht_row_kernel(FQOut o, int64
   }
 }
 
+// ------------------------------------------------------------------------
+// fp16 rows with n = 128 (the per-head KV rotation): four lanes per row,
+// sixteen rows per wavefront, 32 elements per lane, no LDS.
+//
+// Lane l (row l/4, quarter q = l%4) loads the 16-byte chunks q + 4i, i = 0..3,
+// so register index rho = 8i + r holds element e = 32i + 8q + r: element bits
+// 0..2 and 5..6 live in registers, bits 3..4 in the quarter index.  e0 uses
+// v_fma_mix_f32 (widen + add/sub), e1, e2, e5, e6 run in registers and e3, e4
+// use v_fmac_f32_dpp with quad_perm partners (xor 1, xor 2).  The DPP factor
+// g = +-1 leaves the values multiplied by sigma(q) = g0 * g1, which is folded
+// into the quantisation multiplier.  Output order is natural.
+template <bool HAS_SIGNS>
+__global__ __launch_bounds__(256) void fwht128_quad_kernel(FQOut o0, FQOut o1, int64_t rows,
+                                                          const int8_t* __restrict__ signs,
+                                                          float c32) {
+  constexpr int N = 128;
+  const FQOut o = blockIdx.y ? o1 : o0;
+  const int L = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = L & 3;
+  const int64_t row_id = ((int64_t)blockIdx.x * 4 + wave) * 16 + (L >> 2);
+  const bool row_ok = row_id < rows;
+  const int64_t row = row_ok ? row_id : rows - 1;
+  const __half* xr = static_cast<const __half*>(o.x) + row * N;
+
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xr + 8 * (q + 4 * i)));
+    raw[i] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
+  uint2 sg[4];
+  if constexpr (HAS_SIGNS) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sg[i] = *reinterpret_cast<const uint2*>(signs + 8 * (q + 4 * i));
+  }
+  const float g0 = (q & 1) ? -1.0f : 1.0f;
+  const float g1 = (q & 2) ? -1.0f : 1.0f;
+  const float sigma = g0 * g1;
+
+  float u[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t w = w4[p];
+      if constexpr (HAS_SIGNS) {
+        const uint32_t s2 = p < 2 ? sg[i].x : sg[i].y;
+        const uint32_t b0 = (2u * p) & 3u;
+        const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
+        w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;
+      }
+      u[8 * i + 2 * p] = mix_add(w);
+      u[8 * i + 2 * p + 1] = mix_sub(w);
+    }
+  }
+  butterfly_regs(u, 2);  // e1
+  butterfly_regs(u, 4);  // e2
+#pragma unroll
+  for (int b = 0; b < 32; b += 8) RQ_DPP8("quad_perm:[1,0,3,2]", u + b, g0);  // e3
+#pragma unroll
+  for (int b = 0; b < 32; b += 8) RQ_DPP8("quad_perm:[2,3,0,1]", u + b, g1);  // e4
+  butterfly_regs(u, 8);   // e5
+  butterfly_regs(u, 16);  // e6
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(u[r]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+
+  const uint16_t hb = scale_fp16(amax * c32);
+  const bool subnormal = hb != 0 && hb < 0x0400u;
+  const float mult = (hb == 0 ? 0.0f : c32 / h2f(hb)) * sigma;
+  if (q == 0 && row_ok) o.scales[row] = hb;
+  if (o.xrot != nullptr && row_ok) {
+    float* xo = o.xrot + row * N;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) xo[32 * (r >> 3) + 8 * q + (r & 7)] = (u[r] * sigma) * c32;
+  }
+
+  float t[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) t[r] = __builtin_fmaf(u[r], mult, kMagic);
+  if (__ballot(subnormal) != 0) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
+  }
+  if (row_ok) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(o.codes + row * (N / 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // 8 offset-binary codes -> one word of two's-complement nibbles
+      uint32_t b[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = (f2u(t[8 * i + 2 * p + 1]) << 4) | f2u(t[8 * i + 2 * p]);
+      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // bytes b0.0, b1.0
+      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);  // bytes b2.0, b3.0 at 2, 3
+      // codes of elements 32i + 8q .. +7 are bytes 16i + 4q .. +3 of the row
+      __builtin_nontemporal_store((lo | hi) ^ 0x88888888u, dst + 4 * i + q);
+    }
+  }
+}
+
+template <bool HAS_SIGNS>
+hipError_t launch_quad(FQOut o0, FQOut o1, int pairs, int64_t rows, const int8_t* signs,
+                       hipStream_t stream) {
+  const float c32 = (float)(1.0 / __builtin_sqrt(128.0));
+  const int64_t blocks = (rows + 63) / 64;
+  hipLaunchKernelGGL((fwht128_quad_kernel<HAS_SIGNS>), dim3((unsigned)blocks, pairs), dim3(256), 0,
+                     stream, o0, o1, rows, signs, c32);
+  return hipGetLastError();
+}
+
 template <int N, bool HAS_SIGNS>
 hipError_t launch_row(FQOut o, int64_t rows, const int8_t* signs, hipStream_t stream) {
   const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
@@ -648,6 +763,10 @@ hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, co
     return signs ? dispatch_row<true>(o, rows, n, signs, stream)
                  : dispatch_row<false>(o, rows, n, signs, stream);
   }
+  if (n == 128) {
+    return signs ? launch_quad<true>(o, o, 1, rows, signs, stream)
+                 : launch_quad<false>(o, o, 1, rows, signs, stream);
+  }
   return signs ? dispatch_n<__half, true>(o, o, 1, rows, n, signs, stream)
                : dispatch_n<__half, false>(o, o, 1, rows, n, signs, stream);
 }
@@ -657,8 +776,8 @@ hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, in
                                   uint8_t* v_codes, uint16_t* v_scales, hipStream_t stream) {
   const FQOut ok{k_in, k_codes, k_scales, nullptr};
   const FQOut ov{v_in, v_codes, v_scales, nullptr};
-  return signs ? launch_one<__half, 128, 128, true>(ok, ov, 2, rows, signs, stream)
-               : launch_one<__half, 128, 128, false>(ok, ov, 2, rows, signs, stream);
+  return signs ? launch_quad<true>(ok, ov, 2, rows, signs, stream)
+               : launch_quad<false>(ok, ov, 2, rows, signs, stream);
 }
 
 }  // namespace rq
