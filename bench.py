@@ -57,6 +57,22 @@ def kv_bytes(rows: int) -> int:
     return 2 * (rows * 128 * 2 + rows * 64 + rows * 2)
 
 
+def measured_traffic(kernel_source: str, summary: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel source changed since it was measured."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, summary)) as f:
+            rec = json.load(f)
+        with open(os.path.join(root, kernel_source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == sha else None
+
+
 def time_launches(torch, fn, sets: int, steps: int, warmup: int):
     """Average per-call milliseconds of fn(i), i cycling over buffer sets.
 
@@ -153,8 +169,10 @@ def main():
                                "per-token INT4", "tokens": m, "n": n, "input_dtype": "fp16",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "fwht_quant_kernel<__half, 4096, 64>",
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("rotation_w4a4_quantization_amd/csrc/fwht_quant.hip",
+                                                 "profiles/fwht_quant_4096x4096_traffic.json"),
+                     "kernel": "fwht_row_kernel<4096, true>",
                      "algorithmic_bytes_per_launch": nbytes},
         "wall_s_timed_region": round(wall, 3),
     }
