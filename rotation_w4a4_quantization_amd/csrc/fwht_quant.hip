@@ -40,6 +40,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "rq_internal.h"
 
 namespace rq {
@@ -439,10 +441,45 @@ __device__ __forceinline__ void butterfly_regs(float (&u)[R], int h) {
   }
 }
 
-constexpr int kRowWaves = 4;  // rows (wavefronts) per 256-thread workgroup
+constexpr int kRowWaves = 4;  // wavefronts per 256-thread workgroup
 
+// Max over the 64 lanes of a wavefront, returned in every lane.  Within each
+// 16-lane row: DPP max against lane^1, lane^2, the mirrored half row and the
+// mirrored row; across rows: permlane16/32 swaps (each lane sees its own value
+// and that of lane^16, then lane^32).
+__device__ __forceinline__ float wave_max(float m) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"
+      : "+v"(m));
+  const auto a = __builtin_amdgcn_permlane16_swap(f2u(m), f2u(m), false, false);
+  m = fmaxf(u2f(a[0]), u2f(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(f2u(m), f2u(m), false, false);
+  return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+
+template <int NI>
+__device__ __forceinline__ void load_row(uint4 (&raw)[NI], const __half* xr, int L) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xr + 512 * i + 8 * L));
+    raw[i] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
+}
+
+// Each wavefront walks rows w, w + W, w + 2W, ... (W = wavefronts in the
+// grid, sized to four resident wavefronts per SIMD).  For n <= 4096 the kernel
+// stays within 128 VGPRs so that four wavefronts share each SIMD: while one
+// waits for its row, the others keep the VALU busy.  Sign bytes are re-read
+// per row (L1/L2 hits) rather than held in registers for the same reason.
 template <int N, bool HAS_SIGNS>
-__global__ __launch_bounds__(64 * kRowWaves) void fwht_row_kernel(FQOut o, int64_t rows,
+__global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_kernel(FQOut o, int64_t rows,
                                                                  const int8_t* __restrict__ signs,
                                                                  float c32) {
   constexpr int R = N / 64;   // elements per lane
@@ -453,23 +490,9 @@ __global__ __launch_bounds__(64 * kRowWaves) void fwht_row_kernel(FQOut o, int64
   const int L = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   unsigned char* cb = cb_all[wave];
-  const int64_t row_id = (int64_t)blockIdx.x * kRowWaves + wave;
-  const bool row_ok = row_id < rows;
-  const int64_t row = row_ok ? row_id : rows - 1;  // tail waves recompute the last row, store nothing
-  const __half* xr = static_cast<const __half*>(o.x) + row * N;
-
-  // streaming input: nontemporal loads (read once, no reuse to keep in cache)
-  uint4 raw[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xr + 512 * i + 8 * L));
-    raw[i] = make_uint4(t[0], t[1], t[2], t[3]);
-  }
-  uint2 sg[NI];
-  if constexpr (HAS_SIGNS) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) sg[i] = *reinterpret_cast<const uint2*>(signs + 512 * i + 8 * L);
-  }
+  const int64_t stride = (int64_t)gridDim.x * kRowWaves;
+  int64_t row = (int64_t)blockIdx.x * kRowWaves + wave;
+  if (row >= rows) return;  // uniform per wavefront
 
   // per-lane DPP factors and the final sign of this lane's values
   float g[4];
@@ -480,105 +503,130 @@ __global__ __launch_bounds__(64 * kRowWaves) void fwht_row_kernel(FQOut o, int64
     g[k] = lo * dpp_sigma(L & 15, k) * dpp_sigma(P, k);
   }
   const float sigma = dpp_sigma(L & 15, 4);
-
-  float u[R];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t w = w4[p];
-      if constexpr (HAS_SIGNS) {
-        const uint32_t s2 = p < 2 ? sg[i].x : sg[i].y;
-        const uint32_t b0 = (2u * p) & 3u;
-        const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
-        w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;  // sign bits of s_2p, s_2p+1
-      }
-      u[8 * i + 2 * p] = mix_add(w);
-      u[8 * i + 2 * p + 1] = mix_sub(w);
-    }
-  }
-  butterfly_regs(u, 2);  // e1
-  butterfly_regs(u, 4);  // e2
-
-#pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[1,0,3,2]", u + b, g[0]);  // e3
-#pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[2,3,0,1]", u + b, g[1]);  // e4
-#pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("row_half_mirror", u + b, g[2]);      // e5
-#pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("row_ror:8", u + b, g[3]);            // e6
-
-  // lane bit 4 (e7) <-> register bit 2 (e2); lane bit 5 (e8) <-> register bit 1 (e1)
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (!(r & 4)) {
-      const auto sw = __builtin_amdgcn_permlane16_swap(f2u(u[r]), f2u(u[r + 4]), false, false);
-      u[r] = u2f(sw[0]);
-      u[r + 4] = u2f(sw[1]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (!(r & 2)) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(f2u(u[r]), f2u(u[r + 2]), false, false);
-      u[r] = u2f(sw[0]);
-      u[r + 2] = u2f(sw[1]);
-    }
-  }
-  butterfly_regs(u, 4);  // e7
-  butterfly_regs(u, 2);  // e8
-#pragma unroll
-  for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
-
-  // absmax over the row (every lane holds part of the same row)
-  float amax = 0.0f;
-#pragma unroll
-  for (int r = 0; r < R; ++r) amax = fmaxf(amax, fabsf(u[r]));
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-
-  const uint16_t hb = scale_fp16(amax * c32);
-  const bool subnormal = hb != 0 && hb < 0x0400u;
-  const float mult = (hb == 0 ? 0.0f : c32 / h2f(hb)) * sigma;
-  if (L == 0 && row_ok) o.scales[row] = hb;
-
   // element index pieces of this lane
   const int L0 = L & 1, L1 = (L >> 1) & 1, L2 = (L >> 2) & 1, L3 = (L >> 3) & 1;
   const int j = (L0 ^ L2) | ((L1 ^ L2) << 1) | ((L0 ^ L1 ^ L2) << 2) | (L3 << 3);
   const int lane_pair = ((L >> 5) & 1) | (((L >> 4) & 1) << 1) | (j << 2);  // byte index bits 0..5
 
-  if (o.xrot != nullptr && row_ok) {
-    float* xo = o.xrot + row * N;
+  for (;;) {
+    uint4 raw[NI];
+    load_row(raw, static_cast<const __half*>(o.x) + row * N, L);
+    uint2 sg[NI];
+    if constexpr (HAS_SIGNS) {
+      const int8_t* sp = signs;
+      asm volatile("" : "+s"(sp));  // re-read per row, not hoisted into registers
+#pragma unroll
+      for (int i = 0; i < NI; ++i) sg[i] = *reinterpret_cast<const uint2*>(sp + 512 * i + 8 * L);
+    }
+    // Opaque per iteration: keeps the compiler from hoisting one address
+    // register per stored element out of the loop (they fold into immediate
+    // offsets instead).
+    int lp = lane_pair;
+    asm volatile("" : "+v"(lp));
+    float u[R];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t w = w4[p];
+        if constexpr (HAS_SIGNS) {
+          const uint32_t s2 = p < 2 ? sg[i].x : sg[i].y;
+          const uint32_t b0 = (2u * p) & 3u;
+          const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
+          w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;  // sign bits of s_2p, s_2p+1
+        }
+        u[8 * i + 2 * p] = mix_add(w);
+        u[8 * i + 2 * p + 1] = mix_sub(w);
+      }
+    }
+    const int64_t next = row + stride;
+    const bool more = next < rows;
+
+    butterfly_regs(u, 2);  // e1
+    butterfly_regs(u, 4);  // e2
+#pragma unroll
+    for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[1,0,3,2]", u + b, g[0]);  // e3
+#pragma unroll
+    for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[2,3,0,1]", u + b, g[1]);  // e4
+#pragma unroll
+    for (int b = 0; b < R; b += 8) RQ_DPP8("row_half_mirror", u + b, g[2]);      // e5
+#pragma unroll
+    for (int b = 0; b < R; b += 8) RQ_DPP8("row_ror:8", u + b, g[3]);            // e6
+
+    // lane bit 4 (e7) <-> register bit 2 (e2); lane bit 5 (e8) <-> register bit 1 (e1)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int e = (r & 1) | (lane_pair << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8) |
-                    ((r >> 3) << 9);
-      xo[e] = (u[r] * sigma) * c32;
+      if (!(r & 4)) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(f2u(u[r]), f2u(u[r + 4]), false, false);
+        u[r] = u2f(sw[0]);
+        u[r + 4] = u2f(sw[1]);
+      }
     }
-  }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!(r & 2)) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(f2u(u[r]), f2u(u[r + 2]), false, false);
+        u[r] = u2f(sw[0]);
+        u[r + 2] = u2f(sw[1]);
+      }
+    }
+    butterfly_regs(u, 4);  // e7
+    butterfly_regs(u, 2);  // e8
+#pragma unroll
+    for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
 
-  float t[R];
+    float amax = 0.0f;
 #pragma unroll
-  for (int r = 0; r < R; ++r) t[r] = __builtin_fmaf(u[r], mult, kMagic);
-  if (__ballot(subnormal) != 0) {
+    for (int r = 0; r < R; ++r) amax = fmaxf(amax, fabsf(u[r]));
+    amax = wave_max(amax);
+
+    const uint16_t hb = scale_fp16(amax * c32);
+    const bool subnormal = hb != 0 && hb < 0x0400u;
+    const float mult = (hb == 0 ? 0.0f : c32 / h2f(hb)) * sigma;
+    if (L == 0) o.scales[row] = hb;
+
+    if (o.xrot != nullptr) {
+      float* xo = o.xrot + row * N;
 #pragma unroll
-    for (int r = 0; r < R; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
-  }
+      for (int r = 0; r < R; ++r) {
+        const int e = (r & 1) | (lp << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8) |
+                      ((r >> 3) << 9);
+        xo[e] = (u[r] * sigma) * c32;
+      }
+    }
+
+    float t[R];
 #pragma unroll
-  for (int r = 0; r < R; r += 2) {
-    const uint32_t byte = (f2u(t[r + 1]) << 4) | f2u(t[r]);  // low byte: (q1+8)<<4 | (q0+8)
-    const int p = lane_pair | (((r >> 2) & 1) << 6) | (((r >> 1) & 1) << 7) | ((r >> 3) << 8);
-    cb[p] = (unsigned char)byte;
-  }
-  __syncthreads();
-  uint8_t* dst = o.codes + row * (N / 2);
+    for (int r = 0; r < R; ++r) t[r] = __builtin_fmaf(u[r], mult, kMagic);
+    if (subnormal) {  // uniform: the scale is shared by the whole row
 #pragma unroll
-  for (int c = L; c < N / 32 && row_ok; c += 64) {
-    v4u v = *reinterpret_cast<const v4u*>(cb + 16 * c);
-    v ^= 0x88888888u;
-    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(dst + 16 * c));
+      for (int r = 0; r < R; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
+    }
+    // The wavefront stages its row's code bytes in its own LDS slice and
+    // reads them back as 16-byte chunks; LDS instructions of one wavefront
+    // execute in order, so only the compiler needs fencing here.
+#pragma unroll
+    for (int r = 0; r < R; r += 2) {
+      const uint32_t byte = (f2u(t[r + 1]) << 4) | f2u(t[r]);  // low byte: (q1+8)<<4 | (q0+8)
+      const int p = (((r >> 2) & 1) << 6) | (((r >> 1) & 1) << 7) | ((r >> 3) << 8);
+      cb[lp + p] = (unsigned char)byte;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint8_t* dst = o.codes + row * (N / 2);
+#pragma unroll
+    for (int c = L; c < N / 32; c += 64) {
+      v4u v = *reinterpret_cast<const v4u*>(cb + 16 * c);
+      v ^= 0x88888888u;
+      __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(dst + 16 * c));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (!more) break;
+    row = next;
   }
 }
 
@@ -697,10 +745,34 @@ hipError_t launch_quad(FQOut o0, FQOut o1, int pairs, int64_t rows, const int8_t
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Resident wavefronts per SIMD the row kernel is sized for (its VGPR budget).
+template <int N>
+constexpr int row_waves_per_simd() { return N <= 4096 ? 4 : 2; }
+
 template <int N, bool HAS_SIGNS>
 hipError_t launch_row(FQOut o, int64_t rows, const int8_t* signs, hipStream_t stream) {
   const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
-  const int64_t blocks = (rows + kRowWaves - 1) / kRowWaves;
+  const int64_t max_waves = (int64_t)cu_count() * 4 * row_waves_per_simd<N>();
+  int64_t waves = rows < max_waves ? rows : max_waves;
+  const int64_t per_wave = (rows + waves - 1) / waves;  // rows per wavefront, balanced
+  waves = (rows + per_wave - 1) / per_wave;
+  const int64_t blocks = (waves + kRowWaves - 1) / kRowWaves;
   hipLaunchKernelGGL((fwht_row_kernel<N, HAS_SIGNS>), dim3((unsigned)blocks), dim3(kWave * kRowWaves),
                      0, stream, o, rows, signs, c32);
   return hipGetLastError();
