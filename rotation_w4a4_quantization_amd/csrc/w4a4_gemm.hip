@@ -205,29 +205,42 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_kernel(
 // ------------------------------------------------------------ large GEMM
 // 256 x 224 output tile per 512-thread block: 8 waves in a 4 x 2 grid of
 // 64 x 112 wave tiles (4 x 7 MFMA 16x16x64 tiles, 112 int32 accumulators per
-// lane, so two waves fit on each SIMD and cover each other's LDS and global
-// latency).  K runs in steps of 128 codes.  Each step's packed A and B tiles
-// (64 bytes per row) are loaded into registers one step ahead, widened to
-// int8 once, and stored into the other of two LDS buffers (128 bytes per
-// row); the MFMA loop only reads 16-byte fragments.  The 16-byte chunk index
-// of a row is XORed with bits 1..3 of the row, so both the stores and the
-// fragment reads are free of bank conflicts.  For 2048 x 28672 the 256 x 224
-// tile gives exactly 1024 tiles, four per CU.
-constexpr int LM = 256, LN = 224, LK = 128;        // block tile (codes)
-constexpr int LPK = LK / 2;                         // packed bytes per row per step
-constexpr int LROW = LK;                            // widened bytes per row per step
-constexpr int LBUF = (LM + LN) * LROW;              // one LDS buffer: 60 KB
+// lane).  K runs in steps of 256 codes (128 packed bytes per row).
+//
+// Loads go straight from global memory into LDS (global_load_lds_dwordx4: no
+// staging registers) one step ahead into the other of two 64 KB buffers, and
+// the tiles stay packed in LDS.  Each wave issues four 8-row A and four 8-row
+// B loads per step (the B tile is padded to 256 rows so that the count is the
+// same for every wave) and waits for them only at the end of the step, so
+// each load has a whole step of MFMA work to arrive, and the block meets at
+// one barrier per 256 codes.
+//
+// LDS layout per buffer: 256 A rows then 256 B rows, 128 bytes each; the
+// 16-byte part p of row r sits at part position p ^ (r & 7), so the 8-lane
+// phases of the 16-byte fragment reads hit 8 different bank groups.  A DMA
+// load writes lane L's 16 bytes at M0 + 16 L, so lane L of the load of rows
+// r0..r0+7 fetches the global part that belongs at position L & 7 of row
+// r0 + L / 8.
+//
+// Fragments: a step is two halves of 128 codes; in half u, lane
+// (g = lane / 16, r = lane % 16) reads part 4u + g of its row (16 bytes = 32
+// codes) and feeds the first 16 codes to one MFMA and the last 16 to the next.
+// A and B use the same assignment, so every code meets its partner exactly
+// once.  For 2048 x 28672 the tile gives exactly 1024 tiles, four per CU.
+constexpr int LM = 256, LN = 224, LK = 256;  // block tile (codes)
+constexpr int LPK = LK / 2;                   // packed bytes per row per step
+constexpr int LBROWS = 256;                   // B rows per buffer (224 used)
+constexpr int LBUF = (LM + LBROWS) * LPK;     // one LDS buffer: 64 KB
 constexpr int LTHREADS = 512;
 
-__device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * LROW + 16 * (chunk ^ ((row >> 1) & 7));
-}
+__device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); }
 
-// packed chunk (32 codes) -> two widened 16-byte chunks at chunk positions 2p, 2p+1
-__device__ __forceinline__ void stash_chunk(unsigned char* buf, int row, int part, uint4 v) {
-  *reinterpret_cast<v4i*>(buf + tile_off(row, 2 * part)) = widen(v.x, v.y);
-  *reinterpret_cast<v4i*>(buf + tile_off(row, 2 * part + 1)) = widen(v.z, v.w);
-}
+// One 8-row DMA load: lane L's 16 bytes go to LDS byte m0 + 16 L.
+#define RQ_DMA(M0, ADDR)                                                           \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"     \
+               :                                                                   \
+               : "v"(ADDR), "s"(M0)                                                \
+               : "memory", "m0")
 
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
@@ -240,25 +253,39 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   __shared__ __align__(16) unsigned char lds[2 * LBUF];
   const int64_t m0 = (int64_t)(blockIdx.x % tiles_m) * LM;
   const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * LN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x 112
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t rowb = d / 2;
+  const int steps = (int)(rowb / LPK);
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
-  // staging: thread tid moves the packed 16-byte part tid % 4 of rows
-  // tid / 4 and tid / 4 + 128 of the A tile and of the B tile (the second B
-  // row exists for rows < 224).  Rows past the matrix edge re-read the last
-  // row; their results are never stored.  Tile-relative offsets fit in 32 bits.
-  const int srow = tid >> 2, part = tid & 3;
-  const uint8_t* a_base = a_codes + m0 * rowb + 16 * part;
-  const uint8_t* b_base = w_codes + n0 * rowb + 16 * part;
-  const int a_last = (int)(m - 1 - m0), b_last = (int)(k - 1 - n0);
-  const int ar0 = (srow < a_last ? srow : a_last) * (int)rowb;
-  const int ar1 = (srow + 128 < a_last ? srow + 128 : a_last) * (int)rowb;
-  const int br0 = (srow < b_last ? srow : b_last) * (int)rowb;
-  const int brl = srow + 128 < LN ? srow + 128 : LN - 1;
-  const int br1 = (brl < b_last ? brl : b_last) * (int)rowb;
-  const bool b2 = srow + 128 < LN;
+  // DMA sources of this lane: row 32 wave + 8 t + lane / 8 (t = 0..3) of the
+  // A tile and of the (padded) B tile; rows past the matrix edge re-read the
+  // last row (their results are never stored).
+  const uint8_t* asrc[4];
+  const uint8_t* bsrc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 32 * wave + 8 * t + (lane >> 3);
+    const int p = part_pos(r, lane & 7);
+    const int64_t ar = m0 + r < m ? m0 + r : m - 1;
+    const int64_t brr = r < LN ? n0 + r : n0 + LN - 1;
+    const int64_t br = brr < k ? brr : k - 1;
+    asrc[t] = a_codes + ar * rowb + 16 * p;
+    bsrc[t] = w_codes + br * rowb + 16 * p;
+  }
+#define RQ_ISSUE(STEP)                                                              \
+  do {                                                                              \
+    const uint32_t buf_ = lds_base + (uint32_t)(((STEP) & 1) * LBUF);               \
+    const int64_t kb_ = (int64_t)(STEP) * LPK;                                      \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
+      RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * LPK), asrc[t] + kb_);          \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
+      RQ_DMA(buf_ + (uint32_t)((LM + 32 * wave + 8 * t) * LPK), bsrc[t] + kb_);     \
+  } while (0)
 
   v4i acc[4][7];
 #pragma unroll
@@ -266,49 +293,48 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #pragma unroll
     for (int j = 0; j < 7; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  uint4 ra0, ra1, rb0, rb1 = make_uint4(0, 0, 0, 0);
-  const int steps = (int)(rowb / LPK);
-  ra0 = *reinterpret_cast<const uint4*>(a_base + ar0);
-  ra1 = *reinterpret_cast<const uint4*>(a_base + ar1);
-  rb0 = *reinterpret_cast<const uint4*>(b_base + br0);
-  if (b2) rb1 = *reinterpret_cast<const uint4*>(b_base + br1);
-  stash_chunk(lds, srow, part, ra0);
-  stash_chunk(lds, srow + 128, part, ra1);
-  stash_chunk(lds + LM * LROW, srow, part, rb0);
-  if (b2) stash_chunk(lds + LM * LROW, srow + 128, part, rb1);
-  __syncthreads();
+  // fragment offsets of this lane inside a 16-row group, halves 0 and 1
+  const int frag_off0 = r16 * LPK + 16 * part_pos(r16, g);
+  const int frag_off1 = r16 * LPK + 16 * part_pos(r16, 4 + g);
+
+  RQ_ISSUE(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
   for (int s = 0; s < steps; ++s) {
+    if (s + 1 < steps) RQ_ISSUE(s + 1);
     const unsigned char* cur = lds + (s & 1) * LBUF;
-    unsigned char* nxt = lds + ((s + 1) & 1) * LBUF;
-    if (s + 1 < steps) {
-      const int64_t kb = (int64_t)(s + 1) * LPK;
-      ra0 = *reinterpret_cast<const uint4*>(a_base + ar0 + kb);
-      ra1 = *reinterpret_cast<const uint4*>(a_base + ar1 + kb);
-      rb0 = *reinterpret_cast<const uint4*>(b_base + br0 + kb);
-      if (b2) rb1 = *reinterpret_cast<const uint4*>(b_base + br1 + kb);
-    }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v4i bf[7];
-#pragma unroll
-      for (int j = 0; j < 7; ++j)
-        bf[j] = *reinterpret_cast<const v4i*>(cur + LM * LROW + tile_off(wn * 112 + j * 16 + r16, 4 * ks + g));
+    for (int u = 0; u < 2; ++u) {
+      const int fo = u ? frag_off1 : frag_off0;
+      v4i af[2][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const v4i af = *reinterpret_cast<const v4i*>(cur + tile_off(wm * 64 + i * 16 + r16, 4 * ks + g));
+        const uint4 q = *reinterpret_cast<const uint4*>(cur + (wm * 64 + i * 16) * LPK + fo);
+        af[0][i] = widen(q.x, q.y);
+        af[1][i] = widen(q.z, q.w);
+      }
 #pragma unroll
-        for (int j = 0; j < 7; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 7; ++j) {
+        const uint4 q = *reinterpret_cast<const uint4*>(cur + (LM + wn * 112 + j * 16) * LPK + fo);
+        const v4i b0 = widen(q.x, q.y), b1 = widen(q.z, q.w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], b0, acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, acc[i][j], 0, 0, 0);
       }
     }
-    if (s + 1 < steps) {
-      stash_chunk(nxt, srow, part, ra0);
-      stash_chunk(nxt, srow + 128, part, ra1);
-      stash_chunk(nxt + LM * LROW, srow, part, rb0);
-      if (b2) stash_chunk(nxt + LM * LROW, srow + 128, part, rb1);
-    }
-    __syncthreads();
+    // this wave's loads of step s + 1 have landed; after the barrier every
+    // wave's have, and every wave is done reading buffer s & 1, which the
+    // loads of step s + 2 overwrite
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
+#undef RQ_ISSUE
 
   // epilogue: lane holds rows 4g..4g+3 of every 16-row group, column r16 of
   // every 16-column group
@@ -335,6 +361,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     }
   }
 }
+#undef RQ_DMA
 
 }  // namespace
 
