@@ -327,10 +327,11 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, acc[i][j], 0, 0, 0);
       }
     }
-    // this wave's loads of step s + 1 have landed; after the barrier every
-    // wave's have, and every wave is done reading buffer s & 1, which the
-    // loads of step s + 2 overwrite
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // This wave's loads of step s + 1 have landed and its reads of buffer
+    // s & 1 have returned (an asm barrier orders memory operations only, so
+    // the LDS reads are waited for explicitly); after the barrier the same
+    // holds for every wave, so the loads of step s + 2 may overwrite s & 1.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
