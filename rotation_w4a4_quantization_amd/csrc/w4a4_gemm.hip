@@ -247,7 +247,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
                                                               const uint8_t* __restrict__ w_codes,
                                                               const uint16_t* __restrict__ w_scales,
                                                               int64_t m, int64_t k, int64_t d,
-                                                              int tiles_m,
+                                                              int tiles_m, bool wide_store,
                                                               uint16_t* __restrict__ y,
                                                               int32_t* __restrict__ acc_out) {
   __shared__ __align__(16) unsigned char lds[2 * LBUF];
@@ -346,6 +346,35 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     swv[j] = col < k ? h2f(w_scales[col]) : 0.0f;
   }
   const bool full = m0 + LM <= m && n0 + LN <= k;
+  if (full && wide_store) {
+    // The fp16 tile goes through LDS (free after the last barrier; 464-byte
+    // rows) and leaves as coalesced 16-byte stores.
+    constexpr int OP = 464;  // LDS row pitch of the output tile (bytes)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tr = wm * 64 + i * 16 + 4 * g + e;
+        const float sa = h2f(a_scales[m0 + tr]);
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+          const int32_t a = acc[i][j][e] >> 8;  // exact: the MFMA sum is 256 * acc
+          *reinterpret_cast<uint16_t*>(lds + tr * OP + 2 * (wn * 112 + j * 16 + r16)) =
+              f2h_rn(((float)a * sa) * swv[j]);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = LN * 2 / 16;  // 16-byte chunks per output row: 28
+#pragma unroll
+    for (int q = 0; q < LM * CPR / LTHREADS; ++q) {
+      const int c = tid + LTHREADS * q;
+      const int tr = c / CPR, ch = c % CPR;
+      const v4u_g v = *reinterpret_cast<const v4u_g*>(lds + tr * OP + 16 * ch);
+      __builtin_nontemporal_store(v, reinterpret_cast<v4u_g*>(y + (m0 + tr) * k + n0 + 8 * ch));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -372,8 +401,10 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
   if (m >= 128 && k >= 224 && d % LK == 0) {
     const int tiles_m = (int)((m + LM - 1) / LM);
     const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
+    // 16-byte output stores need 16-byte aligned rows and no int32 output
+    const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
     hipLaunchKernelGGL(w4a4_large_kernel, dim3((unsigned)tiles), dim3(LTHREADS), 0, stream, a_codes,
-                       a_scales, w_codes, w_scales, m, k, d, tiles_m, y, acc);
+                       a_scales, w_codes, w_scales, m, k, d, tiles_m, wide_store, y, acc);
   } else if (m <= 16) {
     const int64_t blocks = (k + 15) / 16;
     hipLaunchKernelGGL(w4a4_decode_kernel, dim3((unsigned)blocks), dim3(64 * DEC_WAVES), 0, stream, a_codes,

@@ -156,8 +156,11 @@ def test_fold_tiny_and_decode_weights(rq):
         check_rotation_result(wt, dec["signs"], c, s, r, what=f"fold {k}", report=REPORT)
 
 
+# (512, 448, 512): only full 256 x 224 tiles with 16-byte output rows (the
+# LDS-staged epilogue); (300, 456, 512): full and edge tiles in both dimensions
 GEMM_SHAPES = [(1, 1, 64), (4, 17, 128), (16, 15, 192), (16, 200, 4096), (17, 33, 64),
-               (130, 129, 256), (300, 260, 1024), (129, 257, 4160)]
+               (130, 129, 256), (300, 260, 1024), (129, 257, 4160), (512, 448, 512),
+               (300, 456, 512)]
 
 
 @pytest.mark.parametrize("m,k,d", GEMM_SHAPES)
@@ -233,7 +236,11 @@ def test_prefill_gemm_full_size_sampled(rq):
     ac, sa, _ = rq.fwht_quant(dev(w["x"]), s)
     say("prefill: gemm 2048x8192 -> 28672")
     y, acc = rq.w4a4_gemm(ac, sa, wc, ws, debug=True)
+    # the launch the benchmark times (no int32 output) writes the same fp16
+    y2, _ = rq.w4a4_gemm(ac, sa, wc, ws)
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    del y2
     ac, sa, wc_h, ws_h, y, acc = map(host, (ac, sa, wc, ws, y, acc))
     rng = np.random.default_rng(77)
     rows = np.sort(rng.choice(2048, 128, replace=False))
