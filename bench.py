@@ -215,6 +215,19 @@ def main():
                         "hbm_frac": round(b / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "TOPS": round(2 * mm * k * 4096 / (msg * 1e-3) / 1e12, 3)}
                     log(f"[bench] decode m={mm} k={k}: {sec[f'gemm_decode_m{mm}_k{k}']}")
+                    # the whole decode linear: rotate + quantize the fp16 tokens, then the GEMM
+                    x_m = xa[:mm].contiguous()
+                    a_q = torch.empty((mm, 2048), dtype=torch.uint8, device=dev)
+                    s_q = torch.empty((mm,), dtype=torch.float16, device=dev)
+
+                    def lin_d(i, x_m=x_m, a_q=a_q, s_q=s_q, y=y, mm=mm):
+                        st = lib.rq_fwht_quant(_ptr(x_m), RQ_F16, mm, 4096, _ptr(s), _ptr(a_q),
+                                               _ptr(s_q), None, _stream())
+                        assert st == 0
+                        rq.w4a4_gemm(a_q, s_q, wcs[i], ws, out=y)
+
+                    msl = time_launches(torch, lin_d, nsets, steps2, warm2)
+                    sec[f"linear_decode_m{mm}_k{k}_rotate_plus_gemm"] = {"us": round(msl * 1e3, 3)}
                 del wcs
 
         if want("prefill"):
@@ -226,13 +239,17 @@ def main():
             mm, d, k = pf["m"], pf["d"], pf["k"]
             ac = torch.empty((mm, d // 2), dtype=torch.uint8, device=dev)
             sa = torch.empty((mm,), dtype=torch.float16, device=dev)
+            # rotate over input clones (> 2x the MALL) so repeats cannot hit in it
+            fsets = -(-2 * MALL_BYTES // (xa.numel() * 2)) + 1
+            xas = [xa] + [xa.clone() for _ in range(fsets - 1)]
 
             def f8(i):
-                st = lib.rq_fwht_quant(_ptr(xa), RQ_F16, mm, d, _ptr(s), _ptr(ac), _ptr(sa), None,
+                st = lib.rq_fwht_quant(_ptr(xas[i]), RQ_F16, mm, d, _ptr(s), _ptr(ac), _ptr(sa), None,
                                        _stream())
                 assert st == 0
 
-            msf = time_launches(torch, f8, 1, steps2, warm2)
+            msf = time_launches(torch, f8, fsets, steps2, warm2)
+            del xas[1:]
             b = fwht_bytes(mm, d)
             sec["fwht_quant_2048x8192"] = {"us": round(msf * 1e3, 3),
                                            "GB/s": round(b / (msf * 1e-3) / 1e9, 1),
