@@ -208,14 +208,13 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_kernel(
 // lane).  K runs in steps of 256 codes (128 packed bytes per row).
 //
 // Loads go straight from global memory into LDS (global_load_lds_dwordx4: no
-// staging registers) one step ahead into the other of two 64 KB buffers, and
-// the tiles stay packed in LDS.  Each wave issues four 8-row A and four 8-row
-// B loads per step (the B tile is padded to 256 rows so that the count is the
-// same for every wave) and waits for them only at the end of the step, so
-// each load has a whole step of MFMA work to arrive, and the block meets at
-// one barrier per 256 codes.
+// staging registers) one step ahead into the other of two 60 KB buffers, and
+// the tiles stay packed in LDS.  Each wave issues four 8-row A loads and
+// waves 0..6 four 8-row B loads per step; a wave waits for its loads only at
+// the end of the step, so each load has a whole step of MFMA work to arrive,
+// and the block meets at one barrier per 256 codes.
 //
-// LDS layout per buffer: 256 A rows then 256 B rows, 128 bytes each; the
+// LDS layout per buffer: 256 A rows then 224 B rows, 128 bytes each; the
 // 16-byte part p of row r sits at part position p ^ (r & 7), so the 8-lane
 // phases of the 16-byte fragment reads hit 8 different bank groups.  A DMA
 // load writes lane L's 16 bytes at M0 + 16 L, so lane L of the load of rows
@@ -229,9 +228,9 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_kernel(
 // once.  For 2048 x 28672 the tile gives exactly 1024 tiles, four per CU.
 constexpr int LM = 256, LN = 224, LK = 256;  // block tile (codes)
 constexpr int LPK = LK / 2;                   // packed bytes per row per step
-constexpr int LBROWS = 256;                   // B rows per buffer (224 used)
-constexpr int LBUF = (LM + LBROWS) * LPK;     // one LDS buffer: 64 KB
+constexpr int LBUF = (LM + LN) * LPK;         // one LDS buffer: 60 KB
 constexpr int LTHREADS = 512;
+static_assert(LN % 32 == 0 && LM == 32 * (LTHREADS / 64), "one 32-row DMA slice per wave");
 
 __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); }
 
@@ -251,8 +250,14 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
                                                               uint16_t* __restrict__ y,
                                                               int32_t* __restrict__ acc_out) {
   __shared__ __align__(16) unsigned char lds[2 * LBUF];
-  const int64_t m0 = (int64_t)(blockIdx.x % tiles_m) * LM;
-  const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * LN;
+  // Workgroups go to the 8 XCDs round-robin (workgroup b to XCD b % 8).  Tile
+  // t = (b % 8) * (tiles / 8) + b / 8 hands each XCD a contiguous range of
+  // tiles, so the CUs of one XCD work on neighbouring tiles at the same time
+  // and share their A and B slices in that XCD's L2.
+  const int nb = (int)gridDim.x, nfull = nb / 8 * 8, b = (int)blockIdx.x;
+  const int tile = b < nfull ? (b % 8) * (nfull / 8) + b / 8 : b;
+  const int64_t m0 = (int64_t)(tile % tiles_m) * LM;
+  const int64_t n0 = (int64_t)(tile / tiles_m) * LN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x 112
@@ -263,8 +268,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
   // DMA sources of this lane: row 32 wave + 8 t + lane / 8 (t = 0..3) of the
-  // A tile and of the (padded) B tile; rows past the matrix edge re-read the
-  // last row (their results are never stored).
+  // A tile and (waves 0..6) of the B tile; rows past the matrix edge re-read
+  // the last row (their results are never stored).
   const uint8_t* asrc[4];
   const uint8_t* bsrc[4];
 #pragma unroll
@@ -272,8 +277,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     const int r = 32 * wave + 8 * t + (lane >> 3);
     const int p = part_pos(r, lane & 7);
     const int64_t ar = m0 + r < m ? m0 + r : m - 1;
-    const int64_t brr = r < LN ? n0 + r : n0 + LN - 1;
-    const int64_t br = brr < k ? brr : k - 1;
+    const int64_t br = n0 + r < k ? n0 + r : k - 1;  // r < LN for waves 0..6
     asrc[t] = a_codes + ar * rowb + 16 * p;
     bsrc[t] = w_codes + br * rowb + 16 * p;
   }
@@ -283,8 +287,10 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     const int64_t kb_ = (int64_t)(STEP) * LPK;                                      \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
       RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * LPK), asrc[t] + kb_);          \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-      RQ_DMA(buf_ + (uint32_t)((LM + 32 * wave + 8 * t) * LPK), bsrc[t] + kb_);     \
+    if (wave < LN / 32) {                                                           \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                 \
+        RQ_DMA(buf_ + (uint32_t)((LM + 32 * wave + 8 * t) * LPK), bsrc[t] + kb_);   \
+    }                                                                               \
   } while (0)
 
   v4i acc[4][7];
@@ -350,6 +356,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     // The fp16 tile goes through LDS (free after the last barrier; 464-byte
     // rows) and leaves as coalesced 16-byte stores.
     constexpr int OP = 464;  // LDS row pitch of the output tile (bytes)
+    static_assert(LM * OP <= 2 * LBUF, "the output tile fits in the two step buffers");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
