@@ -745,21 +745,6 @@ hipError_t launch_quad(FQOut o0, FQOut o1, int pairs, int64_t rows, const int8_t
   return hipGetLastError();
 }
 
-// Compute units of the current device (queried once per device).
-int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = 256;
-  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 // Resident wavefronts per SIMD the row kernel is sized for (its VGPR budget).
 template <int N>
@@ -823,6 +808,23 @@ hipError_t dispatch_n(FQOut o0, FQOut o1, int pairs, int64_t rows, int n, const 
 }
 
 }  // namespace
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 
 hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, const int8_t* signs,
                              uint8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream) {

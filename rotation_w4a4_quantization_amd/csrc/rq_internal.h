@@ -8,6 +8,9 @@
 
 namespace rq {
 
+// Compute units of the current device (queried once per device).
+int cu_count();
+
 // Row-wise (x * s) H_n / sqrt(n) fused with symmetric INT4 quantisation.
 // `is_f32` selects the element type of x (fp32 or fp16).
 hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, const int8_t* signs,

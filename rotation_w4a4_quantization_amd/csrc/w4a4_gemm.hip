@@ -241,23 +241,19 @@ __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); 
                : "v"(ADDR), "s"(M0)                                                \
                : "memory", "m0")
 
+// The grid holds at most one workgroup per CU and each workgroup walks its
+// tiles in turn.  During the last K step of a tile it already loads step 0 of
+// its next tile, and the finished tile leaves through the buffer that step
+// does not use, so the next tile starts without a load ramp.
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
                                                               const uint8_t* __restrict__ w_codes,
                                                               const uint16_t* __restrict__ w_scales,
                                                               int64_t m, int64_t k, int64_t d,
-                                                              int tiles_m, bool wide_store,
+                                                              int tiles_m, int tiles, bool wide_store,
                                                               uint16_t* __restrict__ y,
                                                               int32_t* __restrict__ acc_out) {
   __shared__ __align__(16) unsigned char lds[2 * LBUF];
-  // Workgroups go to the 8 XCDs round-robin (workgroup b to XCD b % 8).  Tile
-  // t = (b % 8) * (tiles / 8) + b / 8 hands each XCD a contiguous range of
-  // tiles, so the CUs of one XCD work on neighbouring tiles at the same time
-  // and share their A and B slices in that XCD's L2.
-  const int nb = (int)gridDim.x, nfull = nb / 8 * 8, b = (int)blockIdx.x;
-  const int tile = b < nfull ? (b % 8) * (nfull / 8) + b / 8 : b;
-  const int64_t m0 = (int64_t)(tile % tiles_m) * LM;
-  const int64_t n0 = (int64_t)(tile / tiles_m) * LN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x 112
@@ -267,136 +263,192 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   const uint32_t lds_base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
-  // DMA sources of this lane: row 32 wave + 8 t + lane / 8 (t = 0..3) of the
-  // A tile and (waves 0..6) of the B tile; rows past the matrix edge re-read
-  // the last row (their results are never stored).
+  // Tile order.  Workgroups go to the 8 XCDs round-robin (workgroup b to XCD
+  // b % 8).  When both counts allow it, XCD x owns the contiguous tiles
+  // [x T / 8, (x + 1) T / 8) and its workgroups take them in turn, so the CUs
+  // of one XCD work on neighbouring tiles at the same time and share their A
+  // and B slices in that XCD's L2.
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  const bool by_xcd = tiles % 8 == 0 && nb % 8 == 0;
+  const int per_xcd = tiles / 8, xcd_base = (b % 8) * per_xcd, xcd_stride = nb / 8;
+#define RQ_TILE_OK(R) (by_xcd ? b / 8 + xcd_stride * (R) < per_xcd : b + nb * (R) < tiles)
+#define RQ_TILE(R) (by_xcd ? xcd_base + b / 8 + xcd_stride * (R) : b + nb * (R))
+  if (!RQ_TILE_OK(0)) return;  // uniform per workgroup
+  int64_t m0 = (int64_t)(RQ_TILE(0) % tiles_m) * LM;
+  int64_t n0 = (int64_t)(RQ_TILE(0) / tiles_m) * LN;
+
+  // DMA rows of this lane: row 32 wave + 8 t + lane / 8 (t = 0..3) of the A
+  // tile and (waves 0..6) of the B tile, 16-byte part drp of it; rows past the
+  // matrix edge re-read the last row (their results are never stored).
+  const int dr0 = 32 * wave + (lane >> 3);
+  const int drp = 16 * part_pos(lane >> 3, lane & 7);  // (dr0 + 8 t) & 7 == (lane >> 3)
   const uint8_t* asrc[4];
   const uint8_t* bsrc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = 32 * wave + 8 * t + (lane >> 3);
-    const int p = part_pos(r, lane & 7);
-    const int64_t ar = m0 + r < m ? m0 + r : m - 1;
-    const int64_t br = n0 + r < k ? n0 + r : k - 1;  // r < LN for waves 0..6
-    asrc[t] = a_codes + ar * rowb + 16 * p;
-    bsrc[t] = w_codes + br * rowb + 16 * p;
+#define RQ_SET_SRC(M0_, N0_)                                                        \
+  _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                   \
+    const int64_t ar_ = (M0_) + dr0 + 8 * t, br_ = (N0_) + dr0 + 8 * t;            \
+    asrc[t] = a_codes + (ar_ < m ? ar_ : m - 1) * rowb + drp;                       \
+    bsrc[t] = w_codes + (br_ < k ? br_ : k - 1) * rowb + drp;                       \
   }
-#define RQ_ISSUE(STEP)                                                              \
+#define RQ_ISSUE_FROM(BUF, A_, B_, KB)                                              \
   do {                                                                              \
-    const uint32_t buf_ = lds_base + (uint32_t)(((STEP) & 1) * LBUF);               \
-    const int64_t kb_ = (int64_t)(STEP) * LPK;                                      \
+    const uint32_t buf_ = lds_base + (uint32_t)((BUF) * LBUF);                      \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-      RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * LPK), asrc[t] + kb_);          \
+      RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * LPK), (A_)[t] + (KB));         \
     if (wave < LN / 32) {                                                           \
       _Pragma("unroll") for (int t = 0; t < 4; ++t)                                 \
-        RQ_DMA(buf_ + (uint32_t)((LM + 32 * wave + 8 * t) * LPK), bsrc[t] + kb_);   \
+        RQ_DMA(buf_ + (uint32_t)((LM + 32 * wave + 8 * t) * LPK), (B_)[t] + (KB));  \
     }                                                                               \
   } while (0)
-
-  v4i acc[4][7];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 7; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  RQ_SET_SRC(m0, n0);
 
   // fragment offsets of this lane inside a 16-row group, halves 0 and 1
   const int frag_off0 = r16 * LPK + 16 * part_pos(r16, g);
   const int frag_off1 = r16 * LPK + 16 * part_pos(r16, 4 + g);
 
-  RQ_ISSUE(0);
+  int par = 0;  // buffer of the current step
+  RQ_ISSUE_FROM(0, asrc, bsrc, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  for (int s = 0; s < steps; ++s) {
-    if (s + 1 < steps) RQ_ISSUE(s + 1);
-    const unsigned char* cur = lds + (s & 1) * LBUF;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int fo = u ? frag_off1 : frag_off0;
-      v4i af[2][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 q = *reinterpret_cast<const uint4*>(cur + (wm * 64 + i * 16) * LPK + fo);
-        af[0][i] = widen(q.x, q.y);
-        af[1][i] = widen(q.z, q.w);
-      }
-#pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        const uint4 q = *reinterpret_cast<const uint4*>(cur + (LM + wn * 112 + j * 16) * LPK + fo);
-        const v4i b0 = widen(q.x, q.y), b1 = widen(q.z, q.w);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], b0, acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, acc[i][j], 0, 0, 0);
-      }
-    }
-    // This wave's loads of step s + 1 have landed and its reads of buffer
-    // s & 1 have returned (an asm barrier orders memory operations only, so
-    // the LDS reads are waited for explicitly); after the barrier the same
-    // holds for every wave, so the loads of step s + 2 may overwrite s & 1.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
-#undef RQ_ISSUE
+  for (int r = 0;; ++r) {
+    const bool has_next = RQ_TILE_OK(r + 1);
+    const int tn = has_next ? RQ_TILE(r + 1) : 0;
+    const int64_t m0n = (int64_t)(tn % tiles_m) * LM, n0n = (int64_t)(tn / tiles_m) * LN;
 
-  // epilogue: lane holds rows 4g..4g+3 of every 16-row group, column r16 of
-  // every 16-column group
-  float swv[7];
+    v4i acc[4][7];
 #pragma unroll
-  for (int j = 0; j < 7; ++j) {
-    const int64_t col = n0 + wn * 112 + j * 16 + r16;
-    swv[j] = col < k ? h2f(w_scales[col]) : 0.0f;
-  }
-  const bool full = m0 + LM <= m && n0 + LN <= k;
-  if (full && wide_store) {
-    // The fp16 tile goes through LDS (free after the last barrier; 464-byte
-    // rows) and leaves as coalesced 16-byte stores.
-    constexpr int OP = 464;  // LDS row pitch of the output tile (bytes)
-    static_assert(LM * OP <= 2 * LBUF, "the output tile fits in the two step buffers");
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < 7; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    for (int s = 0; s < steps; ++s) {
+      if (s + 1 < steps) {
+        RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, (int64_t)(s + 1) * LPK);
+      } else if (has_next) {
+        const uint8_t* an[4];
+        const uint8_t* bn[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tr = wm * 64 + i * 16 + 4 * g + e;
-        const float sa = h2f(a_scales[m0 + tr]);
+        for (int t = 0; t < 4; ++t) {
+          const int64_t ar = m0n + dr0 + 8 * t, br = n0n + dr0 + 8 * t;
+          an[t] = a_codes + (ar < m ? ar : m - 1) * rowb + drp;
+          bn[t] = w_codes + (br < k ? br : k - 1) * rowb + drp;
+        }
+        RQ_ISSUE_FROM(par ^ 1, an, bn, 0);
+      }
+      const unsigned char* cur = lds + par * LBUF;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int fo = u ? frag_off1 : frag_off0;
+        v4i af[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 q = *reinterpret_cast<const uint4*>(cur + (wm * 64 + i * 16) * LPK + fo);
+          af[0][i] = widen(q.x, q.y);
+          af[1][i] = widen(q.z, q.w);
+        }
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
-          const int32_t a = acc[i][j][e] >> 8;  // exact: the MFMA sum is 256 * acc
-          *reinterpret_cast<uint16_t*>(lds + tr * OP + 2 * (wn * 112 + j * 16 + r16)) =
-              f2h_rn(((float)a * sa) * swv[j]);
+          const uint4 q = *reinterpret_cast<const uint4*>(cur + (LM + wn * 112 + j * 16) * LPK + fo);
+          const v4i b0 = widen(q.x, q.y), b1 = widen(q.z, q.w);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], b0, acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, acc[i][j], 0, 0, 0);
+        }
+      }
+      // This wave's loads into buffer par ^ 1 have landed and its reads of
+      // buffer par have returned (an asm barrier orders memory operations
+      // only, so the LDS reads are waited for explicitly); after the barrier
+      // the same holds for every wave, so buffer par may be refilled.
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      par ^= 1;
+    }
+
+    // Epilogue: lane holds rows 4g..4g+3 of every 16-row group, column r16 of
+    // every 16-column group.  Buffer par holds step 0 of the next tile;
+    // buffer par ^ 1 is free.  The lane indices are re-derived from an opaque
+    // copy so that the compiler does not hoist one address register per store
+    // out of the tile loop.
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    const int g = (tid_o & 63) >> 4, r16 = tid_o & 15;
+    float swv[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int64_t col = n0 + wn * 112 + j * 16 + r16;
+      swv[j] = col < k ? h2f(w_scales[col]) : 0.0f;
+    }
+    const bool full = m0 + LM <= m && n0 + LN <= k;
+    if (full && wide_store) {
+      // The fp16 tile goes through the free buffer in two halves of 128 rows
+      // (464-byte rows) and leaves as coalesced 16-byte stores.  Half h holds
+      // row groups 2h and 2h + 1 of every wave: staging row tr is tile row
+      // (tr / 32) * 64 + 32 h + tr % 32.
+      constexpr int OP = 464;  // LDS row pitch of the output tile (bytes)
+      constexpr int HR = LM / 2;
+      static_assert(HR * OP <= LBUF, "half the output tile fits in one step buffer");
+      unsigned char* stg = lds + (par ^ 1) * LBUF;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const int i = 2 * h + i2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tr = wm * 32 + i2 * 16 + 4 * g + e;
+            const float sa = h2f(a_scales[m0 + wm * 64 + i * 16 + 4 * g + e]);
+#pragma unroll
+            for (int j = 0; j < 7; ++j) {
+              const int32_t a = acc[i][j][e] >> 8;  // exact: the MFMA sum is 256 * acc
+              *reinterpret_cast<uint16_t*>(stg + tr * OP + 2 * (wn * 112 + j * 16 + r16)) =
+                  f2h_rn(((float)a * sa) * swv[j]);
+            }
+          }
+        }
+        __syncthreads();
+        constexpr int CPR = LN * 2 / 16;  // 16-byte chunks per output row: 28
+#pragma unroll
+        for (int q = 0; q < HR * CPR / LTHREADS; ++q) {
+          const int c = tid_o + LTHREADS * q;
+          const int tr = c / CPR, ch = c % CPR;
+          const v4u_g v = *reinterpret_cast<const v4u_g*>(stg + tr * OP + 16 * ch);
+          const int row = (tr >> 5) * 64 + 32 * h + (tr & 31);
+          __builtin_nontemporal_store(v, reinterpret_cast<v4u_g*>(y + (m0 + row) * k + n0 + 8 * ch));
+        }
+        __syncthreads();
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
+          if (!full && row >= m) continue;
+          const float sa = h2f(a_scales[row]);
+          const int64_t base = row * k + n0 + wn * 112 + r16;
+#pragma unroll
+          for (int j = 0; j < 7; ++j) {
+            if (full || n0 + wn * 112 + j * 16 + r16 < k)
+              epilogue_store(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out);
+          }
         }
       }
     }
-    __syncthreads();
-    constexpr int CPR = LN * 2 / 16;  // 16-byte chunks per output row: 28
-#pragma unroll
-    for (int q = 0; q < LM * CPR / LTHREADS; ++q) {
-      const int c = tid + LTHREADS * q;
-      const int tr = c / CPR, ch = c % CPR;
-      const v4u_g v = *reinterpret_cast<const v4u_g*>(lds + tr * OP + 16 * ch);
-      __builtin_nontemporal_store(v, reinterpret_cast<v4u_g*>(y + (m0 + tr) * k + n0 + 8 * ch));
-    }
-    return;
+    if (!has_next) break;
+    m0 = m0n;
+    n0 = n0n;
+    RQ_SET_SRC(m0, n0);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
-      if (!full && row >= m) continue;
-      const float sa = h2f(a_scales[row]);
-      const int64_t base = row * k + n0 + wn * 112 + r16;
-#pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        if (full || n0 + wn * 112 + j * 16 + r16 < k)
-          epilogue_store(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out);
-      }
-    }
-  }
+#undef RQ_TILE_OK
+#undef RQ_TILE
+#undef RQ_SET_SRC
+#undef RQ_ISSUE_FROM
 }
 #undef RQ_DMA
 
@@ -408,10 +460,13 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
   if (m >= 128 && k >= 224 && d % LK == 0) {
     const int tiles_m = (int)((m + LM - 1) / LM);
     const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
     // 16-byte output stores need 16-byte aligned rows and no int32 output
     const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-    hipLaunchKernelGGL(w4a4_large_kernel, dim3((unsigned)tiles), dim3(LTHREADS), 0, stream, a_codes,
-                       a_scales, w_codes, w_scales, m, k, d, tiles_m, wide_store, y, acc);
+    hipLaunchKernelGGL(w4a4_large_kernel, dim3((unsigned)grid), dim3(LTHREADS), 0, stream, a_codes,
+                       a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles, wide_store, y,
+                       acc);
   } else if (m <= 16) {
     const int64_t blocks = (k + 15) / 16;
     hipLaunchKernelGGL(w4a4_decode_kernel, dim3((unsigned)blocks), dim3(64 * DEC_WAVES), 0, stream, a_codes,
