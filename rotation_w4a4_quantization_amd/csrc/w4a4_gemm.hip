@@ -202,6 +202,117 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_kernel(
   }
 }
 
+// One 8-row DMA load: lane L's 16 bytes go to LDS byte m0 + 16 L.
+#define RQ_DMA(M0, ADDR)                                                           \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"     \
+               :                                                                   \
+               : "v"(ADDR), "s"(M0)                                                \
+               : "memory", "m0")
+// The same with the nontemporal hint, for data read exactly once.
+#define RQ_DMA_NT(M0, ADDR)                                                        \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"  \
+               :                                                                   \
+               : "v"(ADDR), "s"(M0)                                                \
+               : "memory", "m0")
+
+// m <= 16 and d % 256 == 0: the same work split, but the weights go straight
+// from global memory into LDS, one load instruction per 8 rows x 128 bytes,
+// so that every instruction reads whole cache lines (a lane-per-row pattern
+// of 16 rows x 64 bytes splits each line between two instructions of
+// different waves and costs about a fifth more time at the same bytes).
+// A row is cut into 128-byte segments; wave w loads segments 2w and 2w + 1 of
+// each 2 KB chunk of the block's 16 RG rows and is also the only wave that reads
+// them, so the chunk needs no workgroup barrier.  LDS holds [segment][row][128
+// bytes], with the 16-byte part p of row r at position p ^ (r & 7) (the
+// fragment reads of one 8-lane phase hit 8 different bank groups).
+constexpr int DSEG = 128;                 // bytes per row segment
+constexpr int DCHUNK = 2 * DEC_WAVES;     // segments per chunk (2 KB per row)
+
+// RG 16-row groups of weights per workgroup share each activation fragment.
+template <int RG>
+__global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
+    const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int64_t m,
+    int64_t k, int64_t d, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+  __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];  // 32 KB per row group
+  __shared__ v4i partial[DEC_WAVES][RG][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
+  const int64_t rowb = d / 2;
+  const int64_t nseg = rowb / DSEG;
+  const uint32_t wl_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)wl;
+  constexpr int SEGB = 16 * RG * DSEG;  // LDS bytes per segment
+
+  const uint8_t* wsrc[2 * RG];
+#pragma unroll
+  for (int h = 0; h < 2 * RG; ++h) {
+    const int64_t row = n0 + 8 * h + (lane >> 3);
+    wsrc[h] = w_codes + (row < k ? row : k - 1) * rowb + 16 * ((lane & 7) ^ (lane >> 3));
+  }
+  const bool a_ok = r16 < m;
+  const uint8_t* a_src = a_codes + (int64_t)(a_ok ? r16 : 0) * rowb + 16 * g;
+
+  v4i acc0[RG], acc1[RG];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
+  for (int64_t c0 = 0; c0 < nseg; c0 += DCHUNK) {
+    uint4 av[2][2];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int64_t seg = c0 + 2 * wave + sl;
+      if (seg < nseg) {
+        const uint32_t m0_ = wl_base + (uint32_t)((2 * wave + sl) * SEGB);
+#pragma unroll
+        for (int h = 0; h < 2 * RG; ++h) RQ_DMA_NT(m0_ + 8 * h * DSEG, wsrc[h] + seg * DSEG);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        av[sl][h] = make_uint4(0, 0, 0, 0);
+        if (a_ok && seg < nseg)
+          av[sl][h] = *reinterpret_cast<const uint4*>(a_src + seg * DSEG + 64 * h);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (c0 + 2 * wave + sl >= nseg) continue;  // uniform per wave
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4i a0 = widen(av[sl][h].x, av[sl][h].y), a1 = widen(av[sl][h].z, av[sl][h].w);
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          const uint4 w = *reinterpret_cast<const uint4*>(
+              wl + (2 * wave + sl) * SEGB + (16 * q + r16) * DSEG + 16 * ((4 * h + g) ^ (r16 & 7)));
+          acc0[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, widen(w.x, w.y), acc0[q], 0, 0, 0);
+          acc1[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, widen(w.z, w.w), acc1[q], 0, 0, 0);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+#pragma unroll
+  for (int q = 0; q < RG; ++q) partial[wave][q][lane] = acc0[q] + acc1[q];
+  __syncthreads();
+  if (wave < RG) {
+    v4i t = partial[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < DEC_WAVES; ++w) t += partial[w][wave][lane];
+    const int64_t col = n0 + 16 * wave + r16;
+    if (col < k) {
+      const float sw = h2f(w_scales[col]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = 4 * g + e;
+        if (row < m) epilogue_store(t[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out);
+      }
+    }
+  }
+}
+#undef RQ_DMA_NT
+
 // ------------------------------------------------------------ large GEMM
 // 256 x 224 output tile per 512-thread block: 8 waves in a 4 x 2 grid of
 // 64 x 112 wave tiles (4 x 7 MFMA 16x16x64 tiles, 112 int32 accumulators per
@@ -234,12 +345,6 @@ static_assert(LN % 32 == 0 && LM == 32 * (LTHREADS / 64), "one 32-row DMA slice 
 
 __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); }
 
-// One 8-row DMA load: lane L's 16 bytes go to LDS byte m0 + 16 L.
-#define RQ_DMA(M0, ADDR)                                                           \
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"     \
-               :                                                                   \
-               : "v"(ADDR), "s"(M0)                                                \
-               : "memory", "m0")
 
 // The grid holds at most one workgroup per CU and each workgroup walks its
 // tiles in turn.  During the last K step of a tile it already loads step 0 of
@@ -469,8 +574,21 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
                        acc);
   } else if (m <= 16) {
     const int64_t blocks = (k + 15) / 16;
-    hipLaunchKernelGGL(w4a4_decode_kernel, dim3((unsigned)blocks), dim3(64 * DEC_WAVES), 0, stream, a_codes,
-                       a_scales, w_codes, w_scales, m, k, d, y, acc);
+    if (d % (2 * DSEG) == 0) {
+      // Two 16-row groups per workgroup halve the activation reads per weight
+      // byte; worth it for many activation rows when the grid still covers
+      // the CUs one and a half times.
+      if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
+        hipLaunchKernelGGL(w4a4_decode_lds_kernel<2>, dim3((unsigned)((k + 31) / 32)),
+                           dim3(64 * DEC_WAVES), 0, stream, a_codes, a_scales, w_codes, w_scales, m,
+                           k, d, y, acc);
+      else
+        hipLaunchKernelGGL(w4a4_decode_lds_kernel<1>, dim3((unsigned)blocks), dim3(64 * DEC_WAVES),
+                           0, stream, a_codes, a_scales, w_codes, w_scales, m, k, d, y, acc);
+    }
+    else
+      hipLaunchKernelGGL(w4a4_decode_kernel, dim3((unsigned)blocks), dim3(64 * DEC_WAVES), 0, stream,
+                         a_codes, a_scales, w_codes, w_scales, m, k, d, y, acc);
   } else {
     const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
     hipLaunchKernelGGL(w4a4_tile_kernel, grid, dim3(256), 0, stream, a_codes, a_scales, w_codes,
