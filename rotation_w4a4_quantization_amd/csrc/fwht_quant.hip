@@ -719,20 +719,27 @@ __global__ __launch_bounds__(256) void fwht128_quad_kernel(FQOut o0, FQOut o1, i
 #pragma unroll
     for (int r = 0; r < 32; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
   }
-  if (row_ok) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(o.codes + row * (N / 2));
+  // The wavefront's 16 rows of codes (1 KB, contiguous in memory) are staged
+  // in its own LDS slice and leave as one 16-byte store per lane.
+  __shared__ __align__(16) uint32_t kcb[4][16 * 16];
+  uint32_t* cw = kcb[wave] + (L >> 2) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // 8 offset-binary codes -> one word of two's-complement nibbles
-      uint32_t b[4];
+  for (int i = 0; i < 4; ++i) {
+    // 8 offset-binary codes -> one word of two's-complement nibbles
+    uint32_t b[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) b[p] = (f2u(t[8 * i + 2 * p + 1]) << 4) | f2u(t[8 * i + 2 * p]);
-      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // bytes b0.0, b1.0
-      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);  // bytes b2.0, b3.0 at 2, 3
-      // codes of elements 32i + 8q .. +7 are bytes 16i + 4q .. +3 of the row
-      __builtin_nontemporal_store((lo | hi) ^ 0x88888888u, dst + 4 * i + q);
-    }
+    for (int p = 0; p < 4; ++p) b[p] = (f2u(t[8 * i + 2 * p + 1]) << 4) | f2u(t[8 * i + 2 * p]);
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // bytes b0.0, b1.0
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);  // bytes b2.0, b3.0 at 2, 3
+    // codes of elements 32i + 8q .. +7 are bytes 16i + 4q .. +3 of the row
+    cw[4 * i + q] = (lo | hi) ^ 0x88888888u;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const v4u cv = *reinterpret_cast<const v4u*>(kcb[wave] + 4 * L);  // row L / 4, bytes 16 q..
+  if (row_ok)
+    __builtin_nontemporal_store(cv, reinterpret_cast<v4u*>(o.codes + row * (N / 2) + 16 * q));
 }
 
 template <bool HAS_SIGNS>
