@@ -228,6 +228,14 @@ def main():
 
                     msl = time_launches(torch, lin_d, nsets, steps2, warm2)
                     sec[f"linear_decode_m{mm}_k{k}_rotate_plus_gemm"] = {"us": round(msl * 1e3, 3)}
+                    # the same linear as one launch: rotation fused into the GEMM's prologue
+                    ws_ld = rq.linear_decode_workspace(mm, 4096, dev)
+
+                    def lin_f(i, x_m=x_m, y=y, ws_ld=ws_ld):
+                        rq.linear_decode(x_m, s, wcs[i], ws, workspace=ws_ld, out=y)
+
+                    msf = time_launches(torch, lin_f, nsets, steps2, warm2)
+                    sec[f"linear_decode_m{mm}_k{k}_fused"] = {"us": round(msf * 1e3, 3)}
                 del wcs
 
         if want("prefill"):

@@ -162,6 +162,44 @@ int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
                        const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
                        uint8_t* v_codes, uint16_t* v_scales, void* stream);
 
+/*
+ * rq_linear_decode_workspace_size -- bytes of device workspace that
+ * rq_linear_decode needs: m * d / 2 + 64.
+ */
+size_t rq_linear_decode_workspace_size(int64_t m, int64_t d);
+
+/*
+ * rq_linear_decode -- the whole decode-shaped W4A4 linear in one call:
+ * rq_fwht_quant of the fp16 tokens, then rq_w4a4_gemm with the folded weights.
+ *
+ * [SpinQuant] "The architecture: every piece explained" (the online rotation
+ * is fused into the low-bit matmul); [QuaRot] "End-to-end flow" (rotate,
+ * quantise to INT4, multiply in a low-bit kernel).  For m <= 4 it is one
+ * launch: every workgroup of the decode GEMM rotates and quantises the tokens
+ * into LDS as its prologue, with the device code of rq_fwht_quant, while its
+ * weights stream in.  For 4 < m <= 16 it is rq_fwht_quant into the workspace
+ * followed by the decode GEMM.  Either way y is bit-identical to
+ * rq_fwht_quant followed by rq_w4a4_gemm on the same arguments.
+ *
+ *   x          [m][d] fp16 tokens, 16-byte aligned.
+ *   m          tokens, 0 <= m <= 16 (m == 0 returns RQ_OK without launching).
+ *   d          input width, a power of two in [512, 8192].
+ *   signs      [d] int8 +-1 (the ones the weights were folded with), or NULL.
+ *   w_codes    [k][d/2] folded weight codes (rq_fold_weights), 16-byte
+ *              aligned; w_scales [k] fp16.
+ *   k          output channels, >= 1.
+ *   y          [m][k] fp16 output.
+ *   workspace  device memory of at least rq_linear_decode_workspace_size(m, d)
+ *              bytes, 16-byte aligned (any contents).  When m > 4 it receives
+ *              the activation codes ([m][d/2] at offset 0) and scales ([m]
+ *              fp16 after the codes); calls that may overlap in time need
+ *              separate workspaces.
+ *   workspace_bytes  size of workspace.
+ */
+int rq_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                     const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for an rq_status value (static storage, never NULL). */
 const char* rq_status_string(int status);
 

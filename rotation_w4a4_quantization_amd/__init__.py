@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     fold_weights,
     fwht_quant,
     kv_rotate_quant,
+    linear_decode,
+    linear_decode_workspace,
     load_library,
     status_string,
     version,

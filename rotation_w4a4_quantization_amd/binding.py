@@ -25,6 +25,8 @@ EXPORTED = (
     "rq_w4a4_gemm_workspace_size",
     "rq_w4a4_gemm",
     "rq_kv_rotate_quant",
+    "rq_linear_decode_workspace_size",
+    "rq_linear_decode",
     "rq_status_string",
     "rq_version",
 )
@@ -59,6 +61,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_w4a4_gemm.restype = i32
     lib.rq_kv_rotate_quant.argtypes = [p, p, i64, i64, p, p, p, p, p, p]
     lib.rq_kv_rotate_quant.restype = i32
+    lib.rq_linear_decode_workspace_size.argtypes = [i64, i64]
+    lib.rq_linear_decode_workspace_size.restype = sz
+    lib.rq_linear_decode.argtypes = [p, i64, i64, p, p, p, i64, p, p, sz, p]
+    lib.rq_linear_decode.restype = i32
     lib.rq_status_string.argtypes = [i32]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_version.argtypes = []
@@ -188,4 +194,37 @@ def w4a4_linear(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tens
     weights folded with the same signs.  Two launches on the current stream."""
     codes, scales, _ = fwht_quant(x, signs)
     y, _ = w4a4_gemm(codes, scales, w_codes, w_scales)
+    return y
+
+
+def linear_decode_workspace(m: int, d: int, device) -> torch.Tensor:
+    """A workspace for linear_decode (reusable across calls that do not
+    overlap in time)."""
+    nbytes = int(load_library().rq_linear_decode_workspace_size(m, d))
+    return torch.empty((nbytes,), dtype=torch.uint8, device=device)
+
+
+def linear_decode(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tensor,
+                  w_scales: torch.Tensor, workspace: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """rq_linear_decode: rotation + INT4 quantisation of m <= 16 fp16 tokens
+    and the decode GEMM in one call (one launch for m <= 4).  `workspace`
+    comes from linear_decode_workspace (a fresh one is made when omitted)."""
+    for name, t in (("x", x), ("w_codes", w_codes), ("w_scales", w_scales)):
+        _need_cuda(name, t)
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a float16 [m, d] tensor")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.float16:
+        raise ValueError("weight codes must be uint8 and scales float16")
+    x = x.contiguous()
+    m, d = x.shape
+    k, half_d = w_codes.shape
+    if half_d * 2 != d or w_scales.numel() != k:
+        raise ValueError("weight codes do not match x")
+    s = _signs(signs, d, x.device)
+    ws = workspace if workspace is not None else linear_decode_workspace(m, d, x.device)
+    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=x.device)
+    st = load_library().rq_linear_decode(_ptr(x), m, d, _ptr(s), _ptr(w_codes), _ptr(w_scales), k,
+                                         _ptr(y), _ptr(ws), ws.numel(), _stream())
+    _check("rq_linear_decode", st)
     return y

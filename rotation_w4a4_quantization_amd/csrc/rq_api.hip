@@ -93,6 +93,28 @@ int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
                                              v_scales, static_cast<hipStream_t>(stream)));
 }
 
+size_t rq_linear_decode_workspace_size(int64_t m, int64_t d) {
+  if (m < 0 || m > 16 || d < 0) return 0;
+  return rq::linear_decode_workspace_bytes(m, d);
+}
+
+int rq_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                     const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || m > 16) return RQ_ERR_SHAPE;
+  if (!is_pow2(d) || d < 512 || d > 8192) return RQ_ERR_SHAPE;
+  if (k < 1 || k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr ||
+      workspace == nullptr)
+    return RQ_ERR_NULL;
+  if (workspace_bytes < rq::linear_decode_workspace_bytes(m, d)) return RQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(workspace)) return RQ_ERR_ALIGN;
+  if (signs != nullptr && !aligned16(signs)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_linear_decode(x, m, d, signs, w_codes, w_scales, k, y, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 const char* rq_status_string(int status) {
   switch (status) {
     case RQ_OK: return "ok";

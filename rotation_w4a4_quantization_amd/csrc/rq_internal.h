@@ -26,4 +26,11 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream);
 
+// Fused decode linear (m <= 16, fp16 x, d in 512..8192 a power of two):
+// rotation + INT4 quantisation of x as the prologue of the decode GEMM.
+size_t linear_decode_workspace_bytes(int64_t m, int64_t d);
+hipError_t launch_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                                const uint8_t* w_codes, const uint16_t* w_scales, int64_t k,
+                                uint16_t* y, void* workspace, hipStream_t stream);
+
 }  // namespace rq

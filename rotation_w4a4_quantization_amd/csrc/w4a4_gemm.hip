@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include "rq_internal.h"
+#include "rq_row_device.h"
 
 namespace rq {
 namespace {
@@ -39,8 +40,6 @@ __device__ __forceinline__ v4i widen(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ uint16_t f2h_rn(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
 __device__ __forceinline__ void epilogue_store(int32_t raw, float sa, float sw, int64_t idx,
                                                uint16_t* __restrict__ y, int32_t* __restrict__ acc) {
@@ -228,6 +227,120 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_kernel(
 constexpr int DSEG = 128;                 // bytes per row segment
 constexpr int DCHUNK = 2 * DEC_WAVES;     // segments per chunk (2 KB per row)
 
+// Per-lane state of an LDS-staged decode tile of 16 RG weight rows.
+template <int RG>
+struct DecLane {
+  const uint8_t* wsrc[2 * RG];  // DMA source of each 8-row load
+  uint32_t wl_base;             // LDS byte address of the weight staging buffer
+  int wave, lane, g, r16;
+  int64_t n0, nseg;
+};
+
+template <int RG>
+__device__ __forceinline__ DecLane<RG> dec_lane(const uint8_t* __restrict__ w_codes, int64_t k,
+                                                int64_t rowb, unsigned char* wl) {
+  DecLane<RG> t;
+  const int tid = threadIdx.x;
+  t.lane = tid & 63;
+  t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  t.g = t.lane >> 4;
+  t.r16 = t.lane & 15;
+  t.n0 = (int64_t)blockIdx.x * 16 * RG;
+  t.nseg = rowb / DSEG;
+  t.wl_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)wl;
+  // lane L of the load of rows 8 h .. 8 h + 7 fetches part (L % 8) ^ (L / 8)
+  // of row 8 h + L / 8 (rows past k re-read the last one)
+#pragma unroll
+  for (int h = 0; h < 2 * RG; ++h) {
+    const int64_t row = t.n0 + 8 * h + (t.lane >> 3);
+    t.wsrc[h] = w_codes + (row < k ? row : k - 1) * rowb + 16 * ((t.lane & 7) ^ (t.lane >> 3));
+  }
+  return t;
+}
+
+// Loads of this wave's two segments of the chunk that starts at segment c0.
+template <int RG>
+__device__ __forceinline__ void dec_issue_w(const DecLane<RG>& t, int64_t c0) {
+  constexpr int SEGB = 16 * RG * DSEG;  // LDS bytes per segment
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    const int64_t seg = c0 + 2 * t.wave + sl;
+    if (seg < t.nseg) {
+      const uint32_t m0_ = t.wl_base + (uint32_t)((2 * t.wave + sl) * SEGB);
+#pragma unroll
+      for (int h = 0; h < 2 * RG; ++h) RQ_DMA_NT(m0_ + 8 * h * DSEG, t.wsrc[h] + seg * DSEG);
+    }
+  }
+}
+
+// Activation fragments of the chunk, wait for them and for the chunk's
+// weights, then the MFMAs; this wave's LDS reads are back on return (before
+// its next loads may overwrite them).
+template <int RG>
+__device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsigned char* wl,
+                                              const uint8_t* a_src, bool a_ok, int64_t c0,
+                                              v4i (&acc0)[RG], v4i (&acc1)[RG]) {
+  constexpr int SEGB = 16 * RG * DSEG;
+  uint4 av[2][2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    const int64_t seg = c0 + 2 * t.wave + sl;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      av[sl][h] = make_uint4(0, 0, 0, 0);
+      if (a_ok && seg < t.nseg)
+        av[sl][h] = *reinterpret_cast<const uint4*>(a_src + seg * DSEG + 64 * h);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (c0 + 2 * t.wave + sl >= t.nseg) continue;  // uniform per wave
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i a0 = widen(av[sl][h].x, av[sl][h].y), a1 = widen(av[sl][h].z, av[sl][h].w);
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            wl + (2 * t.wave + sl) * SEGB + (16 * q + t.r16) * DSEG +
+            16 * ((4 * h + t.g) ^ (t.r16 & 7)));
+        acc0[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, widen(w.x, w.y), acc0[q], 0, 0, 0);
+        acc1[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, widen(w.z, w.w), acc1[q], 0, 0, 0);
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Partial sums of the 8 waves meet in LDS (wave w's RG x 64 sums start at
+// partial + w * pitch); waves 0..RG-1 finish one 16-row group each.
+template <int RG>
+__device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* partial, int pitch,
+                                                 const v4i (&acc0)[RG], const v4i (&acc1)[RG],
+                                                 int64_t m, int64_t k,
+                                                 const uint16_t* __restrict__ a_scales,
+                                                 const uint16_t* __restrict__ w_scales,
+                                                 uint16_t* __restrict__ y,
+                                                 int32_t* __restrict__ acc_out) {
+#pragma unroll
+  for (int q = 0; q < RG; ++q) partial[t.wave * pitch + q * 64 + t.lane] = acc0[q] + acc1[q];
+  __syncthreads();
+  if (t.wave < RG) {
+    v4i s = partial[t.wave * 64 + t.lane];
+#pragma unroll
+    for (int w = 1; w < DEC_WAVES; ++w) s += partial[w * pitch + t.wave * 64 + t.lane];
+    const int64_t col = t.n0 + 16 * t.wave + t.r16;
+    if (col < k) {
+      const float sw = h2f(w_scales[col]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = 4 * t.g + e;
+        if (row < m) epilogue_store(s[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out);
+      }
+    }
+  }
+}
+
 // RG 16-row groups of weights per workgroup share each activation fragment.
 template <int RG>
 __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
@@ -236,80 +349,79 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
     int64_t k, int64_t d, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
   __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];  // 32 KB per row group
   __shared__ v4i partial[DEC_WAVES][RG][64];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, r16 = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
   const int64_t rowb = d / 2;
-  const int64_t nseg = rowb / DSEG;
-  const uint32_t wl_base =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)wl;
-  constexpr int SEGB = 16 * RG * DSEG;  // LDS bytes per segment
-
-  const uint8_t* wsrc[2 * RG];
-#pragma unroll
-  for (int h = 0; h < 2 * RG; ++h) {
-    const int64_t row = n0 + 8 * h + (lane >> 3);
-    wsrc[h] = w_codes + (row < k ? row : k - 1) * rowb + 16 * ((lane & 7) ^ (lane >> 3));
-  }
-  const bool a_ok = r16 < m;
-  const uint8_t* a_src = a_codes + (int64_t)(a_ok ? r16 : 0) * rowb + 16 * g;
+  const DecLane<RG> t = dec_lane<RG>(w_codes, k, rowb, wl);
+  const bool a_ok = t.r16 < m;
+  const uint8_t* a_src = a_codes + (int64_t)(a_ok ? t.r16 : 0) * rowb + 16 * t.g;
 
   v4i acc0[RG], acc1[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
-  for (int64_t c0 = 0; c0 < nseg; c0 += DCHUNK) {
-    uint4 av[2][2];
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int64_t seg = c0 + 2 * wave + sl;
-      if (seg < nseg) {
-        const uint32_t m0_ = wl_base + (uint32_t)((2 * wave + sl) * SEGB);
-#pragma unroll
-        for (int h = 0; h < 2 * RG; ++h) RQ_DMA_NT(m0_ + 8 * h * DSEG, wsrc[h] + seg * DSEG);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        av[sl][h] = make_uint4(0, 0, 0, 0);
-        if (a_ok && seg < nseg)
-          av[sl][h] = *reinterpret_cast<const uint4*>(a_src + seg * DSEG + 64 * h);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      if (c0 + 2 * wave + sl >= nseg) continue;  // uniform per wave
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const v4i a0 = widen(av[sl][h].x, av[sl][h].y), a1 = widen(av[sl][h].z, av[sl][h].w);
-#pragma unroll
-        for (int q = 0; q < RG; ++q) {
-          const uint4 w = *reinterpret_cast<const uint4*>(
-              wl + (2 * wave + sl) * SEGB + (16 * q + r16) * DSEG + 16 * ((4 * h + g) ^ (r16 & 7)));
-          acc0[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, widen(w.x, w.y), acc0[q], 0, 0, 0);
-          acc1[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, widen(w.z, w.w), acc1[q], 0, 0, 0);
-        }
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
+    dec_issue_w(t, c0);
+    dec_mma_chunk(t, wl, a_src, a_ok, c0, acc0, acc1);
   }
-#pragma unroll
-  for (int q = 0; q < RG; ++q) partial[wave][q][lane] = acc0[q] + acc1[q];
+  dec_reduce_store(t, &partial[0][0][0], RG * 64, acc0, acc1, m, k, a_scales, w_scales, y,
+                   acc_out);
+}
+
+// ------------------------------------------------------- fused decode linear
+// y = W4A4(rotate+quantise(x)) for m <= LD_FUSED_M tokens in one launch: the
+// rotation of the activations runs as the GEMM's prologue ([SpinQuant] "The
+// architecture: every piece explained": the online rotation fused into the
+// low-bit matmul; [QuaRot] "End-to-end flow").
+//
+// Every workgroup first puts the weights of its first chunk in flight, then
+// its waves 0..m-1 each rotate and quantise one token with the device code of
+// rq_fwht_quant, into LDS.  The GEMM then reads its activation fragments from
+// LDS.  Each workgroup repeats the (small) rotation instead of exchanging it
+// with the others: a hand-over between workgroups on different XCDs needs
+// agent-scope release/acquire (an L2 write-back and invalidation per XCD) and
+// a wait, which measured 3x slower than two launches.  The rotation overlaps
+// the weight stream, which the decode GEMM waits for anyway.
+constexpr int LD_FUSED_M = 4;
+
+template <int N, bool HAS_SIGNS, int RG>
+__global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
+    const __half* __restrict__ x, int64_t m, const int8_t* __restrict__ signs, float c32,
+    const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int64_t k,
+    uint16_t* __restrict__ y) {
+  // wl also takes the partial sums: each wave's RG x 64 sums go into the
+  // staging segments that only that wave reads, once its MFMAs are done
+  __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];
+  __shared__ __align__(16) unsigned char acodes[LD_FUSED_M][N / 2];
+  __shared__ uint16_t ascales[LD_FUSED_M];
+  constexpr int kWavePitch = 2 * 16 * RG * DSEG / (int)sizeof(v4i);  // v4i per wave's two segments
+  static_assert(kWavePitch >= RG * 64, "the partial sums fit in a wave's own segments");
+  constexpr int64_t rowb = N / 2;
+  const DecLane<RG> t = dec_lane<RG>(w_codes, k, rowb, wl);
+
+  // The first chunk's weights stream while the tokens are rotated.  A wave
+  // that rotates a token loads it before its weights: loads return in order,
+  // so the token does not wait behind the weight stream.
+  if (t.wave < m) {
+    uint4 raw[N / 512];
+    load_row(raw, x + (int64_t)t.wave * N, t.lane);
+    dec_issue_w(t, 0);
+    row_rotate_quant<N, HAS_SIGNS, true>(raw, signs, t.lane, make_row_lane(t.lane), c32,
+                                         acodes[t.wave], nullptr, ascales + t.wave, nullptr);
+  } else {
+    dec_issue_w(t, 0);
+  }
   __syncthreads();
-  if (wave < RG) {
-    v4i t = partial[0][wave][lane];
+
+  const bool a_ok = t.r16 < m;
+  const unsigned char* a_src = acodes[a_ok ? t.r16 : 0] + 16 * t.g;
+  v4i acc0[RG], acc1[RG];
 #pragma unroll
-    for (int w = 1; w < DEC_WAVES; ++w) t += partial[w][wave][lane];
-    const int64_t col = n0 + 16 * wave + r16;
-    if (col < k) {
-      const float sw = h2f(w_scales[col]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = 4 * g + e;
-        if (row < m) epilogue_store(t[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out);
-      }
-    }
+  for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
+  dec_mma_chunk(t, wl, a_src, a_ok, 0, acc0, acc1);
+  for (int64_t c0 = DCHUNK; c0 < t.nseg; c0 += DCHUNK) {
+    dec_issue_w(t, c0);
+    dec_mma_chunk(t, wl, a_src, a_ok, c0, acc0, acc1);
   }
+  dec_reduce_store(t, reinterpret_cast<v4i*>(wl), kWavePitch, acc0, acc1, m, k, ascales,
+                   w_scales, y, nullptr);
 }
 #undef RQ_DMA_NT
 
@@ -595,6 +707,61 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
                        w_scales, m, k, d, y, acc);
   }
   return hipGetLastError();
+}
+
+
+size_t linear_decode_workspace_bytes(int64_t m, int64_t d) {
+  return (size_t)m * (size_t)(d / 2) + 64;  // codes, then the fp16 scales
+}
+
+namespace {
+template <int N, bool HAS_SIGNS, int RG>
+hipError_t launch_ld(const uint16_t* x, int64_t m, const int8_t* signs, const uint8_t* w_codes,
+                     const uint16_t* w_scales, int64_t k, uint16_t* y, hipStream_t stream) {
+  const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
+  const int64_t grid = (k + 16 * RG - 1) / (16 * RG);
+  hipLaunchKernelGGL((w4a4_linear_decode_kernel<N, HAS_SIGNS, RG>), dim3((unsigned)grid),
+                     dim3(64 * DEC_WAVES), 0, stream, reinterpret_cast<const __half*>(x), m, signs,
+                     c32, w_codes, w_scales, k, y);
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_ld_n(const uint16_t* x, int64_t m, const int8_t* signs, const uint8_t* w_codes,
+                       const uint16_t* w_scales, int64_t k, uint16_t* y, hipStream_t stream) {
+  // Two 16-row weight groups per workgroup when that still gives every CU a
+  // workgroup: the kernel holds a whole row rotation, so fewer of its
+  // workgroups fit on a CU than of the plain decode kernel.
+  const bool rg2 = (k + 31) / 32 >= (int64_t)cu_count();
+  if (signs != nullptr)
+    return rg2 ? launch_ld<N, true, 2>(x, m, signs, w_codes, w_scales, k, y, stream)
+               : launch_ld<N, true, 1>(x, m, signs, w_codes, w_scales, k, y, stream);
+  return rg2 ? launch_ld<N, false, 2>(x, m, signs, w_codes, w_scales, k, y, stream)
+             : launch_ld<N, false, 1>(x, m, signs, w_codes, w_scales, k, y, stream);
+}
+}  // namespace
+
+hipError_t launch_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                                const uint8_t* w_codes, const uint16_t* w_scales, int64_t k,
+                                uint16_t* y, void* workspace, hipStream_t stream) {
+  if (m > LD_FUSED_M) {
+    // More tokens than the prologue rotates cheaply: the rotation kernel
+    // writes codes and scales into the workspace, then the decode GEMM.
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    uint16_t* scales = reinterpret_cast<uint16_t*>(codes + m * (d / 2));
+    const hipError_t e =
+        launch_fwht_quant(x, false, m, (int)d, signs, codes, scales, nullptr, stream);
+    if (e != hipSuccess) return e;
+    return launch_w4a4_gemm(codes, scales, m, w_codes, w_scales, k, d, y, nullptr, stream);
+  }
+  switch (d) {
+    case 512: return launch_ld_n<512>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 1024: return launch_ld_n<1024>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 2048: return launch_ld_n<2048>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 4096: return launch_ld_n<4096>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 8192: return launch_ld_n<8192>(x, m, signs, w_codes, w_scales, k, y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace rq

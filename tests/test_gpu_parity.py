@@ -214,6 +214,64 @@ def test_decode_linear_end_to_end(rq):
         check_codes(O.unpack_int4(host(ac)), mirror_a, "decode activations")
 
 
+def test_linear_decode_fused_matches_two_launches(rq):
+    """rq_linear_decode (one launch for m <= 4: the rotation as the GEMM's
+    prologue) gives the same y as rq_fwht_quant followed by rq_w4a4_gemm, bit
+    for bit, on the decode-linear workload; for m = 16 the codes and scales it
+    hands over in the workspace are rq_fwht_quant's."""
+    dec = datagen.decode_linear(0)
+    s = dev(dec["signs"])
+    ws = rq.linear_decode_workspace(16, 4096, torch.device("cuda"))
+    for k, wt in dec["wts"].items():
+        wc, wsc, _ = rq.fold_weights(dev(wt), s)
+        for m in (1, 2, 4, 16):
+            say(f"fused decode linear m={m} k={k}")
+            x = dev(dec["x"][:m])
+            for rep in range(2):  # the same workspace twice
+                y = rq.linear_decode(x, s, wc, wsc, workspace=ws)
+                torch.cuda.synchronize()
+                y_ref = rq.w4a4_linear(x, s, wc, wsc)
+                torch.cuda.synchronize()
+                assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (m, k, rep)
+        ac, sa, _ = rq.fwht_quant(dev(dec["x"]), s)
+        torch.cuda.synchronize()
+        assert torch.equal(ws[:16 * 2048].view(16, 2048), ac)
+        assert torch.equal(ws[16 * 2048:16 * 2048 + 32].view(torch.float16), sa)
+
+
+@pytest.mark.parametrize("m,k,d,with_signs", [(4, 5, 512, True), (3, 40, 8192, True),
+                                              (2, 300, 1024, False), (1, 12300, 2048, True),
+                                              (4, 14336, 4096, True), (16, 5, 512, True),
+                                              (7, 300, 1024, False)])
+def test_linear_decode_fused_shapes(rq, m, k, d, with_signs):
+    """One workgroup (k = 5), both weight-group widths (k = 12300, 14336 give
+    two 16-row groups per workgroup), every n class, no signs, and the
+    two-launch route (m > 4); y against the oracle's pipeline and against the
+    two-launch path."""
+    rng = np.random.default_rng(m * 7 + k + d)
+    x = (rng.standard_normal((m, d)) * np.where(rng.random(d) < 0.01, 50.0, 1.0)).astype(np.float16)
+    wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
+    signs = datagen.rademacher(rng, d) if with_signs else None
+    sd = dev(signs) if with_signs else None
+    say(f"fused decode linear m={m} k={k} d={d} signs={with_signs}")
+    wc, wsc, _ = rq.fold_weights(dev(wt), sd)
+    y = rq.linear_decode(dev(x), sd, wc, wsc)
+    torch.cuda.synchronize()
+    y_ref = rq.w4a4_linear(dev(x), sd, wc, wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    # the pieces against the oracle: codes up to the 1e-6 rounding band, the
+    # GEMM of those codes exactly
+    ac, sa, xr = rq.fwht_quant(dev(x), sd, debug=True)
+    wr = rq.fold_weights(dev(wt), sd, debug=True)[2]
+    torch.cuda.synchronize()
+    check_rotation_result(x, signs, host(ac), host(sa), host(xr), what="fused decode activations")
+    check_rotation_result(wt, signs, host(wc), host(wsc), host(wr), what="fused decode weights")
+    y_o, _ = check_gemm(host(ac), host(sa), host(wc), host(wsc), host(y), None,
+                        what="fused decode y")
+    np.testing.assert_array_equal(host(y).view(np.uint16), y_o.view(np.uint16))
+
+
 def test_tiny_linear_end_to_end(rq):
     cfg = datagen.tiny_linear(0)
     s = dev(cfg["signs"])
