@@ -49,6 +49,8 @@ import numpy as np
 
 __all__ = [
     "hadamard_transform",
+    "paley_hadamard_28",
+    "kron28_transform",
     "rotate",
     "fp16_rne",
     "quantize_rows",
@@ -67,6 +69,102 @@ QMIN, QMAX = -8, 7
 def _check_pow2(n: int) -> None:
     if n < 1 or (n & (n - 1)) != 0:
         raise ValueError(f"rotation length must be a power of two, got {n}")
+
+
+def _is_pow2(n: int) -> bool:
+    return n >= 1 and (n & (n - 1)) == 0
+
+
+def _is_28_pow2(n: int) -> bool:
+    """n = 28 * 2^k (k >= 0): the non-power-of-two lengths supported."""
+    return n >= 28 and n % 28 == 0 and _is_pow2(n // 28)
+
+
+def _legendre(a: int, q: int) -> int:
+    """Quadratic character of a modulo the odd prime q (Euler's criterion)."""
+    a %= q
+    if a == 0:
+        return 0
+    return 1 if pow(a, (q - 1) // 2, q) == 1 else -1
+
+
+def paley_hadamard_28() -> np.ndarray:
+    """A Hadamard matrix of order 28, by Paley's second construction.
+
+    [RQ] "Learned Orthogonal Rotations: SpinQuant": fixed Hadamard rotations
+    need power-of-two sizes or products of small Hadamard-compatible factors
+    (the input of the down projection, which needs an online rotation
+    ([RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms",
+    part 2), is 14336 = 28 * 512 wide in Llama-class models).  Construction
+    (Paley II, q = 13, a prime with q = 1 mod 4): the Jacobsthal matrix
+    Q[a][b] = chi(a - b) over GF(13), chi the quadratic character; the
+    symmetric conference matrix C = [[0, 1^T], [1, Q]] of order 14 with
+    C C^T = 13 I; then H = C (x) [[1, 1], [1, -1]] + I (x) [[1, -1], [-1, -1]],
+    entries +-1, H H^T = 28 I, and H symmetric.  Index 2i + c of H is
+    (row i of C, component c).
+    """
+    q = 13
+    jac = np.array([[_legendre(a - b, q) for b in range(q)] for a in range(q)], dtype=np.int64)
+    conf = np.zeros((q + 1, q + 1), dtype=np.int64)
+    conf[0, 1:] = 1
+    conf[1:, 0] = 1
+    conf[1:, 1:] = jac
+    h2 = np.array([[1, 1], [1, -1]], dtype=np.int64)
+    j2 = np.array([[1, -1], [-1, -1]], dtype=np.int64)
+    return (np.kron(conf, h2) + np.kron(np.eye(q + 1, dtype=np.int64), j2)).astype(np.int8)
+
+
+def _paley_conference_14() -> np.ndarray:
+    """The order-14 conference matrix C of :func:`paley_hadamard_28`."""
+    h = paley_hadamard_28().astype(np.int64)
+    return h[0::2, 0::2] - np.eye(14, dtype=np.int64)  # C[j][i] + delta_ij * J2[0][0]
+
+
+def kron28_transform(u: np.ndarray, precision: str = "f64") -> np.ndarray:
+    """Unnormalised (H_28 (x) H_P) transform along the last axis, n = 28 * P.
+
+    Element e = P * b + p (block b of 28, position p inside the block).
+    Step 1: the Sylvester FWHT of length P inside every block
+    (:func:`hadamard_transform`, ascending strides).  Step 2: for every
+    position, y[b'] = sum_b H_28[b'][b] t[b] (H_28 symmetric).
+    "f64": step 2 is the dense 28 x 28 product in float64.
+    "f32": step 2 in float32, in the order that the Paley structure
+    H_28 = C (x) H_2 + I (x) J_2 gives: a_i = t[2i] + t[2i+1],
+    d_i = t[2i] - t[2i+1]; then y[2j] = (sum over i != j, ascending, of
+    C[j][i] a_i) + d_j and y[2j+1] = (the same sum of C[j][i] d_i) - a_j,
+    each sum accumulated left to right (C[j][i] = +-1 is a sign flip).
+    """
+    u = np.asarray(u)
+    n = u.shape[-1]
+    if not _is_28_pow2(n):
+        raise ValueError(f"length must be 28 * 2^k, got {n}")
+    pw = n // 28
+    lead = u.shape[:-1]
+    dt = np.float64 if precision == "f64" else np.float32
+    t = hadamard_transform(u.astype(dt).reshape(lead + (28, pw)))
+    if precision == "f64":
+        h = paley_hadamard_28().astype(np.float64)
+        y = np.einsum("ab,...bp->...ap", h, t)
+        return y.reshape(lead + (n,))
+    if precision != "f32":
+        raise ValueError(f"precision must be 'f64' or 'f32', got {precision!r}")
+    conf = _paley_conference_14()
+    a = t[..., 0::2, :] + t[..., 1::2, :]   # [..., 14, P]
+    d = t[..., 0::2, :] - t[..., 1::2, :]
+    y = np.empty_like(t)
+    for j in range(14):
+        acc_a = None
+        acc_d = None
+        for i in range(14):
+            if i == j:
+                continue
+            sa = a[..., i, :] if conf[j, i] > 0 else -a[..., i, :]
+            sd = d[..., i, :] if conf[j, i] > 0 else -d[..., i, :]
+            acc_a = sa.copy() if acc_a is None else acc_a + sa
+            acc_d = sd.copy() if acc_d is None else acc_d + sd
+        y[..., 2 * j, :] = acc_a + d[..., j, :]
+        y[..., 2 * j + 1, :] = acc_d - a[..., j, :]
+    return y.reshape(lead + (n,)).astype(np.float32)
 
 
 def hadamard_transform(u: np.ndarray) -> np.ndarray:
@@ -114,21 +212,24 @@ def rotate(x: np.ndarray, signs: np.ndarray | None, precision: str = "f64") -> n
     butterflies use only add/sub and one global scalar multiplication at the
     end.  The sign diagonal comes first (x * s, then H), the order in which
     the rotated linear layer is specified; the fold below uses the same R.
-    ``signs=None`` means s = 1 (plain H_n / sqrt(n)).
+    ``signs=None`` means s = 1 (plain H_n / sqrt(n)).  For n = 28 * 2^k the
+    Hadamard factor is H_28 (x) H_(n/28) (:func:`kron28_transform`).
     """
     x = np.asarray(x)
     n = x.shape[-1]
-    _check_pow2(n)
+    if not _is_28_pow2(n):
+        _check_pow2(n)
     if precision == "f64":
         u = x.astype(np.float64)
         if signs is not None:
             u = u * np.asarray(signs).astype(np.float64)
-        return hadamard_transform(u) / np.sqrt(np.float64(n))
+        y = kron28_transform(u, "f64") if _is_28_pow2(n) else hadamard_transform(u)
+        return y / np.sqrt(np.float64(n))
     if precision == "f32":
         u = x.astype(np.float32)
         if signs is not None:
             u = u * np.asarray(signs).astype(np.float32)  # exact: s = +-1
-        y = hadamard_transform(u)
+        y = kron28_transform(u, "f32") if _is_28_pow2(n) else hadamard_transform(u)
         return (y * _inv_sqrt_f32(n)).astype(np.float32)
     raise ValueError(f"precision must be 'f64' or 'f32', got {precision!r}")
 

@@ -405,3 +405,81 @@ def test_kv_oracle_is_rowwise_fwht_quant():
     flat = O.fwht_quant(k.reshape(-1, 128), None, "f64")
     np.testing.assert_array_equal(out["k_codes"].reshape(-1, 64), flat["codes"])
     assert out["k_codes"].shape == (2, 3, 5, 64) and out["v_scales"].shape == (2, 3, 5)
+
+
+# ---------------------------------------------------------------------------
+# Non-power-of-two rotation length n = 28 * 2^k (H_28 (x) H_(n/28))
+
+def test_paley_28_is_a_symmetric_hadamard_matrix():
+    h = O.paley_hadamard_28().astype(np.int64)
+    assert h.shape == (28, 28)
+    assert set(np.unique(h).tolist()) == {-1, 1}
+    np.testing.assert_array_equal(h @ h.T, 28 * np.eye(28, dtype=np.int64))
+    np.testing.assert_array_equal(h, h.T)
+
+
+def test_paley_28_conference_matrix_and_residues():
+    # textbook: the quadratic residues modulo 13 are {1, 3, 4, 9, 10, 12}
+    assert sorted({(a * a) % 13 for a in range(1, 13)}) == [1, 3, 4, 9, 10, 12]
+    c = O._paley_conference_14()
+    assert (np.diag(c) == 0).all()
+    assert (c[0, 1:] == 1).all() and (c[1:, 0] == 1).all()
+    # C[1 + a][1 + b] = chi(a - b), chi = +1 on the residues, -1 off them
+    res = {1, 3, 4, 9, 10, 12}
+    for a in range(13):
+        for b in range(13):
+            if a != b:
+                assert c[1 + a, 1 + b] == (1 if (a - b) % 13 in res else -1)
+    np.testing.assert_array_equal(c @ c.T, 13 * np.eye(14, dtype=np.int64))
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 8])
+def test_kron28_transform_equals_dense_kronecker_product(p):
+    import scipy.linalg
+    rng = np.random.default_rng(p)
+    x = rng.standard_normal((3, 28 * p))
+    dense = np.kron(O.paley_hadamard_28().astype(np.float64), scipy.linalg.hadamard(p).astype(np.float64))
+    np.testing.assert_allclose(O.kron28_transform(x, "f64"), x @ dense.T, rtol=0, atol=1e-12)
+    # the structured float32 order stays within float32 rounding of the truth
+    y32 = O.kron28_transform(x.astype(np.float32), "f32").astype(np.float64)
+    assert np.abs(y32 - x.astype(np.float32).astype(np.float64) @ dense.T).max() <= 1e-5 * 28 * p
+
+
+def test_kron28_f32_integer_inputs_are_exact():
+    # small integers: every partial sum is an integer below 2^24, so the
+    # structured float32 order must equal the exact product
+    rng = np.random.default_rng(3)
+    x = rng.integers(-50, 50, size=(4, 28 * 16))
+    exact = O.kron28_transform(x.astype(np.float64), "f64")
+    np.testing.assert_array_equal(O.kron28_transform(x.astype(np.float32), "f32").astype(np.float64), exact)
+
+
+@pytest.mark.parametrize("n", [28, 112, 448])
+def test_rotation_28_orthogonal_and_invariant(n):
+    rng = np.random.default_rng(n)
+    s = datagen.rademacher(rng, n)
+    r = O.rotate(np.eye(n), s, "f64")          # row i of R = e_i R
+    np.testing.assert_allclose(r @ r.T, np.eye(n), atol=1e-12)
+    x = rng.standard_normal((5, n))
+    w = rng.standard_normal((n, 7))
+    xr = O.rotate(x, s, "f64")
+    wt_r = O.rotate(w.T, s, "f64")             # rows of W^T R, i.e. (R^T W)^T
+    np.testing.assert_allclose(xr @ wt_r.T, x @ w, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+
+
+@pytest.mark.parametrize("i", [0, 511, 7000, 14335])
+def test_rotation_14336_one_hot_spike(i):
+    n = 28 * 512
+    x = np.zeros((1, n))
+    x[0, i] = 3.0
+    y = O.rotate(x, None, "f64")
+    np.testing.assert_allclose(np.abs(y), 3.0 / np.sqrt(n), rtol=1e-14)
+
+
+def test_fwht_quant_14336_codes_in_range():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 14336)).astype(np.float16)
+    r = O.fwht_quant(x, datagen.rademacher(rng, 14336), "f32")
+    assert r["codes"].shape == (2, 7168) and r["q"].min() >= -8 and r["q"].max() <= 7
+    assert (np.abs(r["q"]).max(axis=1) == 7).all()
