@@ -283,6 +283,33 @@ def main():
             sec["linear_prefill_rotate_plus_gemm"] = {"us": round(msl * 1e3, 2)}
             del wcs, wc, y
 
+        if want("downproj"):
+            # the online rotation in front of a down projection: 2048 tokens x
+            # 14336 = 28 * 512 (H_28 (x) H_512), same input statistics as the
+            # prefill activations
+            mm, d = 2048, 14336
+            rng = np.random.default_rng(4)
+            x28 = datagen.activations(rng, mm, d, datagen.outlier_channels(rng, d), 100.0)
+            x28 = torch.from_numpy(x28).to(dev)
+            s28 = torch.from_numpy(datagen.rademacher(rng, d)).to(dev)
+            ac28 = torch.empty((mm, d // 2), dtype=torch.uint8, device=dev)
+            sa28 = torch.empty((mm,), dtype=torch.float16, device=dev)
+            fsets = -(-2 * MALL_BYTES // (x28.numel() * 2)) + 1
+            x28s = [x28] + [x28.clone() for _ in range(fsets - 1)]
+
+            def f28(i):
+                st = lib.rq_fwht_quant(_ptr(x28s[i]), RQ_F16, mm, d, _ptr(s28), _ptr(ac28),
+                                       _ptr(sa28), None, _stream())
+                assert st == 0
+
+            ms28 = time_launches(torch, f28, fsets, steps2, warm2)
+            b = fwht_bytes(mm, d)
+            sec["fwht_quant_2048x14336"] = {"us": round(ms28 * 1e3, 3),
+                                            "GB/s": round(b / (ms28 * 1e-3) / 1e9, 1),
+                                            "hbm_frac": round(b / (ms28 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] fwht_quant 2048x14336: {sec['fwht_quant_2048x14336']}")
+            del x28s, x28
+
         if want("kv"):
             kv = datagen.kv_cache(0)
             kt = torch.from_numpy(kv["k"]).to(dev)

@@ -55,9 +55,21 @@ typedef enum {
 
 typedef enum { RQ_F16 = 0, RQ_F32 = 1 } rq_dtype;
 
-/* Smallest and largest supported rotation length n (both powers of two). */
+/* Smallest and largest supported power-of-two rotation length n. */
 #define RQ_MIN_N 2
 #define RQ_MAX_N 8192
+/*
+ * The one supported length that is not a power of two: 28 * 512 = 14336, the
+ * input width of a Llama-class down projection ([RQ] "Learned Orthogonal
+ * Rotations: SpinQuant": fixed Hadamard rotations need power-of-two sizes or
+ * products of small Hadamard-compatible sizes).  Its Hadamard factor is
+ * H_28 (x) H_512 (element e = 512 b + p), H_28 from Paley's second
+ * construction with q = 13 (symmetric, H_28 H_28^T = 28 I).  The 512-point
+ * factor runs first (ascending strides), then H_28 in the order of its Paley
+ * structure H_28 = C (x) H_2 + I (x) [[1, -1], [-1, -1]], C the conference
+ * matrix of order 14.
+ */
+#define RQ_N_28X512 14336
 
 /*
  * rq_fwht_quant -- online rotation fused with per-token INT4 quantisation.
@@ -72,7 +84,8 @@ typedef enum { RQ_F16 = 0, RQ_F32 = 1 } rq_dtype;
  *   x       [m][n] activations, dtype x_dtype (RQ_F16 or RQ_F32), row major,
  *           16-byte aligned.
  *   m       number of rows (tokens), >= 0.
- *   n       rotation length, power of two in [RQ_MIN_N, RQ_MAX_N].
+ *   n       rotation length, a power of two in [RQ_MIN_N, RQ_MAX_N] or
+ *           RQ_N_28X512.
  *   signs   [n] int8, each +1 or -1; NULL means all +1 (plain H_n/sqrt(n)).
  *   codes   [m][n/2] uint8 output, 16-byte aligned.
  *   scales  [m] fp16 output (one per row).
@@ -99,7 +112,8 @@ int rq_fwht_quant(const void* x, int x_dtype, int64_t m, int64_t n, const int8_t
  *            W~^T is w_j R = (w_j * s) H_d / sqrt(d): the same row transform
  *            as rq_fwht_quant, with the same signs as the activations.
  *   k        output channels (rows of W^T), >= 0.
- *   d        input width, power of two in [RQ_MIN_N, RQ_MAX_N].
+ *   d        input width, a power of two in [RQ_MIN_N, RQ_MAX_N] or
+ *            RQ_N_28X512.
  *   signs    [d] int8 +-1 or NULL.
  *   w_codes  [k][d/2] uint8 output; w_scales [k] fp16 output.
  *   w_rot    optional [k][d] float32 output of W~^T (debug), or NULL.

@@ -355,6 +355,229 @@ __global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_ke
 }
 
 // ------------------------------------------------------------------------
+// n = 28 * 512 = 14336 (the width of a Llama-class down projection input):
+// H_14336 = H_28 (x) H_512, H_28 by Paley's second construction with q = 13
+// ([RQ] "Learned Orthogonal Rotations: SpinQuant": fixed Hadamard rotations
+// need power-of-two sizes or products of small Hadamard-compatible sizes;
+// [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms", part 2:
+// the down projection's input needs an online rotation).  Element
+// e = 512 b + p: block b of 28, position p of 512.
+//
+// One row per 512-thread workgroup at a time.  Wave w rotates blocks w, w + 8,
+// w + 16 (and w + 24) with the 512-point stages of the row kernel (one
+// 16-byte chunk per lane and block) and writes them, sign-corrected, to LDS in
+// fp32; the next row's chunks are loaded while the rest of the row runs.
+// After a barrier, thread t takes position t and applies H_28 across the 28
+// blocks in the order the Paley structure H_28 = C (x) H_2 + I (x) J_2 gives
+// (C the order-14 conference matrix, J_2 = [[1, -1], [-1, -1]]):
+// a_i = t_2i + t_2i+1, d_i = t_2i - t_2i+1, then y_2j = sum over i != j of
+// C[j][i] a_i (ascending i) + d_j and y_2j+1 = sum of C[j][i] d_i - a_j.
+// That is 420 add/sub per position instead of 756 for the dense product.
+
+// Quadratic character modulo 13 by Euler's criterion, a^6 mod 13.
+constexpr int paley_chi13(int a) {
+  a = ((a % 13) + 13) % 13;
+  if (a == 0) return 0;
+  int r = 1;
+  for (int i = 0; i < 6; ++i) r = (r * a) % 13;
+  return r == 1 ? 1 : -1;
+}
+// Conference matrix of order 14: 0 on the diagonal, ones in the first row and
+// column, the Jacobsthal matrix chi(a - b) elsewhere.
+constexpr int paley_conf14(int j, int i) {
+  return j == i ? 0 : (j == 0 || i == 0) ? 1 : paley_chi13((j - 1) - (i - 1));
+}
+
+constexpr int kN28 = 28 * 512;
+constexpr int k28Waves = 8;  // wavefronts per workgroup
+
+// The 16-byte (fp16) or 32-byte (fp32) chunk of elements 8L .. 8L + 7 of one
+// block, as raw words.
+template <typename T>
+struct Chunk28 {
+  v4u w[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ Chunk28<T> load_chunk28(const T* xr, int e0) {
+  Chunk28<T> c;
+#pragma unroll
+  for (int h = 0; h < (int)(sizeof(T) / 2); ++h)
+    c.w[h] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(xr + e0 + 8 / (int)(sizeof(T) / 2) * h));
+  return c;
+}
+
+// Signs, then e0 of the 512-point transform on one chunk.
+template <typename T, bool HAS_SIGNS>
+__device__ __forceinline__ void chunk28_e0(const Chunk28<T>& raw, const int8_t* signs, int e0,
+                                           float (&c)[8]) {
+  uint2 sg = make_uint2(0u, 0u);
+  if constexpr (HAS_SIGNS) sg = *reinterpret_cast<const uint2*>(signs + e0);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w = raw.w[0][q];
+      if constexpr (HAS_SIGNS) {
+        const uint32_t s2 = q < 2 ? sg.x : sg.y;
+        const uint32_t b0 = (2u * q) & 3u;
+        const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
+        w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;
+      }
+      c[2 * q] = mix_add(w);
+      c[2 * q + 1] = mix_sub(w);
+    }
+  } else {
+    float v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = u2f(raw.w[r >> 2][r & 3]);
+    if constexpr (HAS_SIGNS) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t sbyte = (r < 4 ? sg.x : sg.y) >> (8 * (r & 3));
+        v[r] = u2f(f2u(v[r]) ^ ((sbyte & 0x80u) << 24));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[2 * q] = v[2 * q] + v[2 * q + 1];
+      c[2 * q + 1] = v[2 * q] - v[2 * q + 1];
+    }
+  }
+}
+
+template <typename T, bool HAS_SIGNS>
+__global__ __launch_bounds__(64 * k28Waves) void fwht28x512_kernel(FQOut o, int64_t rows,
+                                                                  const int8_t* __restrict__ signs,
+                                                                  float c32) {
+  constexpr int P = 512, NB = 28, BPW = (NB + k28Waves - 1) / k28Waves;  // blocks per wave (4 or 3)
+  __shared__ __align__(16) float xb[NB][P];  // 56 KB; then the code bytes of the row
+  __shared__ float amx[k28Waves];
+  const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+  const RowLane rl = make_row_lane(L);
+  unsigned char* cbuf = reinterpret_cast<unsigned char*>(&xb[0][0]);
+
+  int64_t row = blockIdx.x;
+  if (row >= rows) return;  // uniform per workgroup
+  // wave w owns blocks w, w + 8, w + 16 (and w + 24 for w < 4)
+  Chunk28<T> raw[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i)
+    if (wave + k28Waves * i < NB)
+      raw[i] = load_chunk28(static_cast<const T*>(o.x) + row * kN28, P * (wave + k28Waves * i) + 8 * L);
+
+  for (;;) {
+    // 1. the 512-point stages of this wave's blocks, sign-corrected into LDS
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int b = wave + k28Waves * i;
+      if (b >= NB) continue;  // uniform per wave
+      float c[8];
+      chunk28_e0<T, HAS_SIGNS>(raw[i], signs, P * b + 8 * L, c);
+      chunk512_stages(c, rl);
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const int p = (rl.lane_pair << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8);
+        *reinterpret_cast<float2*>(&xb[b][p]) = make_float2(c[r] * rl.sigma, c[r + 1] * rl.sigma);
+      }
+    }
+    // the next row's chunks are in flight during the rest of this row
+    const int64_t next = row + gridDim.x;
+    const bool more = next < rows;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        if (wave + k28Waves * i < NB)
+          raw[i] = load_chunk28(static_cast<const T*>(o.x) + next * kN28,
+                                P * (wave + k28Waves * i) + 8 * L);
+    }
+    __syncthreads();
+
+    // 2. H_28 across the blocks for position tid
+    float y[NB];
+    {
+      float a[14], d[14];
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        const float t0 = xb[2 * i][tid], t1 = xb[2 * i + 1][tid];
+        a[i] = t0 + t1;
+        d[i] = t0 - t1;
+      }
+#pragma unroll
+      for (int j = 0; j < 14; ++j) {
+        float sa = 0.0f, sd = 0.0f;
+        bool first = true;
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+          if (i == j) continue;
+          const bool pos = paley_conf14(j, i) > 0;
+          if (first) {
+            sa = pos ? a[i] : -a[i];
+            sd = pos ? d[i] : -d[i];
+            first = false;
+          } else if (pos) {
+            sa += a[i];
+            sd += d[i];
+          } else {
+            sa -= a[i];
+            sd -= d[i];
+          }
+        }
+        y[2 * j] = sa + d[j];
+        y[2 * j + 1] = sd - a[j];
+      }
+    }
+
+    // 3. absmax over the row
+    float amax = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) amax = fmaxf(amax, fabsf(y[b]));
+    amax = wave_max(amax);
+    if (L == 0) amx[wave] = amax;
+    __syncthreads();  // also: every thread has read xb
+#pragma unroll
+    for (int w = 0; w < k28Waves; ++w) amax = fmaxf(amax, amx[w]);
+    const uint16_t hb = scale_fp16(amax * c32);
+    const bool subnormal = hb != 0 && hb < 0x0400u;
+    const float mult = hb == 0 ? 0.0f : c32 / h2f(hb);
+    if (tid == 0) o.scales[row] = hb;
+    if (o.xrot != nullptr) {
+      float* xo = o.xrot + row * kN28;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xo[P * b + tid] = y[b] * c32;
+    }
+
+    // 4. codes: element 512 b + tid is nibble (tid & 1) of byte 256 b + tid / 2;
+    // the odd lane's code reaches its even neighbour by DPP
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float q = __builtin_fmaf(y[b], mult, kMagic);
+      if (subnormal) q = fminf(fmaxf(q, kMagicLo), kMagicHi);
+      const uint32_t code = f2u(q) & 0xFu;
+      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, 0xB1, 0xF, 0xF, false);
+      if (!(tid & 1)) cbuf[256 * b + (tid >> 1)] = (unsigned char)((code | (other << 4)) ^ 0x88u);
+    }
+    __syncthreads();
+    uint8_t* dst = o.codes + row * (kN28 / 2);
+    for (int c = tid; c < kN28 / 32; c += 64 * k28Waves)
+      __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(cbuf + 16 * c),
+                                  reinterpret_cast<v4u*>(dst + 16 * c));
+    if (!more) break;
+    __syncthreads();  // the next row overwrites xb
+    row = next;
+  }
+}
+
+template <typename T, bool HAS_SIGNS>
+hipError_t launch_28(FQOut o, int64_t rows, const int8_t* signs, hipStream_t stream) {
+  const float c32 = (float)(1.0 / __builtin_sqrt((double)kN28));
+  const int64_t cap = (int64_t)cu_count() * 2;  // two 56 KB workgroups per CU
+  const int64_t blocks = rows < cap ? rows : cap;
+  hipLaunchKernelGGL((fwht28x512_kernel<T, HAS_SIGNS>), dim3((unsigned)blocks), dim3(64 * k28Waves), 0,
+                     stream, o, rows, signs, c32);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
 // fp16 rows with n = 128 (the per-head KV rotation): four lanes per row,
 // sixteen rows per wavefront, 32 elements per lane, no LDS.
 //
@@ -560,6 +783,13 @@ int cu_count() {
 hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, const int8_t* signs,
                              uint8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream) {
   const FQOut o{x, codes, scales, x_rot};
+  if (n == kN28) {
+    if (is_f32)
+      return signs ? launch_28<float, true>(o, rows, signs, stream)
+                   : launch_28<float, false>(o, rows, signs, stream);
+    return signs ? launch_28<__half, true>(o, rows, signs, stream)
+                 : launch_28<__half, false>(o, rows, signs, stream);
+  }
   if (is_f32) {
     return signs ? dispatch_n<float, true>(o, o, 1, rows, n, signs, stream)
                  : dispatch_n<float, false>(o, o, 1, rows, n, signs, stream);

@@ -22,7 +22,7 @@ int check_rotation_args(const void* x, int dtype, int64_t m, int64_t n, const in
                         const void* codes, const void* scales, const void* rot) {
   if (dtype != RQ_F16 && dtype != RQ_F32) return RQ_ERR_DTYPE;
   if (m < 0 || m >= kMaxRows) return RQ_ERR_SHAPE;
-  if (!is_pow2(n) || n < RQ_MIN_N || n > RQ_MAX_N) return RQ_ERR_SHAPE;
+  if (n != RQ_N_28X512 && (!is_pow2(n) || n < RQ_MIN_N || n > RQ_MAX_N)) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return RQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return RQ_ERR_ALIGN;

@@ -194,6 +194,52 @@ __device__ __forceinline__ RowLane make_row_lane(int L) {
   return rl;
 }
 
+// Stages e1..e8 of a 512-element FWHT held as one 16-byte chunk per lane
+// (lane L owns elements 8L .. 8L + 7 in c[0..7], e0 already applied): the
+// same operations as inside row_rotate_quant.  On return element
+// p(r) = (r & 1) | (lane_pair << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8)
+// of the block sits in c[r], multiplied by rl.sigma.
+__device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl) {
+  const float(&g)[4] = rl.g;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {  // e1
+    if (!(r & 2)) { const float x0 = c[r], x1 = c[r + 2]; c[r] = x0 + x1; c[r + 2] = x0 - x1; }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {  // e2
+    if (!(r & 4)) { const float x0 = c[r], x1 = c[r + 4]; c[r] = x0 + x1; c[r + 4] = x0 - x1; }
+  }
+  RQ_DPP8("quad_perm:[1,0,3,2]", c, g[0]);  // e3
+  RQ_DPP8("quad_perm:[2,3,0,1]", c, g[1]);  // e4
+  RQ_DPP8("row_half_mirror", c, g[2]);      // e5
+  RQ_DPP8("row_ror:8", c, g[3]);            // e6
+  // lane bit 4 (e7) <-> register bit 2 (e2); lane bit 5 (e8) <-> register bit 1 (e1)
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (!(r & 4)) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(f2u(c[r]), f2u(c[r + 4]), false, false);
+      c[r] = u2f(sw[0]);
+      c[r + 4] = u2f(sw[1]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (!(r & 2)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(f2u(c[r]), f2u(c[r + 2]), false, false);
+      c[r] = u2f(sw[0]);
+      c[r + 2] = u2f(sw[1]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {  // e7
+    if (!(r & 4)) { const float x0 = c[r], x1 = c[r + 4]; c[r] = x0 + x1; c[r + 4] = x0 - x1; }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {  // e8
+    if (!(r & 2)) { const float x0 = c[r], x1 = c[r + 2]; c[r] = x0 + x1; c[r + 2] = x0 - x1; }
+  }
+}
+
 // Rotates and quantises the row whose chunks `raw` holds (loaded by
 // load_row): lane 0 writes the fp16 scale to *scale_out, the wavefront writes
 // the n/2 code bytes to codes_row through its LDS slice cb (n/2 bytes), or,

@@ -72,6 +72,45 @@ def test_fwht_quant_all_sizes_ragged(rq, n, dtype):
         assert np.array_equal(c, c2) and np.array_equal(s, s2)
 
 
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("m", [1, 7, 600])
+def test_fwht_quant_28x512(rq, m, dtype):
+    """n = 28 * 512 (H_28 (x) H_512): rotated rows bit-identical to the
+    oracle's fp32 mirror, codes within the rounding band; 600 rows exceed the
+    grid, so workgroups take several rows."""
+    n = 14336
+    rng = np.random.default_rng(m)
+    say(f"fwht_quant n=28x512 m={m} dtype={np.dtype(dtype).name}")
+    x = (rng.standard_normal((m, n)) * rng.uniform(0.1, 10, (m, 1))).astype(dtype)
+    x[:, rng.choice(n, 14, replace=False)] *= 100  # outlier channels
+    for signs in (datagen.rademacher(rng, n), None):
+        c, s, r = run_fq(rq, x, signs, fold=dtype == np.float32)
+        check_rotation_result(x, signs, c, s, r, what=f"n=28x512 m={m}", report=REPORT)
+        c2, s2, _ = run_fq(rq, x, signs, debug=False)
+        assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+@pytest.mark.parametrize("m,k", [(4, 40), (300, 256)])
+def test_linear_28x512(rq, m, k):
+    """A W4A4 linear with d = 14336 (the down projection width): the fold and
+    the online rotation with H_28 (x) H_512, then the decode (m = 4) or the
+    large (m = 300) GEMM, against the oracle."""
+    d = 14336
+    rng = np.random.default_rng(m + k)
+    x = (rng.standard_normal((m, d)) * np.where(rng.random(d) < 0.001, 100.0, 1.0)).astype(np.float16)
+    wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
+    signs = datagen.rademacher(rng, d)
+    say(f"linear d=28x512 m={m} k={k}")
+    s = dev(signs)
+    wc, ws, wr = rq.fold_weights(dev(wt), s, debug=True)
+    ac, sa, xr = rq.fwht_quant(dev(x), s, debug=True)
+    y, acc = rq.w4a4_gemm(ac, sa, wc, ws, debug=True)
+    torch.cuda.synchronize()
+    check_rotation_result(wt, signs, host(wc), host(ws), host(wr), what="fold d=28x512")
+    check_rotation_result(x, signs, host(ac), host(sa), host(xr), what="activations d=28x512")
+    check_gemm(host(ac), host(sa), host(wc), host(ws), host(y), host(acc), what="gemm d=28x512")
+
+
 def test_fwht_quant_special_rows(rq):
     n = 4096
     rng = np.random.default_rng(5)
