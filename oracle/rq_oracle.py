@@ -59,11 +59,15 @@ __all__ = [
     "fwht_quant",
     "fold_weights",
     "w4a4_gemm",
+    "quantize_rows_int8",
+    "fwht_quant8",
+    "w4a8_gemm",
     "kv_rotate_quant",
     "dequantize",
 ]
 
 QMIN, QMAX = -8, 7
+QMIN8, QMAX8 = -128, 127
 
 
 def _check_pow2(n: int) -> None:
@@ -360,6 +364,61 @@ def w4a4_gemm(a_codes: np.ndarray, a_scales: np.ndarray, w_codes: np.ndarray,
     if qa.shape[-1] != qw.shape[-1]:
         raise ValueError("inner dimensions differ")
     acc = _int_matmul_nt(qa, qw)
+    sa = np.asarray(a_scales).astype(np.float64)[:, None]
+    sw = np.asarray(w_scales).astype(np.float64)[None, :]
+    y = fp16_rne(acc.astype(np.float64) * sa * sw)
+    return y, acc
+
+
+def quantize_rows_int8(xt: np.ndarray):
+    """Symmetric per-row INT8 quantisation of rotated rows (the W4A8 variant).
+
+    [SpinQuant] "The architecture: every piece explained" and "End-to-end
+    flow": INT4 weights with INT8 activations.  Same rule as
+    :func:`quantize_rows` with 2^7 - 1 in place of 2^3 - 1:
+    scale = fp16_rne(max|x~| / 127), q = clamp(rne(x~/scale), -128, 127),
+    a zero scale gives zero codes.  Returns (q int8, scales float16, v).
+    """
+    xt64 = np.asarray(xt).astype(np.float64)
+    a = np.max(np.abs(xt64), axis=-1)
+    scales = fp16_rne(a / 127.0)
+    s = scales.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s > 0, xt64 / np.where(s > 0, s, 1.0), 0.0)
+    q = np.clip(np.rint(v), QMIN8, QMAX8).astype(np.int8)
+    return q, scales, v
+
+
+def fwht_quant8(x: np.ndarray, signs: np.ndarray | None, precision: str = "f64") -> dict:
+    """Online rotation fused with per-token INT8 quantisation (W4A8).
+
+    [SpinQuant] "End-to-end flow" (runtime: the rotated activation is
+    quantised to INT8); the rotation is :func:`rotate`.  Returns codes int8
+    [m, n] (one byte per element, two's complement), scales float16 [m],
+    x_rot, q (= codes) and v.
+    """
+    xt = rotate(x, signs, precision)
+    q, scales, v = quantize_rows_int8(xt)
+    return {"codes": q.copy(), "scales": scales, "x_rot": xt, "q": q, "v": v}
+
+
+def w4a8_gemm(a_codes8: np.ndarray, a_scales: np.ndarray, w_codes: np.ndarray,
+              w_scales: np.ndarray):
+    """W4A8 linear: INT8 activation codes times packed INT4 weight codes.
+
+    [SpinQuant] "The architecture: every piece explained" (INT4 weights,
+    INT8 activations).  acc[m][j] = sum_i qa[m][i] * qw[j][i] (exact
+    integers), y = fp16_rne(acc * sa[m] * sw[j]) with the product in float64.
+    Returns (y float16 [m, k], acc int64 [m, k]).
+    """
+    qa = np.asarray(a_codes8).astype(np.int8)
+    qw = unpack_int4(w_codes)
+    if qa.shape[-1] != qw.shape[-1]:
+        raise ValueError("inner dimensions differ")
+    d = qa.shape[-1]
+    if 1024 * d >= 2 ** 53:
+        raise ValueError("d too large for an exact float64 accumulation")
+    acc = (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
     sa = np.asarray(a_scales).astype(np.float64)[:, None]
     sw = np.asarray(w_scales).astype(np.float64)[None, :]
     y = fp16_rne(acc.astype(np.float64) * sa * sw)

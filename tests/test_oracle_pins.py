@@ -483,3 +483,76 @@ def test_fwht_quant_14336_codes_in_range():
     r = O.fwht_quant(x, datagen.rademacher(rng, 14336), "f32")
     assert r["codes"].shape == (2, 7168) and r["q"].min() >= -8 and r["q"].max() <= 7
     assert (np.abs(r["q"]).max(axis=1) == 7).all()
+
+
+# ---------------------------------------------------------------------------
+# W4A8 variant: INT8 per-token activations
+
+def test_int8_quantizer_rounding_table_and_range():
+    # scale = 1 exactly: max |x| = 127 -> fp16_rne(127/127) = 1
+    xt = np.array([[127.0, -126.5, -125.5, 0.5, 1.5, -0.5, 2.4999, 3.5000001, -127.0]])
+    q, s, v = O.quantize_rows_int8(xt)
+    assert s[0] == np.float16(1.0)
+    # round half to even: -126.5 -> -126, -125.5 -> -126, 0.5 -> 0, 1.5 -> 2, -0.5 -> 0
+    np.testing.assert_array_equal(q[0], [127, -126, -126, 0, 2, 0, 2, 4, -127])
+
+
+def test_int8_one_hot_and_zero_rows():
+    n = 512
+    x = np.zeros((2, n))
+    x[0, 9] = 5.0
+    r = O.fwht_quant8(x, None, "f64")
+    # one-hot -> every rotated element is +-5/sqrt(n): all codes +-127
+    assert (np.abs(r["q"][0]) == 127).all()
+    assert r["scales"][1] == 0 and (r["q"][1] == 0).all()
+
+
+def test_int8_scale_single_rounding_and_clamp():
+    # a/127 just above an fp16 midpoint rounds up; the clamp keeps +-127 bounds
+    rng = np.random.default_rng(4)
+    xt = rng.standard_normal((64, 256)) * 3
+    q, s, v = O.quantize_rows_int8(xt)
+    a = np.abs(xt).max(axis=1)
+    np.testing.assert_array_equal(s, (a / 127.0).astype(np.float16))
+    assert q.min() >= -128 and q.max() <= 127
+    # |x/scale| <= 127 * (1 + 2^-11) < 127.5, so -128 never appears for normal scales
+    assert q.min() >= -127
+    rec = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    assert np.all(np.abs(rec - xt) <= 0.5 * s.astype(np.float64)[:, None] + 1e-12)
+
+
+def test_w4a8_gemm_brute_force_and_closed_form():
+    rng = np.random.default_rng(6)
+    qa = rng.integers(-128, 128, size=(3, 64)).astype(np.int8)
+    qw = rng.integers(-8, 8, size=(5, 64)).astype(np.int8)
+    sa = np.array([0.5, 1.0, 2.0], np.float16)
+    sw = np.array([1.0, 0.25, 0.5, 1.0, 2.0], np.float16)
+    y, acc = O.w4a8_gemm(qa, sa, O.pack_int4(qw), sw)
+    for i in range(3):
+        for j in range(5):
+            want = sum(int(qa[i, t]) * int(qw[j, t]) for t in range(64))
+            assert acc[i, j] == want
+            assert y[i, j] == np.float16(want * float(sa[i]) * float(sw[j]))
+    # extremes: -128 * -8 over d = 8192 = 8388608 (exact)
+    d = 8192
+    y2, acc2 = O.w4a8_gemm(np.full((1, d), -128, np.int8), np.ones(1, np.float16),
+                           O.pack_int4(np.full((1, d), -8)), np.ones(1, np.float16))
+    assert acc2[0, 0] == 1024 * d
+
+
+def test_w4a8_tracks_float_linear_better_than_w4a4():
+    rng = np.random.default_rng(12)
+    d, k, m = 1024, 64, 16
+    x = rng.standard_normal((m, d))
+    x[:, 5] *= 100
+    w = rng.standard_normal((d, k)) * 0.02
+    s = datagen.rademacher(rng, d)
+    ref = x @ w
+    wq = O.fold_weights(w.T, s, "f64")
+    a8 = O.fwht_quant8(x, s, "f64")
+    a4 = O.fwht_quant(x, s, "f64")
+    y8, _ = O.w4a8_gemm(a8["codes"], a8["scales"], wq["codes"], wq["scales"])
+    y4, _ = O.w4a4_gemm(a4["codes"], a4["scales"], wq["codes"], wq["scales"])
+    e8 = np.abs(y8.astype(np.float64) - ref).mean()
+    e4 = np.abs(y4.astype(np.float64) - ref).mean()
+    assert e8 < e4
