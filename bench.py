@@ -53,6 +53,16 @@ def gemm_bytes(m: int, k: int, d: int) -> int:
     return d * k // 2 + 2 * k + m * d // 2 + 2 * m + 2 * m * k
 
 
+def fwht8_bytes(m: int, n: int) -> int:
+    # fp16 input + one int8 code per element + fp16 scales + int8 signs
+    return m * n * 2 + m * n + 2 * m + n
+
+
+def gemm8_bytes(m: int, k: int, d: int) -> int:
+    # as gemm_bytes with one byte per activation code
+    return d * k // 2 + 2 * k + m * d + 2 * m + 2 * m * k
+
+
 def kv_bytes(rows: int) -> int:
     return 2 * (rows * 128 * 2 + rows * 64 + rows * 2)
 
@@ -309,6 +319,71 @@ def main():
                                             "hbm_frac": round(b / (ms28 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"[bench] fwht_quant 2048x14336: {sec['fwht_quant_2048x14336']}")
             del x28s, x28
+
+        if want("w4a8"):
+            # the W4A8 variant: INT8 per-token activations against the same
+            # folded INT4 weights
+            w8 = datagen.fwht_workload(0)
+            m8, n8 = w8["m"], w8["d"]
+            x8 = torch.from_numpy(w8["x"]).to(dev)
+            s8 = torch.from_numpy(w8["signs"]).to(dev)
+            per8 = fwht8_bytes(m8, n8)
+            sets8 = max(2, -(-2 * MALL_BYTES // per8) + 1)
+            x8s = [x8] + [x8.clone() for _ in range(sets8 - 1)]
+            o8 = [(torch.empty((m8, n8), dtype=torch.int8, device=dev),
+                   torch.empty((m8,), dtype=torch.float16, device=dev)) for _ in range(sets8)]
+
+            def fq8(i):
+                st = lib.rq_fwht_quant8(_ptr(x8s[i]), m8, n8, _ptr(s8), _ptr(o8[i][0]),
+                                        _ptr(o8[i][1]), None, _stream())
+                assert st == 0
+
+            ms8 = time_launches(torch, fq8, sets8, steps2, warm2)
+            sec["fwht_quant8_4096x4096"] = {"us": round(ms8 * 1e3, 3),
+                                            "GB/s": round(per8 / (ms8 * 1e-3) / 1e9, 1),
+                                            "hbm_frac": round(per8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] fwht_quant8 4096x4096: {sec['fwht_quant8_4096x4096']}")
+            del x8s, o8, x8
+            dec = datagen.decode_linear(0)
+            s = torch.from_numpy(dec["signs"]).to(dev)
+            ac8, sa8, _ = rq.fwht_quant8(torch.from_numpy(dec["x"]).to(dev), s)
+            for k, wt in dec["wts"].items():
+                wc, ws, _ = rq.fold_weights(torch.from_numpy(wt).to(dev), s)
+                nsets = max(2, -(-2 * MALL_BYTES // wc.numel()) + 1)
+                wcs = [wc.clone() for _ in range(nsets)]
+                for mm in (1, 4, 16):
+                    y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+                    a_m, s_m = ac8[:mm].contiguous(), sa8[:mm].contiguous()
+
+                    def g8(i, a_m=a_m, s_m=s_m, y=y):
+                        rq.w4a8_gemm(a_m, s_m, wcs[i], ws, out=y)
+
+                    msg = time_launches(torch, g8, nsets, steps2, warm2)
+                    bb = gemm8_bytes(mm, k, 4096)
+                    key = f"gemm_w4a8_decode_m{mm}_k{k}"
+                    sec[key] = {"us": round(msg * 1e3, 3), "GB/s": round(bb / (msg * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(bb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    log(f"[bench] {key}: {sec[key]}")
+                del wcs, wc
+            pf = datagen.prefill_linear(0)
+            sp = torch.from_numpy(pf["signs"]).to(dev)
+            wc, ws, _ = rq.fold_weights(torch.from_numpy(pf["wt"]).to(dev), sp)
+            del pf["wt"]
+            mm, d, k = pf["m"], pf["d"], pf["k"]
+            ac8, sa8, _ = rq.fwht_quant8(torch.from_numpy(pf["x"]).to(dev), sp)
+            y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+            wcs = [wc, wc.clone()]
+
+            def gp8(i):
+                rq.w4a8_gemm(ac8, sa8, wcs[i], ws, out=y)
+
+            msp = time_launches(torch, gp8, 2, max(5, steps2 // 4), warm2)
+            tops = 2 * mm * d * k / (msp * 1e-3) / 1e12
+            sec["gemm_w4a8_prefill_2048x8192x28672"] = {
+                "us": round(msp * 1e3, 2), "TOPS": round(tops, 1),
+                "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+            log(f"[bench] w4a8 prefill gemm: {sec['gemm_w4a8_prefill_2048x8192x28672']}")
+            del wcs, wc, y, ac8
 
         if want("kv"):
             kv = datagen.kv_cache(0)

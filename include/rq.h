@@ -214,6 +214,54 @@ int rq_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* sign
                      const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rq_fwht_quant8 -- online rotation fused with per-token INT8 quantisation,
+ * the activation side of the W4A8 variant.
+ *
+ * [SpinQuant] "The architecture: every piece explained" and "End-to-end
+ * flow" (INT4 weights with 8-bit activations: the rotated activation is
+ * quantised to INT8 at run time).  The rotation is the one of rq_fwht_quant
+ * (same stages, same fp32 rounding); the quantiser is the symmetric per-row
+ * rule with 127 in place of 7: scale = fp16_rne(max |x~| / 127) rounded once
+ * from the exact quotient, code = rne(x~ / scale) in [-128, 127] (a zero
+ * scale gives zero codes).
+ *
+ *   x       [m][n] fp16 activations, row major, 16-byte aligned.
+ *   m       rows (tokens), >= 0.
+ *   n       a power of two in [512, RQ_MAX_N].
+ *   signs   [n] int8 +-1, or NULL for all +1; 16-byte aligned when given.
+ *   codes   [m][n] int8 output (one two's-complement code per element),
+ *           16-byte aligned.
+ *   scales  [m] fp16 output.
+ *   x_rot   optional [m][n] float32 rotated rows, or NULL.
+ */
+int rq_fwht_quant8(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs, int8_t* codes,
+                   uint16_t* scales, float* x_rot, void* stream);
+
+/*
+ * rq_w4a8_gemm -- W4A8 linear: INT8 activation codes times packed INT4
+ * folded weight codes, y = fp16(acc * sa[m] * sw[j]),
+ * acc[m][j] = sum_i qa[m][i] * qw[j][i] in int32.
+ *
+ * [SpinQuant] "The architecture: every piece explained" (INT4 weights, INT8
+ * activations, integer matmul).  The weight codes are widened to 16 * q in
+ * int8 lanes and multiplied with the activation bytes by int8 MFMA; the
+ * int32 sum is exactly 16 * acc (|16 * acc| <= 2^14 * d).  The epilogue is
+ * the one of rq_w4a4_gemm.
+ *
+ *   a_codes  [m][d] int8 activation codes (rq_fwht_quant8), 16-byte aligned;
+ *            a_scales [m] fp16.
+ *   m        tokens, >= 0.
+ *   w_codes  [k][d/2] uint8 weight codes (rq_fold_weights), 16-byte aligned;
+ *            w_scales [k] fp16.
+ *   k        output channels, >= 1 when m > 0.
+ *   d        reduction length, a multiple of 64 in [64, 16384].
+ *   y        [m][k] fp16 output; acc optional [m][k] int32 accumulators.
+ */
+int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                 const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                 uint16_t* y, int32_t* acc, void* stream);
+
 /* Text for an rq_status value (static storage, never NULL). */
 const char* rq_status_string(int status);
 

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     RQError,
     fold_weights,
     fwht_quant,
+    fwht_quant8,
     kv_rotate_quant,
     linear_decode,
     linear_decode_workspace,
@@ -19,5 +20,7 @@ from .binding import (  # noqa: F401
     version,
     w4a4_gemm,
     w4a4_linear,
+    w4a8_gemm,
+    w4a8_linear,
 )
 from .build import LIB_PATH  # noqa: F401

@@ -27,6 +27,8 @@ EXPORTED = (
     "rq_kv_rotate_quant",
     "rq_linear_decode_workspace_size",
     "rq_linear_decode",
+    "rq_fwht_quant8",
+    "rq_w4a8_gemm",
     "rq_status_string",
     "rq_version",
 )
@@ -65,6 +67,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_linear_decode_workspace_size.restype = sz
     lib.rq_linear_decode.argtypes = [p, i64, i64, p, p, p, i64, p, p, sz, p]
     lib.rq_linear_decode.restype = i32
+    lib.rq_fwht_quant8.argtypes = [p, i64, i64, p, p, p, p, p]
+    lib.rq_fwht_quant8.restype = i32
+    lib.rq_w4a8_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, p, p]
+    lib.rq_w4a8_gemm.restype = i32
     lib.rq_status_string.argtypes = [i32]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_version.argtypes = []
@@ -227,4 +233,55 @@ def linear_decode(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Te
     st = load_library().rq_linear_decode(_ptr(x), m, d, _ptr(s), _ptr(w_codes), _ptr(w_scales), k,
                                          _ptr(y), _ptr(ws), ws.numel(), _stream())
     _check("rq_linear_decode", st)
+    return y
+
+
+def fwht_quant8(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+    """rq_fwht_quant8 (W4A8 activations): returns (codes int8 [m, n],
+    scales fp16 [m], x_rot fp32 or None)."""
+    _need_cuda("x", x)
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a float16 [rows, n] tensor")
+    rows, n = x.shape
+    s = _signs(signs, n, x.device)
+    codes = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+    scales = torch.empty((rows,), dtype=torch.float16, device=x.device)
+    rot = torch.empty((rows, n), dtype=torch.float32, device=x.device) if debug else None
+    st = load_library().rq_fwht_quant8(_ptr(x), rows, n, _ptr(s), _ptr(codes), _ptr(scales),
+                                       _ptr(rot), _stream())
+    _check("rq_fwht_quant8", st)
+    return codes, scales, rot
+
+
+def w4a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+              w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
+    """rq_w4a8_gemm: INT8 activation codes [m, d] times packed INT4 weight
+    codes [k, d/2]; returns (y fp16 [m, k], acc int32 [m, k] or None)."""
+    for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes),
+                    ("w_scales", w_scales)):
+        _need_cuda(name, t)
+    if a_codes.dtype != torch.int8 or w_codes.dtype != torch.uint8:
+        raise ValueError("activation codes must be int8 and weight codes uint8")
+    if a_scales.dtype != torch.float16 or w_scales.dtype != torch.float16:
+        raise ValueError("scales must be float16")
+    m, d = a_codes.shape
+    k, half_d = w_codes.shape
+    if d != 2 * half_d:
+        raise ValueError("activation and weight codes differ in d")
+    if a_scales.numel() != m or w_scales.numel() != k:
+        raise ValueError("scale counts do not match the code rows")
+    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
+    acc = torch.empty((m, k), dtype=torch.int32, device=a_codes.device) if debug else None
+    st = load_library().rq_w4a8_gemm(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes),
+                                     _ptr(w_scales), k, d, _ptr(y), _ptr(acc), _stream())
+    _check("rq_w4a8_gemm", st)
+    return y, acc
+
+
+def w4a8_linear(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tensor,
+                w_scales: torch.Tensor) -> torch.Tensor:
+    """Online rotation + INT8 quantisation of x, then the W4A8 GEMM against
+    INT4 weights folded with the same signs.  Two launches."""
+    codes, scales, _ = fwht_quant8(x, signs)
+    y, _ = w4a8_gemm(codes, scales, w_codes, w_scales)
     return y

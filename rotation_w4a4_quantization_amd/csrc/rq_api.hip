@@ -51,6 +51,16 @@ int rq_fold_weights(const void* wt, int wt_dtype, int64_t k, int64_t d, const in
                                         w_scales, w_rot, static_cast<hipStream_t>(stream)));
 }
 
+int rq_fwht_quant8(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs, int8_t* codes,
+                   uint16_t* scales, float* x_rot, void* stream) {
+  if (m < 0 || m >= kMaxRows) return RQ_ERR_SHAPE;
+  if (!is_pow2(n) || n < 512 || n > RQ_MAX_N) return RQ_ERR_SHAPE;
+  const int st = check_rotation_args(x, RQ_F16, m, n, signs, codes, scales, x_rot);
+  if (st != RQ_OK || m == 0) return st;
+  return from_hip(rq::launch_fwht_quant8(x, m, (int)n, signs, codes, scales, x_rot,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d) {
   (void)m;
   (void)k;
@@ -91,6 +101,22 @@ int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
   if (signs != nullptr && !aligned16(signs)) return RQ_ERR_ALIGN;
   return from_hip(rq::launch_kv_rotate_quant(k_in, v_in, rows, signs, k_codes, k_scales, v_codes,
                                              v_scales, static_cast<hipStream_t>(stream)));
+}
+
+int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                 const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                 uint16_t* y, int32_t* acc, void* stream) {
+  if (m < 0 || k < 0 || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (k == 0) return RQ_ERR_SHAPE;
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr || w_scales == nullptr ||
+      y == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_w4a8_gemm(a_codes, a_scales, m, w_codes, w_scales, k, d, y, acc,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 size_t rq_linear_decode_workspace_size(int64_t m, int64_t d) {

@@ -16,6 +16,11 @@ int cu_count();
 hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, const int8_t* signs,
                              uint8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream);
 
+// Row-wise (x * s) H_n / sqrt(n) fused with symmetric per-row INT8
+// quantisation (fp16 x, n in 512..8192 a power of two); codes [rows][n].
+hipError_t launch_fwht_quant8(const uint16_t* x, int64_t rows, int n, const int8_t* signs,
+                              int8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream);
+
 // Same transform for the two KV tensors (fp16, n = 128) in one launch.
 hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
                                   const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
@@ -23,6 +28,12 @@ hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, in
 
 // y[m][k] = fp16(acc * sa * sw), acc = qa . qw over d.
 hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                            const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                            uint16_t* y, int32_t* acc, hipStream_t stream);
+
+// W4A8: y[m][k] = fp16(acc * sa * sw), acc = qa . qw over d with INT8
+// activation codes qa ([m][d] bytes) and packed INT4 weight codes.
+hipError_t launch_w4a8_gemm(const int8_t* a_codes8, const uint16_t* a_scales, int64_t m,
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream);
 

@@ -27,6 +27,11 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr float kMagic = 8388616.0f;
 constexpr float kMagicLo = 8388608.0f;   // code -8
 constexpr float kMagicHi = 8388623.0f;   // code +7
+// The same for INT8 codes: fma(v, m, kMagic8) = 2^23 + 128 + rne(v*m) for
+// |v*m| < 128 leaves the offset-binary code q + 128 in the low 8 bits.
+constexpr float kMagic8 = 8388736.0f;
+constexpr float kMagic8Lo = 8388608.0f;  // code -128
+constexpr float kMagic8Hi = 8388863.0f;  // code +127
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
 
@@ -35,20 +40,23 @@ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(flo
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h_rn(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
-// fp16_rne(xm / 7) rounded once from the exact quotient (xm >= 0, finite).
-// The fp32 quotient is correctly rounded; only when it lands exactly on an
-// fp16 rounding midpoint can a second rounding go the wrong way, and then the
-// exact residual xm - 7q (representable, computed exactly by fma) says on
-// which side of the midpoint the true quotient lies.
+// fp16_rne(xm / D) rounded once from the exact quotient (xm >= 0, finite;
+// D = 7 for INT4 codes, 127 for INT8).  The fp32 quotient is correctly
+// rounded; only when it lands exactly on an fp16 rounding midpoint can a
+// second rounding go the wrong way, and then the exact residual xm - D q says
+// on which side of the midpoint the true quotient lies.  The residual is a
+// multiple of ulp(q) below D ulp(q) in size, so it is representable and the
+// fma computes it exactly.
+template <int D = 7>
 __device__ __forceinline__ uint16_t scale_fp16(float xm) {
-  const float q = xm / 7.0f;
+  const float q = xm / (float)D;
   uint16_t hb = f2h_rn(q);
   const float back = (hb == 0x7C00u) ? 65536.0f : h2f(hb);
   if (q != back) {
     const uint16_t ob = (back < q) ? (uint16_t)(hb + 1) : (uint16_t)(hb - 1);
     const float other = (ob == 0x7C00u) ? 65536.0f : h2f(ob);
     if (q == 0.5f * (back + other)) {
-      const float r = __builtin_fmaf(-7.0f, q, xm);
+      const float r = __builtin_fmaf(-(float)D, q, xm);
       if (r > 0.0f) hb = hb > ob ? hb : ob;
       else if (r < 0.0f) hb = hb < ob ? hb : ob;
     }
@@ -242,10 +250,11 @@ __device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl
 
 // Rotates and quantises the row whose chunks `raw` holds (loaded by
 // load_row): lane 0 writes the fp16 scale to *scale_out, the wavefront writes
-// the n/2 code bytes to codes_row through its LDS slice cb (n/2 bytes), or,
-// with TO_LDS, leaves them in cb (codes_row unused), and the fp32 rotated row
-// goes to xrot_row when it is not null.
-template <int N, bool HAS_SIGNS, bool TO_LDS = false>
+// the code bytes (n/2 packed INT4 codes, or n INT8 codes for BITS == 8) to
+// codes_row through its LDS slice cb (as many bytes), or, with TO_LDS, leaves
+// them in cb (codes_row unused), and the fp32 rotated row goes to xrot_row
+// when it is not null.
+template <int N, bool HAS_SIGNS, bool TO_LDS = false, int BITS = 4>
 __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
                                                  const int8_t* __restrict__ signs, int L,
                                                  const RowLane& rl, float c32, unsigned char* cb,
@@ -325,7 +334,11 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
   for (int r = 0; r < R; ++r) amax = fmaxf(amax, fabsf(u[r]));
   amax = wave_max(amax);
 
-  const uint16_t hb = scale_fp16(amax * c32);
+  static_assert(BITS == 4 || BITS == 8, "INT4 or INT8 codes");
+  constexpr float kM = BITS == 4 ? kMagic : kMagic8;
+  constexpr float kMLo = BITS == 4 ? kMagicLo : kMagic8Lo;
+  constexpr float kMHi = BITS == 4 ? kMagicHi : kMagic8Hi;
+  const uint16_t hb = scale_fp16<BITS == 4 ? 7 : 127>(amax * c32);
   const bool subnormal = hb != 0 && hb < 0x0400u;
   const float mult = (hb == 0 ? 0.0f : c32 / h2f(hb)) * sigma;
   if (L == 0) *scale_out = hb;
@@ -342,28 +355,34 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
 
   float t[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) t[r] = __builtin_fmaf(u[r], mult, kMagic);
+  for (int r = 0; r < R; ++r) t[r] = __builtin_fmaf(u[r], mult, kM);
   if (subnormal) {  // uniform: the scale is shared by the whole row
 #pragma unroll
-    for (int r = 0; r < R; ++r) t[r] = fminf(fmaxf(t[r], kMagicLo), kMagicHi);
+    for (int r = 0; r < R; ++r) t[r] = fminf(fmaxf(t[r], kMLo), kMHi);
   }
   // The wavefront stages its row's code bytes in its own LDS slice and
   // reads them back as 16-byte chunks; LDS instructions of one wavefront
   // execute in order, so only the compiler needs fencing here.
 #pragma unroll
   for (int r = 0; r < R; r += 2) {
-    const uint32_t byte = (f2u(t[r + 1]) << 4) | f2u(t[r]);  // low byte: (q1+8)<<4 | (q0+8)
     const int p = (((r >> 2) & 1) << 6) | (((r >> 1) & 1) << 7) | ((r >> 3) << 8);
-    cb[lp + p] = (unsigned char)byte;
+    if constexpr (BITS == 4) {
+      const uint32_t byte = (f2u(t[r + 1]) << 4) | f2u(t[r]);  // low byte: (q1+8)<<4 | (q0+8)
+      cb[lp + p] = (unsigned char)byte;
+    } else {  // elements 2(lp + p) and + 1: bytes (q0+128), (q1+128)
+      const uint32_t pair = (f2u(t[r]) & 0xFFu) | ((f2u(t[r + 1]) & 0xFFu) << 8);
+      *reinterpret_cast<uint16_t*>(cb + 2 * (lp + p)) = (uint16_t)pair;
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint8_t* dst = codes_row;
+  constexpr int kCodeBytes = BITS == 4 ? N / 2 : N;
 #pragma unroll
-  for (int c = L; c < N / 32; c += 64) {
+  for (int c = L; c < kCodeBytes / 16; c += 64) {
     v4u v = *reinterpret_cast<const v4u*>(cb + 16 * c);
-    v ^= 0x88888888u;
+    v ^= BITS == 4 ? 0x88888888u : 0x80808080u;
     if constexpr (TO_LDS)
       *reinterpret_cast<v4u*>(cb + 16 * c) = v;
     else

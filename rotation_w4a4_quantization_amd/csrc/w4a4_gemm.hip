@@ -31,6 +31,17 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// 16 INT8 activation codes (natural order) rearranged into the k order that
+// widen() gives the weight codes: (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,...).
+__device__ __forceinline__ v4i order_a8(const uint4& q) {
+  v4i r;
+  r[0] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
+  r[1] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
+  r[2] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
+  r[3] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
+  return r;
+}
+
 __device__ __forceinline__ v4i widen(uint32_t w0, uint32_t w1) {
   v4i r;
   r[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
@@ -41,9 +52,12 @@ __device__ __forceinline__ v4i widen(uint32_t w0, uint32_t w1) {
 }
 
 
+// raw is 256 * acc for INT4 activations (both operands widened to 16 q) and
+// 16 * acc for INT8 activations (SHIFT 4): the shift is exact.
+template <int SHIFT = 8>
 __device__ __forceinline__ void epilogue_store(int32_t raw, float sa, float sw, int64_t idx,
                                                uint16_t* __restrict__ y, int32_t* __restrict__ acc) {
-  const int32_t a = raw >> 8;  // exact: raw is 256 * acc
+  const int32_t a = raw >> SHIFT;
   if (acc != nullptr) acc[idx] = a;
   y[idx] = f2h_rn(((float)a * sa) * sw);
 }
@@ -54,7 +68,10 @@ __device__ __forceinline__ void epilogue_store(int32_t raw, float sa, float sw, 
 constexpr int TM = 128, TN = 128, TK = 64;
 constexpr int ROWB = TK / 2;      // packed bytes per row per step
 constexpr int PITCH = ROWB + 8;   // LDS row pitch (bytes), breaks the 32-byte stride
+constexpr int PITCH8 = TK + 16;   // INT8 activation rows (64 bytes per step), 16-byte aligned
 
+// A8: INT8 activation codes ([m][d] bytes, W4A8); the MFMA sum is 16 * acc.
+template <bool A8 = false>
 __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restrict__ a_codes,
                                                         const uint16_t* __restrict__ a_scales,
                                                         const uint8_t* __restrict__ w_codes,
@@ -62,7 +79,9 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
                                                         int64_t m, int64_t k, int64_t d,
                                                         uint16_t* __restrict__ y,
                                                         int32_t* __restrict__ acc_out) {
-  __shared__ __align__(16) unsigned char sa_tile[TM * PITCH];
+  constexpr int AW = A8 ? 2 : 1;  // activation bytes per weight byte
+  constexpr int APITCH = A8 ? PITCH8 : PITCH;
+  __shared__ __align__(16) unsigned char sa_tile[TM * APITCH];
   __shared__ __align__(16) unsigned char sb_tile[TN * PITCH];
 
   const int tid = threadIdx.x;
@@ -83,24 +102,35 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
   const int lhalf = tid & 1;   // which 16-byte half of the 32-byte step
   const bool a_ok = m0 + lrow < m;
   const bool b_ok = n0 + lrow < k;
-  const uint8_t* a_src = a_codes + (m0 + lrow) * rowb + 16 * lhalf;
+  const uint8_t* a_src = a_codes + (m0 + lrow) * rowb * AW + 16 * AW * lhalf;
   const uint8_t* b_src = w_codes + (n0 + lrow) * rowb + 16 * lhalf;
 
   const int g = lane >> 4;     // k group of this lane inside an MFMA operand
   const int r16 = lane & 15;
 
   for (int64_t kb = 0; kb < rowb; kb += ROWB) {
-    const uint4 av = a_ok ? *reinterpret_cast<const uint4*>(a_src + kb) : make_uint4(0, 0, 0, 0);
+    uint4 av[AW];
+#pragma unroll
+    for (int u = 0; u < AW; ++u)
+      av[u] = a_ok ? *reinterpret_cast<const uint4*>(a_src + AW * kb + 16 * u)
+                   : make_uint4(0, 0, 0, 0);
     const uint4 bv = b_ok ? *reinterpret_cast<const uint4*>(b_src + kb) : make_uint4(0, 0, 0, 0);
     __syncthreads();  // previous step's fragments have been read
-    *reinterpret_cast<uint4*>(sa_tile + lrow * PITCH + 16 * lhalf) = av;
+#pragma unroll
+    for (int u = 0; u < AW; ++u)
+      *reinterpret_cast<uint4*>(sa_tile + lrow * APITCH + 16 * (AW * lhalf + u)) = av[u];
     *reinterpret_cast<uint4*>(sb_tile + lrow * PITCH + 16 * lhalf) = bv;
     __syncthreads();
     v4i af[4], bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint2 p = *reinterpret_cast<const uint2*>(sa_tile + (wm * 64 + i * 16 + r16) * PITCH + 8 * g);
-      af[i] = widen(p.x, p.y);
+      const unsigned char* ap = sa_tile + (wm * 64 + i * 16 + r16) * APITCH;
+      if constexpr (A8) {
+        af[i] = order_a8(*reinterpret_cast<const uint4*>(ap + 16 * g));
+      } else {
+        const uint2 p = *reinterpret_cast<const uint2*>(ap + 8 * g);
+        af[i] = widen(p.x, p.y);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -125,7 +155,9 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = n0 + wn * 64 + j * 16 + r16;
-        if (col < k) epilogue_store(acc[i][j][e], sa, h2f(w_scales[col]), row * k + col, y, acc_out);
+        if (col < k)
+          epilogue_store<A8 ? 4 : 8>(acc[i][j][e], sa, h2f(w_scales[col]), row * k + col, y,
+                                     acc_out);
       }
     }
   }
@@ -275,22 +307,28 @@ __device__ __forceinline__ void dec_issue_w(const DecLane<RG>& t, int64_t c0) {
 
 // Activation fragments of the chunk, wait for them and for the chunk's
 // weights, then the MFMAs; this wave's LDS reads are back on return (before
-// its next loads may overwrite them).
-template <int RG>
+// its next loads may overwrite them).  A8: the activations are INT8 codes
+// (one byte per code, a_src advancing 2 bytes per weight byte), so a lane's
+// 32 codes of a part take two 16-byte loads.
+template <int RG, bool A8 = false>
 __device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsigned char* wl,
                                               const uint8_t* a_src, bool a_ok, int64_t c0,
                                               v4i (&acc0)[RG], v4i (&acc1)[RG]) {
   constexpr int SEGB = 16 * RG * DSEG;
-  uint4 av[2][2];
+  constexpr int AW = A8 ? 2 : 1;  // 16-byte activation loads per part
+  uint4 av[2][2][AW];
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     const int64_t seg = c0 + 2 * t.wave + sl;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      av[sl][h] = make_uint4(0, 0, 0, 0);
-      if (a_ok && seg < t.nseg)
-        av[sl][h] = *reinterpret_cast<const uint4*>(a_src + seg * DSEG + 64 * h);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < AW; ++u) {
+        av[sl][h][u] = make_uint4(0, 0, 0, 0);
+        if (a_ok && seg < t.nseg)
+          av[sl][h][u] =
+              *reinterpret_cast<const uint4*>(a_src + AW * (seg * DSEG + 64 * h) + 16 * u);
+      }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
@@ -298,7 +336,14 @@ __device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsign
     if (c0 + 2 * t.wave + sl >= t.nseg) continue;  // uniform per wave
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const v4i a0 = widen(av[sl][h].x, av[sl][h].y), a1 = widen(av[sl][h].z, av[sl][h].w);
+      v4i a0, a1;
+      if constexpr (A8) {
+        a0 = order_a8(av[sl][h][0]);
+        a1 = order_a8(av[sl][h][AW - 1]);
+      } else {
+        a0 = widen(av[sl][h][0].x, av[sl][h][0].y);
+        a1 = widen(av[sl][h][0].z, av[sl][h][0].w);
+      }
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         const uint4 w = *reinterpret_cast<const uint4*>(
@@ -314,7 +359,7 @@ __device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsign
 
 // Partial sums of the 8 waves meet in LDS (wave w's RG x 64 sums start at
 // partial + w * pitch); waves 0..RG-1 finish one 16-row group each.
-template <int RG>
+template <int RG, int SHIFT = 8>
 __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* partial, int pitch,
                                                  const v4i (&acc0)[RG], const v4i (&acc1)[RG],
                                                  int64_t m, int64_t k,
@@ -335,14 +380,17 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 4 * t.g + e;
-        if (row < m) epilogue_store(s[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out);
+        if (row < m)
+          epilogue_store<SHIFT>(s[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out);
       }
     }
   }
 }
 
 // RG 16-row groups of weights per workgroup share each activation fragment.
-template <int RG>
+// A8: INT8 activation codes ([m][d] bytes) against the INT4 weights (W4A8);
+// the MFMA sum is then 16 * acc.
+template <int RG, bool A8 = false>
 __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int64_t m,
@@ -352,17 +400,18 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
   const int64_t rowb = d / 2;
   const DecLane<RG> t = dec_lane<RG>(w_codes, k, rowb, wl);
   const bool a_ok = t.r16 < m;
-  const uint8_t* a_src = a_codes + (int64_t)(a_ok ? t.r16 : 0) * rowb + 16 * t.g;
+  constexpr int AW = A8 ? 2 : 1;  // activation bytes per weight byte
+  const uint8_t* a_src = a_codes + (int64_t)(a_ok ? t.r16 : 0) * rowb * AW + 16 * AW * t.g;
 
   v4i acc0[RG], acc1[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
   for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
     dec_issue_w(t, c0);
-    dec_mma_chunk(t, wl, a_src, a_ok, c0, acc0, acc1);
+    dec_mma_chunk<RG, A8>(t, wl, a_src, a_ok, c0, acc0, acc1);
   }
-  dec_reduce_store(t, &partial[0][0][0], RG * 64, acc0, acc1, m, k, a_scales, w_scales, y,
-                   acc_out);
+  dec_reduce_store<RG, A8 ? 4 : 8>(t, &partial[0][0][0], RG * 64, acc0, acc1, m, k, a_scales,
+                                   w_scales, y, acc_out);
 }
 
 // ------------------------------------------------------- fused decode linear
@@ -703,7 +752,28 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
                          a_codes, a_scales, w_codes, w_scales, m, k, d, y, acc);
   } else {
     const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
-    hipLaunchKernelGGL(w4a4_tile_kernel, grid, dim3(256), 0, stream, a_codes, a_scales, w_codes,
+    hipLaunchKernelGGL(w4a4_tile_kernel<false>, grid, dim3(256), 0, stream, a_codes, a_scales,
+                       w_codes, w_scales, m, k, d, y, acc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm(const int8_t* a_codes8, const uint16_t* a_scales, int64_t m,
+                            const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
+                            uint16_t* y, int32_t* acc, hipStream_t stream) {
+  const uint8_t* a = reinterpret_cast<const uint8_t*>(a_codes8);
+  if (m <= 16 && d % (2 * DSEG) == 0) {
+    if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
+      hipLaunchKernelGGL((w4a4_decode_lds_kernel<2, true>), dim3((unsigned)((k + 31) / 32)),
+                         dim3(64 * DEC_WAVES), 0, stream, a, a_scales, w_codes, w_scales, m, k, d,
+                         y, acc);
+    else
+      hipLaunchKernelGGL((w4a4_decode_lds_kernel<1, true>), dim3((unsigned)((k + 15) / 16)),
+                         dim3(64 * DEC_WAVES), 0, stream, a, a_scales, w_codes, w_scales, m, k, d,
+                         y, acc);
+  } else {
+    const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
+    hipLaunchKernelGGL(w4a4_tile_kernel<true>, grid, dim3(256), 0, stream, a, a_scales, w_codes,
                        w_scales, m, k, d, y, acc);
   }
   return hipGetLastError();

@@ -131,3 +131,8 @@ def random_codes(rng: np.random.Generator, rows: int, d: int) -> np.ndarray:
 
 def random_scales(rng: np.random.Generator, rows: int, lo: float = 1e-3, hi: float = 1.0) -> np.ndarray:
     return rng.uniform(lo, hi, size=rows).astype(np.float16)
+
+
+def random_codes8(rng: np.random.Generator, rows: int, d: int) -> np.ndarray:
+    """Uniform random INT8 activation codes [rows][d] (every value in [-128, 127])."""
+    return rng.integers(-128, 128, size=(rows, d), dtype=np.int8)

@@ -14,6 +14,15 @@ Tolerances (fixed by the rotated-quantisation contract this project builds to):
     row's measured rotation error;
   * GEMM: int32 accumulators bit-identical given identical codes; fp16 output
     within 1e-2 relative (floor 2^-14 for fp16 subnormals).
+The INT8 activation variant (W4A8) is held to the same rules with its own
+oracle functions (scale fp16_rne(a/127), codes in [-128, 127]), except that
+the rounding band grows with the code: the kernel rounds u * fp32(c/s) (u the
+unnormalised butterfly sum, c = fp32(1/sqrt(n))) where the mirror rounds
+fp32(u c) / s; each side has one fp32 rounding, so the two pre-round values
+differ by at most 2^-23 |v|.  For |v| <= 7.5 that is below 1e-6 (the INT4
+band covers it); for |v| up to 127.5 it reaches 1.5e-5, so INT8 codes may
+differ by one step where the pre-round value lies within 1e-6 + 2^-22 |v|
+of a half-integer.
 """
 
 from __future__ import annotations
@@ -23,6 +32,7 @@ import numpy as np
 from oracle import rq_oracle as O
 
 BAND = 1e-6
+BAND8_REL = 2.0 ** -22
 ROT_TOL = 1e-5
 Y_TOL = 1e-2
 
@@ -31,15 +41,16 @@ def dist_to_half_integer(v: np.ndarray) -> np.ndarray:
     return np.abs(np.abs(v - np.floor(v)) - 0.5)
 
 
-def check_codes(q_gpu: np.ndarray, ref: dict, what: str) -> int:
-    """GPU codes against an oracle result dict; returns the in-band mismatch count."""
+def check_codes(q_gpu: np.ndarray, ref: dict, what: str, band_rel: float = 0.0) -> int:
+    """GPU codes against an oracle result dict; returns the in-band mismatch
+    count.  The band is BAND + band_rel * |v| around each half-integer."""
     q_ref = ref["q"]
     bad = q_gpu != q_ref
     n_bad = int(bad.sum())
     if n_bad:
         v = ref["v"][bad]
         step = np.abs(q_gpu[bad].astype(np.int16) - q_ref[bad].astype(np.int16))
-        near = dist_to_half_integer(v) <= BAND
+        near = dist_to_half_integer(v) <= BAND + band_rel * np.abs(v)
         assert np.all(step == 1), f"{what}: code differs by more than one step"
         assert np.all(near), (f"{what}: {int((~near).sum())} code mismatches outside the 1e-6 band; "
                               f"worst distance {dist_to_half_integer(v).min():.3e}")
@@ -47,11 +58,14 @@ def check_codes(q_gpu: np.ndarray, ref: dict, what: str) -> int:
 
 
 def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant",
-                          rows=None, report=None):
-    """Full check of one rq_fwht_quant / rq_fold_weights result.
+                          rows=None, report=None, bits=4):
+    """Full check of one rq_fwht_quant / rq_fold_weights result (bits=4) or
+    rq_fwht_quant8 result (bits=8, codes int8 [m, n]).
 
     ``rows`` optionally selects the rows (of x and of the outputs) to check.
     """
+    quant = O.fwht_quant if bits == 4 else O.fwht_quant8
+    unpack = O.unpack_int4 if bits == 4 else (lambda c: np.asarray(c).astype(np.int8))
     x = np.asarray(x)
     if rows is not None:
         x = x[rows]
@@ -59,7 +73,7 @@ def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant"
         scales = scales[rows]
         if x_rot is not None:
             x_rot = x_rot[rows]
-    mirror = O.fwht_quant(x, signs, "f32")
+    mirror = quant(x, signs, "f32")
     if x_rot is not None:
         diff = x_rot.view(np.uint32) != mirror["x_rot"].view(np.uint32)
         # +0 and -0 are the same value
@@ -71,19 +85,20 @@ def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant"
         assert np.all(err <= ROT_TOL * ref_max + 1e-300), f"{what}: rotation error above 1e-5 relative"
     assert np.array_equal(scales.view(np.uint16), mirror["scales"].view(np.uint16)), \
         f"{what}: scales differ from the mirror"
-    q_gpu = O.unpack_int4(codes)
-    n_band = check_codes(q_gpu, mirror, what)
+    q_gpu = unpack(codes)
+    band_rel = 0.0 if bits == 4 else BAND8_REL
+    n_band = check_codes(q_gpu, mirror, what, band_rel)
     # against the fp64 oracle: report, and require each difference to be explained
-    truth = O.fwht_quant(x, signs, "f64")
+    truth = quant(x, signs, "f64")
     same_scale = scales.view(np.uint16) == truth["scales"].view(np.uint16)
     d = (q_gpu != truth["q"]) & same_scale[..., None]
     n_truth = int(d.sum())
     if n_truth:
         rot_err = np.abs(mirror["x_rot"].astype(np.float64) - truth["x_rot"]).max(axis=-1, keepdims=True)
         s = truth["scales"].astype(np.float64)[..., None]
-        allow = rot_err / s + BAND
         v = truth["v"]
-        assert np.all(dist_to_half_integer(v[d]) <= np.broadcast_to(allow, v.shape)[d]), \
+        allow = rot_err / s + BAND + band_rel * np.abs(v)
+        assert np.all(dist_to_half_integer(v[d]) <= allow[d]), \
             f"{what}: code mismatch vs fp64 not explained by the rotation error"
     if report is not None:
         report.append({"what": what, "elements": int(q_gpu.size), "band_mismatch_vs_mirror": n_band,
@@ -93,11 +108,12 @@ def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant"
 
 
 def check_gemm(a_codes, a_scales, w_codes, w_scales, y, acc=None, what="gemm",
-               rows=None, cols=None):
-    """Oracle GEMM on (a subset of) the same codes; acc exact, y within 1e-2."""
+               rows=None, cols=None, a8=False):
+    """Oracle GEMM on (a subset of) the same codes; acc exact, y within 1e-2.
+    a8: the activation codes are INT8 bytes (W4A8)."""
     ra = slice(None) if rows is None else rows
     cb = slice(None) if cols is None else cols
-    y_ref, acc_ref = O.w4a4_gemm(a_codes[ra], a_scales[ra], w_codes[cb], w_scales[cb])
+    y_ref, acc_ref = (O.w4a8_gemm if a8 else O.w4a4_gemm)(a_codes[ra], a_scales[ra], w_codes[cb], w_scales[cb])
     y_g = y[ra][:, cb]
     if acc is not None:
         acc_g = acc[ra][:, cb]

@@ -109,6 +109,65 @@ def test_kv_argument_errors(lib):
     assert f(*args[:4], MIS, *args[5:]) == binding.RQ_ERR_ALIGN
 
 
+def test_fwht_quant8_argument_errors(lib):
+    f = lib.rq_fwht_quant8
+
+    def call(x=A16, m=4, n=4096, signs=None, codes=A16b, scales=A16b, rot=None):
+        return f(x, m, n, signs, codes, scales, rot, None)
+
+    assert call(m=0) == binding.RQ_OK
+    assert call(m=0, x=None) == binding.RQ_OK
+    assert call(x=None) == binding.RQ_ERR_NULL
+    assert call(codes=None) == binding.RQ_ERR_NULL
+    assert call(scales=None) == binding.RQ_ERR_NULL
+    assert call(n=256) == binding.RQ_ERR_SHAPE      # below the smallest length
+    assert call(n=14336) == binding.RQ_ERR_SHAPE    # 28 x 512 has no INT8 kernel
+    assert call(n=16384) == binding.RQ_ERR_SHAPE
+    assert call(n=3000) == binding.RQ_ERR_SHAPE
+    assert call(m=-1) == binding.RQ_ERR_SHAPE
+    assert call(x=MIS) == binding.RQ_ERR_ALIGN
+    assert call(codes=MIS) == binding.RQ_ERR_ALIGN
+    assert call(signs=MIS) == binding.RQ_ERR_ALIGN
+    assert call(rot=MIS) == binding.RQ_ERR_ALIGN
+
+
+def test_w4a8_gemm_argument_errors(lib):
+    def call(a=A16, sa=A16b, m=4, w=A16, sw=A16b, k=64, d=4096, y=A16b, acc=None):
+        return lib.rq_w4a8_gemm(a, sa, m, w, sw, k, d, y, acc, None)
+
+    assert call(m=0) == binding.RQ_OK
+    assert call(a=None) == binding.RQ_ERR_NULL
+    assert call(sa=None) == binding.RQ_ERR_NULL
+    assert call(y=None) == binding.RQ_ERR_NULL
+    assert call(d=96) == binding.RQ_ERR_SHAPE
+    assert call(d=32768) == binding.RQ_ERR_SHAPE
+    assert call(k=0) == binding.RQ_ERR_SHAPE
+    assert call(m=-1) == binding.RQ_ERR_SHAPE
+    assert call(m=128 * 65536) == binding.RQ_ERR_SHAPE
+    assert call(a=MIS) == binding.RQ_ERR_ALIGN
+    assert call(w=MIS) == binding.RQ_ERR_ALIGN
+
+
+def test_linear_decode_argument_errors(lib):
+    need = lib.rq_linear_decode_workspace_size(4, 4096)
+    assert need == 4 * 2048 + 64
+
+    def call(x=A16, m=4, d=4096, signs=None, w=A16, sw=A16b, k=64, y=A16b, ws=A16b,
+             nbytes=need):
+        return lib.rq_linear_decode(x, m, d, signs, w, sw, k, y, ws, nbytes, None)
+
+    assert call(m=0) == binding.RQ_OK
+    assert call(m=17) == binding.RQ_ERR_SHAPE
+    assert call(d=256) == binding.RQ_ERR_SHAPE
+    assert call(d=14336) == binding.RQ_ERR_SHAPE
+    assert call(k=0) == binding.RQ_ERR_SHAPE
+    assert call(nbytes=need - 1) == binding.RQ_ERR_SHAPE
+    assert call(x=None) == binding.RQ_ERR_NULL
+    assert call(ws=None) == binding.RQ_ERR_NULL
+    assert call(x=MIS) == binding.RQ_ERR_ALIGN
+    assert call(ws=MIS) == binding.RQ_ERR_ALIGN
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
