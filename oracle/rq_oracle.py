@@ -64,10 +64,18 @@ __all__ = [
     "w4a8_gemm",
     "kv_rotate_quant",
     "dequantize",
+    "quantize_rows_asym",
+    "fwht_quant_asym",
+    "unpack_uint4",
+    "w4a4_gemm_asym",
+    "quantize_groups",
+    "w4a4_gemm_grouped",
 ]
 
 QMIN, QMAX = -8, 7
 QMIN8, QMAX8 = -128, 127
+UMAX4 = 15          # asymmetric INT4: unsigned codes 0 .. 2^4 - 1
+GROUP = 128         # per-group weight scales: elements per group
 
 
 def _check_pow2(n: int) -> None:
@@ -445,3 +453,139 @@ def kv_rotate_quant(k: np.ndarray, v: np.ndarray, signs: np.ndarray | None = Non
         out[name + "_v"] = r["v"]
         out[name + "_rot"] = r["x_rot"]
     return out
+
+
+# --------------------------------------------------------------- asymmetric
+def quantize_rows_asym(xt: np.ndarray):
+    """Asymmetric per-row INT4 quantisation (unsigned codes, integer zero point).
+
+    [RQ] "The Activation Outlier Bottleneck in Low-Bit Serving": the step of a
+    uniform b-bit grid spans the whole range, Delta = (max - min) / (2^b - 1).
+    Reading of the zero point (the page gives only the step): the affine grid
+    x ~ Delta * (q - z) with unsigned codes q in [0, 15] and an integer zero
+    point z; the range is widened to contain 0 (lo = min(min x, 0),
+    hi = max(max x, 0)) so that z = rne(-lo / Delta) lies in [0, 15] and 0 is
+    exactly representable.
+
+      r      = hi - lo, in the precision of the given values (float32 values
+               give a float32 difference, as a float32 kernel computes it)
+      Delta  = fp16_rne(r / 15), rounded once from the exact quotient
+      z      = clamp(rne(-lo / Delta), 0, 15)
+      q      = clamp(rne(x / Delta) + z, 0, 15)
+
+    Delta == 0 (a zero row) gives z = 0 and all-zero codes; an infinite Delta
+    gives z = 0 and all-zero codes.  Returns (q uint8, scales float16,
+    zeros uint8, v = x / Delta float64, w = -lo / Delta float64).
+    """
+    xt = np.asarray(xt)
+    hi = np.maximum(np.max(xt, axis=-1), 0)
+    lo = np.minimum(np.min(xt, axis=-1), 0)
+    r = (hi - lo).astype(np.float64)          # float32 subtraction for float32 rows
+    scales = fp16_rne(r / UMAX4)
+    s = scales.astype(np.float64)
+    ok = (s > 0) & np.isfinite(s)
+    safe = np.where(ok, s, 1.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        w = np.where(ok, -lo.astype(np.float64) / safe, 0.0)
+        v = np.where(ok[..., None], xt.astype(np.float64) / safe[..., None], 0.0)
+    z = np.clip(np.rint(w), 0, UMAX4)
+    q = np.clip(np.rint(v) + z[..., None], 0, UMAX4)
+    q = np.where(ok[..., None], q, 0)
+    return q.astype(np.uint8), scales, z.astype(np.uint8), v, w
+
+
+def unpack_uint4(codes: np.ndarray) -> np.ndarray:
+    """Unsigned nibbles of packed codes (code 2i in the low nibble of byte i)."""
+    c = np.asarray(codes).astype(np.uint8)
+    out = np.empty(c.shape[:-1] + (2 * c.shape[-1],), np.uint8)
+    out[..., 0::2] = c & 0xF
+    out[..., 1::2] = c >> 4
+    return out
+
+
+def _pack_uint4(q: np.ndarray) -> np.ndarray:
+    q = np.asarray(q).astype(np.uint8)
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
+def fwht_quant_asym(x: np.ndarray, signs: np.ndarray | None, precision: str = "f64") -> dict:
+    """Online rotation followed by asymmetric per-token INT4.
+
+    The rotation is :func:`rotate`; the quantiser is
+    :func:`quantize_rows_asym` ([RQ] "The Activation Outlier Bottleneck in
+    Low-Bit Serving").  Returns codes uint8 [m, n/2] (unsigned nibbles,
+    packed like the symmetric codes), scales float16 [m], zeros uint8 [m],
+    x_rot, q (unsigned codes), v and w (pre-round values of the codes and of
+    the zero point).
+    """
+    xt = rotate(x, signs, precision)
+    q, scales, z, v, w = quantize_rows_asym(xt)
+    return {"codes": _pack_uint4(q), "scales": scales, "zeros": z, "x_rot": xt, "q": q, "v": v,
+            "w": w}
+
+
+def w4a4_gemm_asym(a_codes: np.ndarray, a_scales: np.ndarray, a_zeros: np.ndarray,
+                   w_codes: np.ndarray, w_scales: np.ndarray):
+    """W4A4 linear with asymmetric activations and symmetric weights.
+
+    Dequantised activation x^ = sa * (qa - za); weight w^ = sw * qw.  The
+    integer accumulator is acc[m][j] = sum_i (qa[m][i] - za[m]) * qw[j][i]
+    (exact), y = fp16_rne(acc * sa[m] * sw[j]) with the product in float64.
+    Returns (y float16 [m, k], acc int64 [m, k]).
+    """
+    qa = unpack_uint4(a_codes).astype(np.int64) - np.asarray(a_zeros).astype(np.int64)[:, None]
+    qw = unpack_int4(w_codes)
+    if qa.shape[-1] != qw.shape[-1]:
+        raise ValueError("inner dimensions differ")
+    d = qa.shape[-1]
+    if 128 * d >= 2 ** 53:
+        raise ValueError("d too large for an exact float64 accumulation")
+    acc = (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+    sa = np.asarray(a_scales).astype(np.float64)[:, None]
+    sw = np.asarray(w_scales).astype(np.float64)[None, :]
+    return fp16_rne(acc.astype(np.float64) * sa * sw), acc
+
+
+# ------------------------------------------------------- per-group weights
+def quantize_groups(xt: np.ndarray, group: int = GROUP):
+    """Symmetric INT4 with one scale per group of `group` consecutive
+    elements of each row ([SpinQuant] "End-to-end flow": INT4 weights with
+    per-channel or per-group scales).
+
+    Each group is quantised by the symmetric rule of :func:`quantize_rows`
+    on its own: scale = fp16_rne(max |x~| / 7) over the group, codes
+    clamp(rne(x~ / scale), -8, 7).  Returns (q int8 [..., n], scales float16
+    [..., n / group], v float64 [..., n]).
+    """
+    xt = np.asarray(xt)
+    n = xt.shape[-1]
+    if n % group:
+        raise ValueError("the group size must divide the row length")
+    g = xt.reshape(xt.shape[:-1] + (n // group, group))
+    q, scales, v = quantize_rows(g)
+    return q.reshape(xt.shape), scales, v.reshape(xt.shape)
+
+
+def w4a4_gemm_grouped(a_codes: np.ndarray, a_scales: np.ndarray, w_codes: np.ndarray,
+                      w_group_scales: np.ndarray, group: int = GROUP):
+    """W4A4 linear with per-token activation scales and per-group weight
+    scales: y[m][j] = fp16_rne(sa[m] * sum_g sw[j][g] * acc[m][j][g]) with
+    acc[m][j][g] = sum_{i in group g} qa[m][i] * qw[j][i] (exact integers)
+    and the outer sum in float64.  Returns (y float16 [m, k], acc int64
+    [m, k, d / group]).
+    """
+    qa = unpack_int4(a_codes)
+    qw = unpack_int4(w_codes)
+    m, d = qa.shape
+    k = qw.shape[0]
+    if qw.shape[-1] != d or d % group:
+        raise ValueError("inner dimensions differ or are not a multiple of the group")
+    ng = d // group
+    acc = np.empty((m, k, ng), np.int64)
+    for g in range(ng):
+        sl = slice(g * group, (g + 1) * group)
+        acc[:, :, g] = _int_matmul_nt(qa[:, sl], qw[:, sl])
+    sw = np.asarray(w_group_scales).astype(np.float64).reshape(k, ng)
+    sa = np.asarray(a_scales).astype(np.float64)
+    y = fp16_rne(sa[:, None] * np.einsum("mkg,kg->mk", acc.astype(np.float64), sw))
+    return y, acc

@@ -556,3 +556,205 @@ def test_w4a8_tracks_float_linear_better_than_w4a4():
     e8 = np.abs(y8.astype(np.float64) - ref).mean()
     e4 = np.abs(y4.astype(np.float64) - ref).mean()
     assert e8 < e4
+
+
+# ------------------------------------------------- asymmetric INT4 (f4)
+# The pages give only the step, Delta = (max - min) / (2^b - 1) ([RQ] "The
+# Activation Outlier Bottleneck in Low-Bit Serving"); the zero point is the
+# usual integer one, with the range widened to contain 0.
+
+def _fp16_nearest(fr):
+    """Nearest binary16 value to the rational fr >= 0 (ties to even), by
+    search over neighbouring fp16 values: independent of numpy's cast."""
+    from fractions import Fraction
+    x = float(fr)
+    cand = np.float16(x)
+    best = None
+    for c in {cand, np.nextafter(cand, np.float16(np.inf)), np.nextafter(cand, np.float16(0))}:
+        if not np.isfinite(c):
+            continue
+        dist = abs(Fraction(float(c)) - fr)
+        key = (dist, int(np.array(c).view(np.uint16)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def _asym_brute(row):
+    """Asymmetric quantiser with exact rational arithmetic (Python Fraction,
+    round() on a Fraction is round-half-even)."""
+    from fractions import Fraction
+    xs = [Fraction(float(v)) for v in row]
+    hi = max(max(xs), Fraction(0))
+    lo = min(min(xs), Fraction(0))
+    scale = _fp16_nearest((hi - lo) / 15)
+    s = Fraction(float(scale))
+    if s == 0:
+        return [0] * len(xs), scale, 0
+    z = min(max(round(-lo / s), 0), 15)
+    q = [min(max(round(x / s) + z, 0), 15) for x in xs]
+    return q, scale, z
+
+
+def test_asym_worked_example():
+    # [-1, 0, 2, 3]: r = 4, 4/15 -> fp16 1092 * 2^-12 = 0.2666015625;
+    # z = rne(1 / 0.26660...) = rne(3.7509) = 4; 2 / Delta = 7.5018 -> 8 -> 12;
+    # 3 / Delta = 11.2527 -> 11 -> 15; -1 / Delta = -3.7509 -> -4 -> 0.
+    q, s, z, _, _ = O.quantize_rows_asym(np.array([[-1.0, 0.0, 2.0, 3.0]]))
+    assert float(s[0]) == 1092 * 2.0 ** -12
+    assert int(z[0]) == 4
+    assert q[0].tolist() == [0, 4, 12, 15]
+
+
+def test_asym_brute_force_rational():
+    rng = np.random.default_rng(41)
+    for trial in range(60):
+        n = int(rng.integers(2, 40))
+        row = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        if trial % 5 == 0:
+            row = np.abs(row)            # one-sided rows: lo = 0, z = 0
+        if trial % 7 == 0:
+            row = -np.abs(row)           # hi = 0, z = 15
+        q, s, z, _, _ = O.quantize_rows_asym(row.astype(np.float64)[None, :])
+        qb, sb, zb = _asym_brute(row)
+        assert np.float16(s[0]).view(np.uint16) == np.float16(sb).view(np.uint16), trial
+        assert int(z[0]) == zb and q[0].tolist() == qb, trial
+
+
+def test_asym_reduces_to_symmetric_on_a_matched_range():
+    # With min = -8t and max = 7t (t a power of two) the asymmetric step is
+    # 15t / 15 = t, the same as the symmetric scale 7t / 7, the zero point
+    # is 8, and the codes are the symmetric codes shifted by 8.
+    rng = np.random.default_rng(42)
+    t = 2.0 ** -5
+    x = rng.uniform(-7 * t, 7 * t, (6, 64))  # interior values within the symmetric range
+    x[:, 0], x[:, 1] = -8 * t, 7 * t
+    qa, sa, za, _, _ = O.quantize_rows_asym(x)
+    qs, ss, _ = O.quantize_rows(np.where(x == -8 * t, -7 * t, x))  # symmetric max must be 7t
+    assert (sa.astype(np.float64) == t).all() and (ss.astype(np.float64) == t).all()
+    assert (za == 8).all()
+    inner = np.ones_like(x, bool)
+    inner[:, 0] = False
+    assert np.array_equal(qa.astype(np.int16)[inner] - 8, qs.astype(np.int16)[inner])
+    assert (qa[:, 0] == 0).all()
+
+
+def test_asym_invariants_zero_and_constant_rows():
+    x = np.zeros((4, 16))
+    x[1] = 3.0
+    x[2] = -3.0
+    x[3, 5] = 1.0
+    q, s, z, _, _ = O.quantize_rows_asym(x)
+    assert float(s[0]) == 0 and z[0] == 0 and not q[0].any()
+    assert z[1] == 0 and (q[1] == 15).all()
+    assert z[2] == 15 and (q[2] == 0).all()
+    assert z[3] == 0 and q[3, 5] == 15 and (np.delete(q[3], 5) == 0).all()
+    rng = np.random.default_rng(43)
+    xr = rng.standard_normal((50, 256)) * rng.uniform(0.01, 100, (50, 1))
+    q, s, z, _, _ = O.quantize_rows_asym(xr)
+    s64 = s.astype(np.float64)[:, None]
+    deq = s64 * (q.astype(np.float64) - z.astype(np.float64)[:, None])
+    assert np.all(np.abs(deq - xr) <= 0.51 * s64)
+    assert np.all(q[np.arange(50), np.argmin(xr, axis=1)] == 0)
+    assert q.max() <= 15
+
+
+def test_asym_fwht_quant_composition_and_packing():
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    signs = datagen.rademacher(rng, 256)
+    r = O.fwht_quant_asym(x, signs, "f32")
+    q, s, z, _, _ = O.quantize_rows_asym(O.rotate(x, signs, "f32"))
+    assert np.array_equal(r["q"], q) and np.array_equal(r["zeros"], z)
+    assert np.array_equal(O.unpack_uint4(r["codes"]), q)
+    # packing: code 2i in the low nibble of byte i
+    assert O._pack_uint4(np.array([[1, 2, 3, 15]])).tolist() == [[0x21, 0xF3]]
+
+
+def test_asym_gemm_brute_force():
+    rng = np.random.default_rng(45)
+    m, k, d = 3, 4, 64
+    qa = rng.integers(0, 16, (m, d)).astype(np.uint8)
+    za = rng.integers(0, 16, m).astype(np.uint8)
+    qw = rng.integers(-8, 8, (k, d))
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k)
+    y, acc = O.w4a4_gemm_asym(O._pack_uint4(qa), sa, za, O.pack_int4(qw), sw)
+    for i in range(m):
+        for j in range(k):
+            want = sum((int(qa[i, t]) - int(za[i])) * int(qw[j, t]) for t in range(d))
+            assert acc[i, j] == want
+    # the identity the GPU epilogue uses: acc = sum qa qw - za * sum qw
+    assert np.array_equal(acc, qa.astype(np.int64) @ qw.T - za[:, None].astype(np.int64) * qw.sum(1)[None, :])
+    # closed form: qa = 15, za = 0, qw = 7 -> 105 d
+    y2, acc2 = O.w4a4_gemm_asym(O._pack_uint4(np.full((1, d), 15)), np.ones(1, np.float16),
+                                np.zeros(1, np.uint8), O.pack_int4(np.full((1, d), 7)),
+                                np.ones(1, np.float16))
+    assert acc2[0, 0] == 105 * d and float(y2[0, 0]) == 105 * d
+
+
+def test_asym_beats_symmetric_on_one_sided_rows():
+    # a one-sided distribution uses all 16 asymmetric levels but only 8
+    # symmetric ones, so the asymmetric error is smaller
+    rng = np.random.default_rng(46)
+    x = np.abs(rng.standard_normal((64, 512)))
+    qa, sa, za, _, _ = O.quantize_rows_asym(x)
+    qs, ss, _ = O.quantize_rows(x)
+    ea = np.abs(sa.astype(np.float64)[:, None] * (qa.astype(np.float64) - za[:, None]) - x).mean()
+    es = np.abs(ss.astype(np.float64)[:, None] * qs - x).mean()
+    assert ea < 0.6 * es
+
+
+# ---------------------------------------------- per-group weight scales (f4)
+
+def test_groups_worked_example_and_rowwise_equivalence():
+    # group 2 on [1, -2, 0.5, 0.25]: scales fp16(2/7), fp16(0.5/7)
+    q, s, _ = O.quantize_groups(np.array([[1.0, -2.0, 0.5, 0.25]]), group=2)
+    from fractions import Fraction
+    s0, s1 = _fp16_nearest(Fraction(2, 7)), _fp16_nearest(Fraction(1, 14))
+    assert s[0].tolist() == [float(s0), float(s1)]
+    want = [round(Fraction(1.0) / Fraction(float(s0))), round(Fraction(-2.0) / Fraction(float(s0))),
+            round(Fraction(0.5) / Fraction(float(s1))), round(Fraction(0.25) / Fraction(float(s1)))]
+    assert q[0].tolist() == [max(-8, min(7, v)) for v in want]
+    rng = np.random.default_rng(47)
+    x = rng.standard_normal((5, 512))
+    qg, sg, _ = O.quantize_groups(x, 128)
+    for g in range(4):
+        qr, sr, _ = O.quantize_rows(x[:, 128 * g:128 * (g + 1)])
+        assert np.array_equal(qg[:, 128 * g:128 * (g + 1)], qr)
+        assert np.array_equal(sg[:, g].view(np.uint16), sr.view(np.uint16))
+
+
+def test_grouped_gemm_brute_force_and_per_channel_case():
+    from fractions import Fraction
+    rng = np.random.default_rng(48)
+    m, k, d, g = 2, 3, 256, 128
+    qa = rng.integers(-8, 8, (m, d))
+    qw = rng.integers(-8, 8, (k, d))
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k * 2).reshape(k, 2)
+    y, acc = O.w4a4_gemm_grouped(O.pack_int4(qa), sa, O.pack_int4(qw), sw, g)
+    for i in range(m):
+        for j in range(k):
+            tot = Fraction(0)
+            for gi in range(2):
+                a = sum(int(qa[i, t]) * int(qw[j, t]) for t in range(gi * g, (gi + 1) * g))
+                assert acc[i, j, gi] == a
+                tot += Fraction(float(sw[j, gi])) * a
+            ref = float(Fraction(float(sa[i])) * tot)
+            assert abs(float(y[i, j]) - ref) <= 2.0 ** -11 * abs(ref) + 2.0 ** -24
+    # equal group scales reduce to the per-channel GEMM
+    sw1 = datagen.random_scales(rng, k)
+    yg, _ = O.w4a4_gemm_grouped(O.pack_int4(qa), sa, O.pack_int4(qw), np.repeat(sw1[:, None], 2, 1), g)
+    yc, _ = O.w4a4_gemm(O.pack_int4(qa), sa, O.pack_int4(qw), sw1)
+    assert np.array_equal(yg.view(np.uint16), yc.view(np.uint16))
+
+
+def test_groups_cut_weight_error_when_group_ranges_differ():
+    rng = np.random.default_rng(49)
+    w = rng.standard_normal((32, 1024)) * np.repeat(10.0 ** rng.uniform(-2, 0, (32, 8)), 128, axis=1)
+    qg, sg, _ = O.quantize_groups(w, 128)
+    qc, sc, _ = O.quantize_rows(w)
+    eg = np.abs(np.repeat(sg.astype(np.float64), 128, axis=1) * qg - w).mean()
+    ec = np.abs(sc.astype(np.float64)[:, None] * qc - w).mean()
+    assert eg < 0.5 * ec
