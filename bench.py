@@ -385,6 +385,54 @@ def main():
             log(f"[bench] w4a8 prefill gemm: {sec['gemm_w4a8_prefill_2048x8192x28672']}")
             del wcs, wc, y, ac8
 
+        if want("asym"):
+            # asymmetric activations: rotation + unsigned INT4 with zero
+            # points, and the GEMM with the zero-point epilogue
+            wa = datagen.fwht_workload(0)
+            ma, na = wa["m"], wa["d"]
+            xa0 = torch.from_numpy(wa["x"]).to(dev)
+            sga = torch.from_numpy(wa["signs"]).to(dev)
+            pera = ma * na * 2 + ma * na // 2 + 3 * ma + na
+            setsa = max(2, -(-2 * MALL_BYTES // pera) + 1)
+            xas_ = [xa0] + [xa0.clone() for _ in range(setsa - 1)]
+            oa = [(torch.empty((ma, na // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((ma,), dtype=torch.float16, device=dev),
+                   torch.empty((ma,), dtype=torch.uint8, device=dev)) for _ in range(setsa)]
+
+            def fqa(i):
+                st = lib.rq_fwht_quant_asym(_ptr(xas_[i]), ma, na, _ptr(sga), _ptr(oa[i][0]),
+                                            _ptr(oa[i][1]), _ptr(oa[i][2]), None, _stream())
+                assert st == 0
+
+            msa = time_launches(torch, fqa, setsa, steps2, warm2)
+            sec["fwht_quant_asym_4096x4096"] = {"us": round(msa * 1e3, 3),
+                                                "GB/s": round(pera / (msa * 1e-3) / 1e9, 1),
+                                                "hbm_frac": round(pera / (msa * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] fwht_quant_asym 4096x4096: {sec['fwht_quant_asym_4096x4096']}")
+            del xas_, oa, xa0
+            dec = datagen.decode_linear(0)
+            s = torch.from_numpy(dec["signs"]).to(dev)
+            acq, saq, zaq, _ = rq.fwht_quant_asym(torch.from_numpy(dec["x"]).to(dev), s)
+            for k, wt in dec["wts"].items():
+                wc, ws, _ = rq.fold_weights(torch.from_numpy(wt).to(dev), s)
+                wsum = rq.weight_code_sums(wc)
+                nsets = max(2, -(-2 * MALL_BYTES // wc.numel()) + 1)
+                wcs = [wc.clone() for _ in range(nsets)]
+                for mm in (1, 4, 16):
+                    y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+                    a_m, s_m, z_m = acq[:mm].contiguous(), saq[:mm].contiguous(), zaq[:mm].contiguous()
+
+                    def ga(i, a_m=a_m, s_m=s_m, z_m=z_m, y=y):
+                        rq.w4a4_gemm_asym(a_m, s_m, z_m, wcs[i], ws, wsum, out=y)
+
+                    msg = time_launches(torch, ga, nsets, steps2, warm2)
+                    bb = gemm_bytes(mm, k, 4096) + mm + 4 * k
+                    key = f"gemm_asym_decode_m{mm}_k{k}"
+                    sec[key] = {"us": round(msg * 1e3, 3), "GB/s": round(bb / (msg * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(bb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    log(f"[bench] {key}: {sec[key]}")
+                del wcs, wc
+
         if want("kv"):
             kv = datagen.kv_cache(0)
             kt = torch.from_numpy(kv["k"]).to(dev)

@@ -262,6 +262,63 @@ int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
                  const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                  uint16_t* y, int32_t* acc, void* stream);
 
+/*
+ * rq_fwht_quant_asym -- online rotation fused with asymmetric per-token INT4.
+ *
+ * [RQ] "The Activation Outlier Bottleneck in Low-Bit Serving" (a uniform
+ * b-bit grid whose step spans the whole range, Delta = (max - min) /
+ * (2^b - 1)).  The rotation is the one of rq_fwht_quant.  Per row, with lo
+ * and hi the row's min and max widened to contain 0 (fp32 rotated values):
+ * scale = fp16(fp32(hi - lo) / 15) rounded once, zero = rne(-lo / scale) in
+ * [0, 15], code = clamp(rne(x~ / scale) + zero, 0, 15).  A zero or infinite
+ * scale gives zero = 0 and all-zero codes.  Dequantisation:
+ * x~ ~ scale * (code - zero).
+ *
+ *   x       [m][n] fp16, 16-byte aligned; n a power of two in [512, RQ_MAX_N].
+ *   signs   [n] int8 +-1 or NULL.
+ *   codes   [m][n/2] uint8 output: unsigned 4-bit codes, code 2i in the low
+ *           nibble of byte i; 16-byte aligned.
+ *   scales  [m] fp16 output; zeros [m] uint8 output (0..15).
+ *   x_rot   optional [m][n] float32 rotated rows, or NULL.
+ */
+int rq_fwht_quant_asym(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs,
+                       uint8_t* codes, uint16_t* scales, uint8_t* zeros, float* x_rot,
+                       void* stream);
+
+/*
+ * rq_weight_code_sums -- sums[j] = sum_i qw[j][i] over the signed INT4 codes
+ * of each folded weight row (an offline companion of rq_fold_weights that the
+ * asymmetric GEMM needs: sum_i (qa_i - z) qw_i = sum_i qa_i qw_i - z sums[j]).
+ *
+ *   w_codes  [k][d/2] uint8 (rq_fold_weights output), 16-byte aligned.
+ *   k        rows, >= 0;  d  a multiple of 64 in [64, 16384].
+ *   sums     [k] int32 output.
+ */
+int rq_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
+                        void* stream);
+
+/*
+ * rq_w4a4_gemm_asym -- W4A4 linear with asymmetric activations:
+ * y = fp16(acc * sa[m] * sw[j]), acc[m][j] = sum_i (qa[m][i] - za[m]) qw[j][i].
+ *
+ * [RQ] "The Activation Outlier Bottleneck in Low-Bit Serving" (asymmetric
+ * step) and "Hardware Execution and Serving Economics", part 1 (integer GEMM).
+ * The unsigned activation codes are widened to int8 lanes as they are, the
+ * weights to 16 * q; the int32 MFMA sum is 16 * sum qa qw, and the epilogue
+ * subtracts za * w_sums[j] before the fp16 scaling of rq_w4a4_gemm.
+ *
+ *   a_codes  [m][d/2] unsigned codes (rq_fwht_quant_asym), 16-byte aligned;
+ *            a_scales [m] fp16; a_zeros [m] uint8.
+ *   w_codes  [k][d/2] signed codes (rq_fold_weights), 16-byte aligned;
+ *            w_scales [k] fp16; w_sums [k] int32 (rq_weight_code_sums).
+ *   m >= 0, k >= 1 when m > 0, d a multiple of 64 in [64, 16384].
+ *   y        [m][k] fp16 output; acc optional [m][k] int32 accumulators.
+ */
+int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
+                      int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
+                      const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
+                      void* stream);
+
 /* Text for an rq_status value (static storage, never NULL). */
 const char* rq_status_string(int status);
 

@@ -12,14 +12,18 @@ from .binding import (  # noqa: F401
     fold_weights,
     fwht_quant,
     fwht_quant8,
+    fwht_quant_asym,
     kv_rotate_quant,
     linear_decode,
     linear_decode_workspace,
     load_library,
     status_string,
     version,
+    weight_code_sums,
     w4a4_gemm,
+    w4a4_gemm_asym,
     w4a4_linear,
+    w4a4_linear_asym,
     w4a8_gemm,
     w4a8_linear,
 )

@@ -29,6 +29,9 @@ EXPORTED = (
     "rq_linear_decode",
     "rq_fwht_quant8",
     "rq_w4a8_gemm",
+    "rq_fwht_quant_asym",
+    "rq_weight_code_sums",
+    "rq_w4a4_gemm_asym",
     "rq_status_string",
     "rq_version",
 )
@@ -71,6 +74,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_fwht_quant8.restype = i32
     lib.rq_w4a8_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, p, p]
     lib.rq_w4a8_gemm.restype = i32
+    lib.rq_fwht_quant_asym.argtypes = [p, i64, i64, p, p, p, p, p, p]
+    lib.rq_fwht_quant_asym.restype = i32
+    lib.rq_weight_code_sums.argtypes = [p, i64, i64, p, p]
+    lib.rq_weight_code_sums.restype = i32
+    lib.rq_w4a4_gemm_asym.argtypes = [p, p, p, i64, p, p, p, i64, i64, p, p, p]
+    lib.rq_w4a4_gemm_asym.restype = i32
     lib.rq_status_string.argtypes = [i32]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_version.argtypes = []
@@ -284,4 +293,67 @@ def w4a8_linear(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tens
     INT4 weights folded with the same signs.  Two launches."""
     codes, scales, _ = fwht_quant8(x, signs)
     y, _ = w4a8_gemm(codes, scales, w_codes, w_scales)
+    return y
+
+
+def fwht_quant_asym(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+    """rq_fwht_quant_asym: returns (codes uint8 [m, n/2] unsigned nibbles,
+    scales fp16 [m], zeros uint8 [m], x_rot fp32 or None)."""
+    _need_cuda("x", x)
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a float16 [rows, n] tensor")
+    rows, n = x.shape
+    s = _signs(signs, n, x.device)
+    codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows,), dtype=torch.float16, device=x.device)
+    zeros = torch.empty((rows,), dtype=torch.uint8, device=x.device)
+    rot = torch.empty((rows, n), dtype=torch.float32, device=x.device) if debug else None
+    st = load_library().rq_fwht_quant_asym(_ptr(x), rows, n, _ptr(s), _ptr(codes), _ptr(scales),
+                                           _ptr(zeros), _ptr(rot), _stream())
+    _check("rq_fwht_quant_asym", st)
+    return codes, scales, zeros, rot
+
+
+def weight_code_sums(w_codes: torch.Tensor) -> torch.Tensor:
+    """rq_weight_code_sums: int32 [k] sums of the signed INT4 codes per row."""
+    _need_cuda("w_codes", w_codes)
+    if w_codes.dtype != torch.uint8 or w_codes.dim() != 2:
+        raise ValueError("w_codes must be a uint8 [k, d/2] tensor")
+    k, half_d = w_codes.shape
+    sums = torch.empty((k,), dtype=torch.int32, device=w_codes.device)
+    st = load_library().rq_weight_code_sums(_ptr(w_codes), k, 2 * half_d, _ptr(sums), _stream())
+    _check("rq_weight_code_sums", st)
+    return sums
+
+
+def w4a4_gemm_asym(a_codes: torch.Tensor, a_scales: torch.Tensor, a_zeros: torch.Tensor,
+                   w_codes: torch.Tensor, w_scales: torch.Tensor, w_sums: torch.Tensor,
+                   debug: bool = False, out: torch.Tensor | None = None):
+    """rq_w4a4_gemm_asym: returns (y fp16 [m, k], acc int32 [m, k] or None)."""
+    for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("a_zeros", a_zeros),
+                    ("w_codes", w_codes), ("w_scales", w_scales), ("w_sums", w_sums)):
+        _need_cuda(name, t)
+    if a_codes.dtype != torch.uint8 or w_codes.dtype != torch.uint8 or a_zeros.dtype != torch.uint8:
+        raise ValueError("codes and zero points must be uint8")
+    if w_sums.dtype != torch.int32:
+        raise ValueError("w_sums must be int32")
+    m, half_d = a_codes.shape
+    k, half_d2 = w_codes.shape
+    if half_d != half_d2 or a_scales.numel() != m or a_zeros.numel() != m or \
+            w_scales.numel() != k or w_sums.numel() != k:
+        raise ValueError("shapes do not match")
+    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
+    acc = torch.empty((m, k), dtype=torch.int32, device=a_codes.device) if debug else None
+    st = load_library().rq_w4a4_gemm_asym(_ptr(a_codes), _ptr(a_scales), _ptr(a_zeros), m,
+                                          _ptr(w_codes), _ptr(w_scales), _ptr(w_sums), k,
+                                          2 * half_d, _ptr(y), _ptr(acc), _stream())
+    _check("rq_w4a4_gemm_asym", st)
+    return y, acc
+
+
+def w4a4_linear_asym(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tensor,
+                     w_scales: torch.Tensor, w_sums: torch.Tensor) -> torch.Tensor:
+    """Online rotation + asymmetric INT4 quantisation of x, then the GEMM."""
+    codes, scales, zeros, _ = fwht_quant_asym(x, signs)
+    y, _ = w4a4_gemm_asym(codes, scales, zeros, w_codes, w_scales, w_sums)
     return y

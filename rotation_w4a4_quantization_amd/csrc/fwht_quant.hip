@@ -89,6 +89,7 @@ struct FQOut {
   uint8_t* codes;
   uint16_t* scales;
   float* xrot;
+  uint8_t* zeros;  // asymmetric quantiser only: per-row zero points
 };
 
 template <typename T>
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(64) void fwht_quant_kernel(FQOut o0, FQOut o1, int6
 // stays within 128 VGPRs so that four wavefronts share each SIMD: while one
 // waits for its row, the others keep the VALU busy.  Sign bytes are re-read
 // per row (L1/L2 hits) rather than held in registers for the same reason.
-template <int N, bool HAS_SIGNS, int BITS = 4>
+template <int N, bool HAS_SIGNS, int BITS = 4, bool ASYM = false>
 __global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_kernel(FQOut o, int64_t rows,
                                                                  const int8_t* __restrict__ signs,
                                                                  float c32) {
@@ -347,9 +348,9 @@ __global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_ke
   for (;;) {
     uint4 raw[NI];
     load_row(raw, static_cast<const __half*>(o.x) + row * N, L);
-    row_rotate_quant<N, HAS_SIGNS, false, BITS>(raw, signs, L, rl, c32, cb,
-                                                o.codes + row * kCodeBytes, o.scales + row,
-                                                o.xrot != nullptr ? o.xrot + row * N : nullptr);
+    row_rotate_quant<N, HAS_SIGNS, false, BITS, ASYM>(
+        raw, signs, L, rl, c32, cb, o.codes + row * kCodeBytes, o.scales + row,
+        o.xrot != nullptr ? o.xrot + row * N : nullptr, ASYM ? o.zeros + row : nullptr);
     const int64_t next = row + stride;
     if (next >= rows) break;
     row = next;
@@ -706,7 +707,7 @@ hipError_t launch_quad(FQOut o0, FQOut o1, int pairs, int64_t rows, const int8_t
 template <int N>
 constexpr int row_waves_per_simd() { return N <= 4096 ? 4 : 2; }
 
-template <int N, bool HAS_SIGNS, int BITS = 4>
+template <int N, bool HAS_SIGNS, int BITS = 4, bool ASYM = false>
 hipError_t launch_row(FQOut o, int64_t rows, const int8_t* signs, hipStream_t stream) {
   const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
   const int64_t max_waves = (int64_t)cu_count() * 4 * row_waves_per_simd<N>();
@@ -714,7 +715,7 @@ hipError_t launch_row(FQOut o, int64_t rows, const int8_t* signs, hipStream_t st
   const int64_t per_wave = (rows + waves - 1) / waves;  // rows per wavefront, balanced
   waves = (rows + per_wave - 1) / per_wave;
   const int64_t blocks = (waves + kRowWaves - 1) / kRowWaves;
-  hipLaunchKernelGGL((fwht_row_kernel<N, HAS_SIGNS, BITS>), dim3((unsigned)blocks), dim3(kWave * kRowWaves),
+  hipLaunchKernelGGL((fwht_row_kernel<N, HAS_SIGNS, BITS, ASYM>), dim3((unsigned)blocks), dim3(kWave * kRowWaves),
                      0, stream, o, rows, signs, c32);
   return hipGetLastError();
 }
@@ -825,6 +826,27 @@ hipError_t launch_fwht_quant8(const uint16_t* x, int64_t rows, int n, const int8
   const FQOut o{x, reinterpret_cast<uint8_t*>(codes), scales, x_rot};
   return signs ? dispatch_row8<true>(o, rows, n, signs, stream)
                : dispatch_row8<false>(o, rows, n, signs, stream);
+}
+
+template <bool HAS_SIGNS>
+hipError_t dispatch_row_asym(FQOut o, int64_t rows, int n, const int8_t* signs,
+                             hipStream_t stream) {
+  switch (n) {
+    case 512: return launch_row<512, HAS_SIGNS, 4, true>(o, rows, signs, stream);
+    case 1024: return launch_row<1024, HAS_SIGNS, 4, true>(o, rows, signs, stream);
+    case 2048: return launch_row<2048, HAS_SIGNS, 4, true>(o, rows, signs, stream);
+    case 4096: return launch_row<4096, HAS_SIGNS, 4, true>(o, rows, signs, stream);
+    case 8192: return launch_row<8192, HAS_SIGNS, 4, true>(o, rows, signs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fwht_quant_asym(const uint16_t* x, int64_t rows, int n, const int8_t* signs,
+                                  uint8_t* codes, uint16_t* scales, uint8_t* zeros, float* x_rot,
+                                  hipStream_t stream) {
+  const FQOut o{x, codes, scales, x_rot, zeros};
+  return signs ? dispatch_row_asym<true>(o, rows, n, signs, stream)
+               : dispatch_row_asym<false>(o, rows, n, signs, stream);
 }
 
 hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,

@@ -61,6 +61,28 @@ int rq_fwht_quant8(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int rq_fwht_quant_asym(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs,
+                       uint8_t* codes, uint16_t* scales, uint8_t* zeros, float* x_rot,
+                       void* stream) {
+  if (m < 0 || m >= kMaxRows) return RQ_ERR_SHAPE;
+  if (!is_pow2(n) || n < 512 || n > RQ_MAX_N) return RQ_ERR_SHAPE;
+  const int st = check_rotation_args(x, RQ_F16, m, n, signs, codes, scales, x_rot);
+  if (st != RQ_OK || m == 0) return st;
+  if (zeros == nullptr) return RQ_ERR_NULL;
+  return from_hip(rq::launch_fwht_quant_asym(x, m, (int)n, signs, codes, scales, zeros, x_rot,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int rq_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
+                        void* stream) {
+  if (k < 0 || k >= kMaxRows || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if (k == 0) return RQ_OK;
+  if (w_codes == nullptr || sums == nullptr) return RQ_ERR_NULL;
+  if (!aligned16(w_codes)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_weight_code_sums(w_codes, k, d, sums,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d) {
   (void)m;
   (void)k;
@@ -117,6 +139,24 @@ int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
   if (!aligned16(a_codes) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
   return from_hip(rq::launch_w4a8_gemm(a_codes, a_scales, m, w_codes, w_scales, k, d, y, acc,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
+                      int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
+                      const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
+                      void* stream) {
+  if (m < 0 || k < 0 || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (k == 0) return RQ_ERR_SHAPE;
+  if (a_codes == nullptr || a_scales == nullptr || a_zeros == nullptr || w_codes == nullptr ||
+      w_scales == nullptr || w_sums == nullptr || y == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_w4a4_gemm_asym(a_codes, a_scales, a_zeros, m, w_codes, w_scales,
+                                            w_sums, k, d, y, acc,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t rq_linear_decode_workspace_size(int64_t m, int64_t d) {

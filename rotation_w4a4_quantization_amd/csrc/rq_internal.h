@@ -21,6 +21,12 @@ hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, co
 hipError_t launch_fwht_quant8(const uint16_t* x, int64_t rows, int n, const int8_t* signs,
                               int8_t* codes, uint16_t* scales, float* x_rot, hipStream_t stream);
 
+// Row-wise (x * s) H_n / sqrt(n) fused with the asymmetric per-row INT4
+// quantiser (unsigned codes, integer zero points; fp16 x, n in 512..8192).
+hipError_t launch_fwht_quant_asym(const uint16_t* x, int64_t rows, int n, const int8_t* signs,
+                                  uint8_t* codes, uint16_t* scales, uint8_t* zeros, float* x_rot,
+                                  hipStream_t stream);
+
 // Same transform for the two KV tensors (fp16, n = 128) in one launch.
 hipError_t launch_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
                                   const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
@@ -36,6 +42,15 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
 hipError_t launch_w4a8_gemm(const int8_t* a_codes8, const uint16_t* a_scales, int64_t m,
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream);
+
+// Asymmetric activations: y = fp16(acc * sa * sw) with
+// acc = sum_i (qa[i] - za) * qw[i]; qa unsigned packed INT4, w_sums[j] = sum_i qw[j][i].
+hipError_t launch_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales,
+                                 const uint8_t* a_zeros, int64_t m, const uint8_t* w_codes,
+                                 const uint16_t* w_scales, const int32_t* w_sums, int64_t k,
+                                 int64_t d, uint16_t* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
+                                   hipStream_t stream);
 
 // Fused decode linear (m <= 16, fp16 x, d in 512..8192 a power of two):
 // rotation + INT4 quantisation of x as the prologue of the decode GEMM.

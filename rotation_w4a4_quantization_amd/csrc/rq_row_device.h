@@ -254,13 +254,19 @@ __device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl
 // codes_row through its LDS slice cb (as many bytes), or, with TO_LDS, leaves
 // them in cb (codes_row unused), and the fp32 rotated row goes to xrot_row
 // when it is not null.
-template <int N, bool HAS_SIGNS, bool TO_LDS = false, int BITS = 4>
+//
+// ASYM (INT4 only): the asymmetric quantiser.  The row range [lo, hi] is
+// widened to contain 0, the step is fp16(fp32(hi - lo) / 15) rounded once,
+// the zero point z = rne(-lo / step) (lane 0 writes it to *zero_out), and the
+// codes are the unsigned nibbles clamp(rne(x / step) + z, 0, 15).
+template <int N, bool HAS_SIGNS, bool TO_LDS = false, int BITS = 4, bool ASYM = false>
 __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
                                                  const int8_t* __restrict__ signs, int L,
                                                  const RowLane& rl, float c32, unsigned char* cb,
                                                  uint8_t* __restrict__ codes_row,
                                                  uint16_t* __restrict__ scale_out,
-                                                 float* __restrict__ xrot_row) {
+                                                 float* __restrict__ xrot_row,
+                                                 uint8_t* __restrict__ zero_out = nullptr) {
   constexpr int R = N / 64;    // elements per lane
   constexpr int NI = N / 512;  // 16-byte loads per lane
   static_assert(N >= 512 && N <= 8192, "one row per wavefront covers 512..8192");
@@ -329,16 +335,37 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
 #pragma unroll
   for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
 
-  float amax = 0.0f;
-#pragma unroll
-  for (int r = 0; r < R; ++r) amax = fmaxf(amax, fabsf(u[r]));
-  amax = wave_max(amax);
-
   static_assert(BITS == 4 || BITS == 8, "INT4 or INT8 codes");
-  constexpr float kM = BITS == 4 ? kMagic : kMagic8;
+  static_assert(!ASYM || BITS == 4, "the asymmetric quantiser has INT4 codes");
+  float kM = BITS == 4 ? kMagic : kMagic8;
   constexpr float kMLo = BITS == 4 ? kMagicLo : kMagic8Lo;
   constexpr float kMHi = BITS == 4 ? kMagicHi : kMagic8Hi;
-  const uint16_t hb = scale_fp16<BITS == 4 ? 7 : 127>(amax * c32);
+  uint16_t hb;
+  if constexpr (ASYM) {
+    // u[r] * sigma is the value: the lane's max and min swap when sigma < 0
+    float vmax = 0.0f, vmin = 0.0f;  // the range always contains 0
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      vmax = fmaxf(vmax, u[r]);
+      vmin = fminf(vmin, u[r]);
+    }
+    float hi_u = sigma > 0.0f ? vmax : -vmin;
+    float nlo_u = sigma > 0.0f ? -vmin : vmax;
+    hi_u = wave_max(hi_u);
+    nlo_u = wave_max(nlo_u);
+    const float hi32 = hi_u * c32, nlo32 = nlo_u * c32;  // fp32 hi and -lo of the rotated row
+    hb = scale_fp16<15>(hi32 + nlo32);
+    float zf = 0.0f;
+    if (hb != 0 && hb != 0x7C00u) zf = fminf(rintf(nlo32 / h2f(hb)), 15.0f);
+    if (L == 0) *zero_out = (uint8_t)zf;
+    kM = kMagicLo + zf;  // 2^23 + z: the low nibble of the sum is the code
+  } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) amax = fmaxf(amax, fabsf(u[r]));
+    amax = wave_max(amax);
+    hb = scale_fp16<BITS == 4 ? 7 : 127>(amax * c32);
+  }
   const bool subnormal = hb != 0 && hb < 0x0400u;
   const float mult = (hb == 0 ? 0.0f : c32 / h2f(hb)) * sigma;
   if (L == 0) *scale_out = hb;
@@ -356,7 +383,10 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
   float t[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) t[r] = __builtin_fmaf(u[r], mult, kM);
-  if (subnormal) {  // uniform: the scale is shared by the whole row
+  if constexpr (ASYM) {  // codes past 15 (step rounded down) or below 0 clamp
+#pragma unroll
+    for (int r = 0; r < R; ++r) t[r] = __builtin_amdgcn_fmed3f(t[r], kMagicLo, kMagicLo + 15.0f);
+  } else if (subnormal) {  // uniform: the scale is shared by the whole row
 #pragma unroll
     for (int r = 0; r < R; ++r) t[r] = fminf(fmaxf(t[r], kMLo), kMHi);
   }
@@ -382,7 +412,7 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
 #pragma unroll
   for (int c = L; c < kCodeBytes / 16; c += 64) {
     v4u v = *reinterpret_cast<const v4u*>(cb + 16 * c);
-    v ^= BITS == 4 ? 0x88888888u : 0x80808080u;
+    if constexpr (!ASYM) v ^= BITS == 4 ? 0x88888888u : 0x80808080u;  // to two's complement
     if constexpr (TO_LDS)
       *reinterpret_cast<v4u*>(cb + 16 * c) = v;
     else

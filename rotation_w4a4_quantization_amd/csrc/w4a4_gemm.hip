@@ -31,6 +31,10 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// Activation code formats: packed signed INT4 (W4A4), INT8 bytes (W4A8), and
+// packed unsigned INT4 with a per-row zero point (asymmetric activations).
+constexpr int kA4 = 0, kA8 = 1, kAU4 = 2;
+
 // 16 INT8 activation codes (natural order) rearranged into the k order that
 // widen() gives the weight codes: (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,...).
 __device__ __forceinline__ v4i order_a8(const uint4& q) {
@@ -39,6 +43,17 @@ __device__ __forceinline__ v4i order_a8(const uint4& q) {
   r[1] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
   r[2] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
   r[3] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
+  return r;
+}
+
+// Unsigned nibbles widened as q itself (0..15 fits a signed byte), in the
+// same k order as widen(); against 16 * q weights the MFMA sum is 16 * acc.
+__device__ __forceinline__ v4i widen_u(uint32_t w0, uint32_t w1) {
+  v4i r;
+  r[0] = (int)(w0 & 0x0F0F0F0Fu);
+  r[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
+  r[2] = (int)(w1 & 0x0F0F0F0Fu);
+  r[3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
   return r;
 }
 
@@ -53,11 +68,14 @@ __device__ __forceinline__ v4i widen(uint32_t w0, uint32_t w1) {
 
 
 // raw is 256 * acc for INT4 activations (both operands widened to 16 q) and
-// 16 * acc for INT8 activations (SHIFT 4): the shift is exact.
+// 16 * acc for INT8 and unsigned INT4 activations (SHIFT 4): the shift is
+// exact.  zsum = z * sum_i qw[j][i] turns the unsigned sum into the
+// accumulator of (qa - z) * qw (asymmetric activations; 0 otherwise).
 template <int SHIFT = 8>
 __device__ __forceinline__ void epilogue_store(int32_t raw, float sa, float sw, int64_t idx,
-                                               uint16_t* __restrict__ y, int32_t* __restrict__ acc) {
-  const int32_t a = raw >> SHIFT;
+                                               uint16_t* __restrict__ y, int32_t* __restrict__ acc,
+                                               int32_t zsum = 0) {
+  const int32_t a = (raw >> SHIFT) - zsum;
   if (acc != nullptr) acc[idx] = a;
   y[idx] = f2h_rn(((float)a * sa) * sw);
 }
@@ -70,15 +88,19 @@ constexpr int ROWB = TK / 2;      // packed bytes per row per step
 constexpr int PITCH = ROWB + 8;   // LDS row pitch (bytes), breaks the 32-byte stride
 constexpr int PITCH8 = TK + 16;   // INT8 activation rows (64 bytes per step), 16-byte aligned
 
-// A8: INT8 activation codes ([m][d] bytes, W4A8); the MFMA sum is 16 * acc.
-template <bool A8 = false>
+// AM: the activation code format (kA4, kA8: INT8 bytes [m][d], kAU4:
+// unsigned INT4 with zero points a_zeros and weight code sums w_sums).
+template <int AM = kA4>
 __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restrict__ a_codes,
                                                         const uint16_t* __restrict__ a_scales,
                                                         const uint8_t* __restrict__ w_codes,
                                                         const uint16_t* __restrict__ w_scales,
                                                         int64_t m, int64_t k, int64_t d,
                                                         uint16_t* __restrict__ y,
-                                                        int32_t* __restrict__ acc_out) {
+                                                        int32_t* __restrict__ acc_out,
+                                                        const uint8_t* __restrict__ a_zeros,
+                                                        const int32_t* __restrict__ w_sums) {
+  constexpr bool A8 = AM == kA8;
   constexpr int AW = A8 ? 2 : 1;  // activation bytes per weight byte
   constexpr int APITCH = A8 ? PITCH8 : PITCH;
   __shared__ __align__(16) unsigned char sa_tile[TM * APITCH];
@@ -129,7 +151,7 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
         af[i] = order_a8(*reinterpret_cast<const uint4*>(ap + 16 * g));
       } else {
         const uint2 p = *reinterpret_cast<const uint2*>(ap + 8 * g);
-        af[i] = widen(p.x, p.y);
+        af[i] = AM == kAU4 ? widen_u(p.x, p.y) : widen(p.x, p.y);
       }
     }
 #pragma unroll
@@ -152,12 +174,13 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
       const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
       if (row >= m) continue;
       const float sa = h2f(a_scales[row]);
+      const int32_t z = AM == kAU4 ? (int32_t)a_zeros[row] : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = n0 + wn * 64 + j * 16 + r16;
         if (col < k)
-          epilogue_store<A8 ? 4 : 8>(acc[i][j][e], sa, h2f(w_scales[col]), row * k + col, y,
-                                     acc_out);
+          epilogue_store<AM == kA4 ? 8 : 4>(acc[i][j][e], sa, h2f(w_scales[col]), row * k + col,
+                                            y, acc_out, AM == kAU4 ? z * w_sums[col] : 0);
       }
     }
   }
@@ -310,11 +333,12 @@ __device__ __forceinline__ void dec_issue_w(const DecLane<RG>& t, int64_t c0) {
 // its next loads may overwrite them).  A8: the activations are INT8 codes
 // (one byte per code, a_src advancing 2 bytes per weight byte), so a lane's
 // 32 codes of a part take two 16-byte loads.
-template <int RG, bool A8 = false>
+template <int RG, int AM = kA4>
 __device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsigned char* wl,
                                               const uint8_t* a_src, bool a_ok, int64_t c0,
                                               v4i (&acc0)[RG], v4i (&acc1)[RG]) {
   constexpr int SEGB = 16 * RG * DSEG;
+  constexpr bool A8 = AM == kA8;
   constexpr int AW = A8 ? 2 : 1;  // 16-byte activation loads per part
   uint4 av[2][2][AW];
 #pragma unroll
@@ -340,6 +364,9 @@ __device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsign
       if constexpr (A8) {
         a0 = order_a8(av[sl][h][0]);
         a1 = order_a8(av[sl][h][AW - 1]);
+      } else if constexpr (AM == kAU4) {
+        a0 = widen_u(av[sl][h][0].x, av[sl][h][0].y);
+        a1 = widen_u(av[sl][h][0].z, av[sl][h][0].w);
       } else {
         a0 = widen(av[sl][h][0].x, av[sl][h][0].y);
         a1 = widen(av[sl][h][0].z, av[sl][h][0].w);
@@ -366,7 +393,9 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
                                                  const uint16_t* __restrict__ a_scales,
                                                  const uint16_t* __restrict__ w_scales,
                                                  uint16_t* __restrict__ y,
-                                                 int32_t* __restrict__ acc_out) {
+                                                 int32_t* __restrict__ acc_out,
+                                                 const uint8_t* __restrict__ a_zeros = nullptr,
+                                                 const int32_t* __restrict__ w_sums = nullptr) {
 #pragma unroll
   for (int q = 0; q < RG; ++q) partial[t.wave * pitch + q * 64 + t.lane] = acc0[q] + acc1[q];
   __syncthreads();
@@ -377,24 +406,29 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
     const int64_t col = t.n0 + 16 * t.wave + t.r16;
     if (col < k) {
       const float sw = h2f(w_scales[col]);
+      const int32_t ws = w_sums != nullptr ? w_sums[col] : 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 4 * t.g + e;
         if (row < m)
-          epilogue_store<SHIFT>(s[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out);
+          epilogue_store<SHIFT>(s[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out,
+                                a_zeros != nullptr ? (int32_t)a_zeros[row] * ws : 0);
       }
     }
   }
 }
 
 // RG 16-row groups of weights per workgroup share each activation fragment.
-// A8: INT8 activation codes ([m][d] bytes) against the INT4 weights (W4A8);
-// the MFMA sum is then 16 * acc.
-template <int RG, bool A8 = false>
+// AM: activation code format, kA8 (INT8 codes [m][d] bytes, W4A8) or kAU4
+// (unsigned INT4 with zero points a_zeros and weight code sums w_sums); for
+// both the MFMA sum is 16 * acc.
+template <int RG, int AM = kA4>
 __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int64_t m,
-    int64_t k, int64_t d, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out) {
+    int64_t k, int64_t d, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out,
+    const uint8_t* __restrict__ a_zeros, const int32_t* __restrict__ w_sums) {
+  constexpr bool A8 = AM == kA8;
   __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];  // 32 KB per row group
   __shared__ v4i partial[DEC_WAVES][RG][64];
   const int64_t rowb = d / 2;
@@ -408,10 +442,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
   for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
   for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
     dec_issue_w(t, c0);
-    dec_mma_chunk<RG, A8>(t, wl, a_src, a_ok, c0, acc0, acc1);
+    dec_mma_chunk<RG, AM>(t, wl, a_src, a_ok, c0, acc0, acc1);
   }
-  dec_reduce_store<RG, A8 ? 4 : 8>(t, &partial[0][0][0], RG * 64, acc0, acc1, m, k, a_scales,
-                                   w_scales, y, acc_out);
+  dec_reduce_store<RG, AM == kA4 ? 8 : 4>(t, &partial[0][0][0], RG * 64, acc0, acc1, m, k,
+                                          a_scales, w_scales, y, acc_out,
+                                          AM == kAU4 ? a_zeros : nullptr,
+                                          AM == kAU4 ? w_sums : nullptr);
 }
 
 // ------------------------------------------------------- fused decode linear
@@ -718,7 +754,43 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 }
 #undef RQ_DMA
 
+// sums[j] = sum_i qw[j][i] over the packed signed INT4 codes of weight row j
+// (one wavefront per row; an offline companion of the folded weights).
+__global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __restrict__ w_codes,
+                                                               int64_t k, int64_t rowb,
+                                                               int32_t* __restrict__ sums) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t j = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); j < k;
+       j += waves) {
+    int32_t acc = 0;
+    for (int64_t c = lane; c < rowb / 16; c += 64) {
+      const uint4 v = *reinterpret_cast<const uint4*>(w_codes + j * rowb + 16 * c);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int32_t nib = (int32_t)((w4[q] >> (4 * b)) & 15u);
+          acc += nib - ((nib & 8) << 1);  // sign-extend the nibble
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) sums[j] = acc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
+                                   hipStream_t stream) {
+  const int64_t blocks = (k + 3) / 4;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  hipLaunchKernelGGL(weight_code_sums_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)),
+                     dim3(256), 0, stream, w_codes, k, d / 2, sums);
+  return hipGetLastError();
+}
 
 hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
@@ -742,18 +814,43 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
       if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
         hipLaunchKernelGGL(w4a4_decode_lds_kernel<2>, dim3((unsigned)((k + 31) / 32)),
                            dim3(64 * DEC_WAVES), 0, stream, a_codes, a_scales, w_codes, w_scales, m,
-                           k, d, y, acc);
+                           k, d, y, acc, nullptr, nullptr);
       else
         hipLaunchKernelGGL(w4a4_decode_lds_kernel<1>, dim3((unsigned)blocks), dim3(64 * DEC_WAVES),
-                           0, stream, a_codes, a_scales, w_codes, w_scales, m, k, d, y, acc);
+                           0, stream, a_codes, a_scales, w_codes, w_scales, m, k, d, y, acc,
+                           nullptr, nullptr);
     }
     else
       hipLaunchKernelGGL(w4a4_decode_kernel, dim3((unsigned)blocks), dim3(64 * DEC_WAVES), 0, stream,
                          a_codes, a_scales, w_codes, w_scales, m, k, d, y, acc);
   } else {
     const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
-    hipLaunchKernelGGL(w4a4_tile_kernel<false>, grid, dim3(256), 0, stream, a_codes, a_scales,
-                       w_codes, w_scales, m, k, d, y, acc);
+    hipLaunchKernelGGL(w4a4_tile_kernel<kA4>, grid, dim3(256), 0, stream, a_codes, a_scales,
+                       w_codes, w_scales, m, k, d, y, acc, nullptr, nullptr);
+  }
+  return hipGetLastError();
+}
+
+// The decode kernel (m <= 16, d % 256 == 0) or the tile kernel, for the
+// activation format AM.
+template <int AM>
+hipError_t launch_gemm_variant(const uint8_t* a, const uint16_t* a_scales, const uint8_t* a_zeros,
+                               int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
+                               const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y,
+                               int32_t* acc, hipStream_t stream) {
+  if (m <= 16 && d % (2 * DSEG) == 0) {
+    if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
+      hipLaunchKernelGGL((w4a4_decode_lds_kernel<2, AM>), dim3((unsigned)((k + 31) / 32)),
+                         dim3(64 * DEC_WAVES), 0, stream, a, a_scales, w_codes, w_scales, m, k, d,
+                         y, acc, a_zeros, w_sums);
+    else
+      hipLaunchKernelGGL((w4a4_decode_lds_kernel<1, AM>), dim3((unsigned)((k + 15) / 16)),
+                         dim3(64 * DEC_WAVES), 0, stream, a, a_scales, w_codes, w_scales, m, k, d,
+                         y, acc, a_zeros, w_sums);
+  } else {
+    const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
+    hipLaunchKernelGGL(w4a4_tile_kernel<AM>, grid, dim3(256), 0, stream, a, a_scales, w_codes,
+                       w_scales, m, k, d, y, acc, a_zeros, w_sums);
   }
   return hipGetLastError();
 }
@@ -761,22 +858,16 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
 hipError_t launch_w4a8_gemm(const int8_t* a_codes8, const uint16_t* a_scales, int64_t m,
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream) {
-  const uint8_t* a = reinterpret_cast<const uint8_t*>(a_codes8);
-  if (m <= 16 && d % (2 * DSEG) == 0) {
-    if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
-      hipLaunchKernelGGL((w4a4_decode_lds_kernel<2, true>), dim3((unsigned)((k + 31) / 32)),
-                         dim3(64 * DEC_WAVES), 0, stream, a, a_scales, w_codes, w_scales, m, k, d,
-                         y, acc);
-    else
-      hipLaunchKernelGGL((w4a4_decode_lds_kernel<1, true>), dim3((unsigned)((k + 15) / 16)),
-                         dim3(64 * DEC_WAVES), 0, stream, a, a_scales, w_codes, w_scales, m, k, d,
-                         y, acc);
-  } else {
-    const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
-    hipLaunchKernelGGL(w4a4_tile_kernel<true>, grid, dim3(256), 0, stream, a, a_scales, w_codes,
-                       w_scales, m, k, d, y, acc);
-  }
-  return hipGetLastError();
+  return launch_gemm_variant<kA8>(reinterpret_cast<const uint8_t*>(a_codes8), a_scales, nullptr,
+                                  m, w_codes, w_scales, nullptr, k, d, y, acc, stream);
+}
+
+hipError_t launch_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales,
+                                 const uint8_t* a_zeros, int64_t m, const uint8_t* w_codes,
+                                 const uint16_t* w_scales, const int32_t* w_sums, int64_t k,
+                                 int64_t d, uint16_t* y, int32_t* acc, hipStream_t stream) {
+  return launch_gemm_variant<kAU4>(a_codes, a_scales, a_zeros, m, w_codes, w_scales, w_sums, k,
+                                   d, y, acc, stream);
 }
 
 

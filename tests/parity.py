@@ -126,3 +126,48 @@ def check_gemm(a_codes, a_scales, w_codes, w_scales, y, acc=None, what="gemm",
     ok = (np.abs(yg - yr) <= tol) | both_inf
     assert ok.all(), f"{what}: {int((~ok).sum())} fp16 outputs outside 1e-2 relative"
     return y_ref, acc_ref
+
+
+def check_asym_result(x, signs, codes, scales, zeros, x_rot=None, what="fwht_quant_asym",
+                      report=None):
+    """Full check of one rq_fwht_quant_asym result against the oracle.
+
+    Rotated rows and scales bit-identical to the fp32 mirror (the range
+    hi - lo is an fp32 difference on both sides).  The zero point and the
+    codes are decisions on pre-round values that the kernel and the mirror
+    compute with one fp32 rounding each (|dv| <= 2^-23 |v|): a zero point may
+    differ by one only where the mirror's -lo/scale lies within
+    BAND + BAND8_REL |w| of a half-integer, and a code only where x~/scale
+    does; codes are compared against the mirror's level shifted by the
+    kernel's own zero point.
+    """
+    x = np.asarray(x)
+    mirror = O.fwht_quant_asym(x, signs, "f32")
+    if x_rot is not None:
+        diff = x_rot.view(np.uint32) != mirror["x_rot"].view(np.uint32)
+        diff &= ~((x_rot == 0) & (mirror["x_rot"] == 0))
+        assert not diff.any(), f"{what}: rotated rows differ from the fp32 mirror"
+    assert np.array_equal(scales.view(np.uint16), mirror["scales"].view(np.uint16)), \
+        f"{what}: scales differ from the mirror"
+    zd = zeros.astype(np.int16) - mirror["zeros"].astype(np.int16)
+    if zd.any():
+        w = mirror["w"][zd != 0]
+        assert np.all(np.abs(zd[zd != 0]) == 1), f"{what}: zero point off by more than one"
+        assert np.all(dist_to_half_integer(w) <= BAND + BAND8_REL * np.abs(w)), \
+            f"{what}: zero-point mismatch outside the rounding band"
+    q_gpu = O.unpack_uint4(codes).astype(np.int16)
+    v = mirror["v"]
+    q_ref = np.clip(np.rint(v) + zeros.astype(np.float64)[:, None], 0, 15).astype(np.int16)
+    scale_ok = (mirror["scales"].astype(np.float64) > 0) & np.isfinite(mirror["scales"].astype(np.float64))
+    q_ref = np.where(scale_ok[:, None], q_ref, 0)
+    bad = q_gpu != q_ref
+    n_bad = int(bad.sum())
+    if n_bad:
+        assert np.all(np.abs(q_gpu[bad] - q_ref[bad]) == 1), f"{what}: code off by more than one"
+        vb = v[bad]
+        assert np.all(dist_to_half_integer(vb) <= BAND + BAND8_REL * np.abs(vb)), \
+            f"{what}: {n_bad} code mismatches, some outside the rounding band"
+    if report is not None:
+        report.append({"what": what, "elements": int(q_gpu.size), "band_mismatch_vs_mirror": n_bad,
+                       "zero_point_band_mismatch": int((zd != 0).sum())})
+    return n_bad

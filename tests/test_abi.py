@@ -168,6 +168,37 @@ def test_linear_decode_argument_errors(lib):
     assert call(ws=MIS) == binding.RQ_ERR_ALIGN
 
 
+def test_asym_argument_errors(lib):
+    f = lib.rq_fwht_quant_asym
+
+    def fq(x=A16, m=4, n=4096, signs=None, codes=A16b, scales=A16b, zeros=A16b, rot=None):
+        return f(x, m, n, signs, codes, scales, zeros, rot, None)
+
+    assert fq(m=0) == binding.RQ_OK
+    assert fq(x=None) == binding.RQ_ERR_NULL
+    assert fq(zeros=None) == binding.RQ_ERR_NULL
+    assert fq(n=256) == binding.RQ_ERR_SHAPE
+    assert fq(n=14336) == binding.RQ_ERR_SHAPE
+    assert fq(codes=MIS) == binding.RQ_ERR_ALIGN
+    s = lib.rq_weight_code_sums
+    assert s(A16, 0, 4096, A16b, None) == binding.RQ_OK
+    assert s(None, 4, 4096, A16b, None) == binding.RQ_ERR_NULL
+    assert s(A16, 4, 4096, None, None) == binding.RQ_ERR_NULL
+    assert s(A16, 4, 96, A16b, None) == binding.RQ_ERR_SHAPE
+    assert s(MIS, 4, 4096, A16b, None) == binding.RQ_ERR_ALIGN
+    g = lib.rq_w4a4_gemm_asym
+
+    def gemm(a=A16, sa=A16b, za=A16b, m=4, w=A16, sw=A16b, ws=A16b, k=64, d=4096, y=A16b):
+        return g(a, sa, za, m, w, sw, ws, k, d, y, None, None)
+
+    assert gemm(m=0) == binding.RQ_OK
+    assert gemm(za=None) == binding.RQ_ERR_NULL
+    assert gemm(ws=None) == binding.RQ_ERR_NULL
+    assert gemm(d=96) == binding.RQ_ERR_SHAPE
+    assert gemm(k=0) == binding.RQ_ERR_SHAPE
+    assert gemm(a=MIS) == binding.RQ_ERR_ALIGN
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

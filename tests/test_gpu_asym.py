@@ -1,0 +1,161 @@
+"""GPU parity of the asymmetric-activation variant: rq_fwht_quant_asym,
+rq_weight_code_sums and rq_w4a4_gemm_asym through the C ABI against the CPU
+oracle (rules in tests/parity.py: bit-identical rotation and scales, zero
+points and codes equal up to the fp32 rounding band, exact int32
+accumulators, fp16 outputs within 1e-2)."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import rq_oracle as O
+from rotation_w4a4_quantization_amd import datagen
+from tests.parity import Y_TOL, check_asym_result
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rq():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import rotation_w4a4_quantization_amd as rq
+    rq.load_library()
+    return rq
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def run_asym(rq, x, signs, debug=True):
+    c, s, z, r = rq.fwht_quant_asym(dev(x), None if signs is None else dev(signs), debug=debug)
+    torch.cuda.synchronize()
+    return host(c), host(s), host(z), host(r)
+
+
+def check_gemm_asym(ac, sa, za, wc, sw, y, acc, what):
+    y_ref, acc_ref = O.w4a4_gemm_asym(ac, sa, za, wc, sw)
+    assert np.array_equal(acc.astype(np.int64), acc_ref), \
+        f"{what}: accumulators differ in {int((acc != acc_ref).sum())} places"
+    yr, yg = y_ref.astype(np.float64), y.astype(np.float64)
+    both_inf = np.isinf(yr) & np.isinf(yg) & (np.sign(yr) == np.sign(yg))
+    ok = (np.abs(yg - yr) <= Y_TOL * np.maximum(np.abs(yr), 2.0 ** -14)) | both_inf
+    assert ok.all(), f"{what}: {int((~ok).sum())} fp16 outputs outside 1e-2 relative"
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096, 8192])
+def test_fwht_quant_asym_sizes_ragged(rq, n):
+    rng = np.random.default_rng(900 + n)
+    m = 37
+    say(f"fwht_quant_asym n={n} m={m}")
+    x = (rng.standard_normal((m, n)) * rng.uniform(0.1, 10, (m, 1))).astype(np.float16)
+    x[0, rng.integers(n)] *= 100
+    x[1] = np.abs(x[1]) + 1.0  # a mean offset: a skewed rotated row
+    for signs in (datagen.rademacher(rng, n), None):
+        c, s, z, r = run_asym(rq, x, signs)
+        check_asym_result(x, signs, c, s, z, r, what=f"asym n={n}")
+        c2, s2, z2, _ = run_asym(rq, x, signs, debug=False)
+        assert np.array_equal(c, c2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+
+
+def test_fwht_quant_asym_special_rows(rq):
+    n = 4096
+    x = np.zeros((6, n), np.float16)
+    x[1, 0] = 3.0                         # no signs: x~ = 3/64 everywhere -> lo = 0, z = 0, codes 15
+    x[2, 0] = -3.0                        # x~ = -3/64 everywhere -> hi = 0, z = 15, codes 0
+    x[3, :3] = [6e-8, -6e-8, 0.0]         # range / 15 below half the smallest fp16 subnormal
+    x[4, :4] = [4e-4, -4e-4, 1e-4, 0.0]   # fp16-subnormal step (codes clamp)
+    rng = np.random.default_rng(9)
+    x[5] = rng.standard_normal(n)
+    say("fwht_quant_asym special rows")
+    c, s, z, r = run_asym(rq, x, None)
+    check_asym_result(x, None, c, s, z, r, what="asym special rows")
+    q = O.unpack_uint4(c)
+    assert s.view(np.uint16)[0] == 0 and z[0] == 0 and not q[0].any()
+    assert z[1] == 0 and (q[1] == 15).all()
+    assert z[2] == 15 and (q[2] == 0).all()
+    assert s.view(np.uint16)[3] == 0 and z[3] == 0 and not q[3].any()
+    assert 0 < s.view(np.uint16)[4] < 0x0400
+
+
+def test_weight_code_sums(rq):
+    rng = np.random.default_rng(10)
+    for k, d in ((1, 64), (37, 512), (300, 4160), (5, 16384)):
+        wc = datagen.random_codes(rng, k, d)
+        say(f"weight_code_sums k={k} d={d}")
+        sums = host(rq.weight_code_sums(dev(wc)))
+        assert np.array_equal(sums.astype(np.int64), O.unpack_int4(wc).astype(np.int64).sum(axis=1))
+
+
+ASYM_SHAPES = [(1, 1, 64), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
+               (5, 33, 192), (17, 33, 64), (130, 129, 256), (300, 260, 1024)]
+
+
+@pytest.mark.parametrize("m,k,d", ASYM_SHAPES)
+def test_w4a4_gemm_asym_random_codes(rq, m, k, d):
+    rng = np.random.default_rng(m * 1000 + k + d + 16)
+    ac = datagen.random_codes(rng, m, d)
+    za = rng.integers(0, 16, m).astype(np.uint8)
+    wc = datagen.random_codes(rng, k, d)
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k)
+    say(f"w4a4 asym gemm m={m} k={k} d={d}")
+    wsum = rq.weight_code_sums(dev(wc))
+    y, acc = rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum, debug=True)
+    torch.cuda.synchronize()
+    check_gemm_asym(ac, sa, za, wc, sw, host(y), host(acc), f"asym {m}x{k}x{d}")
+    y2, _ = rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum)
+    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
+
+
+def test_w4a4_gemm_asym_closed_form(rq):
+    m, k, d = 3, 40, 16384
+    a = O._pack_uint4(np.full((m, d), 15))
+    w = O.pack_int4(np.full((k, d), -8))
+    w[1::2] = O.pack_int4(np.full((1, d), 7))
+    za = np.array([0, 15, 7], np.uint8)
+    say("w4a4 asym gemm closed form")
+    wsum = rq.weight_code_sums(dev(w))
+    y, acc = rq.w4a4_gemm_asym(dev(a), dev(np.full(m, 2.0 ** -12, np.float16)), dev(za), dev(w),
+                               dev(np.full(k, 2.0 ** -12, np.float16)), wsum, debug=True)
+    acc = host(acc)
+    for i, z in enumerate(za.tolist()):
+        assert (acc[i, 0::2] == (15 - z) * -8 * d).all() and (acc[i, 1::2] == (15 - z) * 7 * d).all()
+
+
+def test_asym_decode_linear_end_to_end(rq):
+    dec = datagen.decode_linear(0)
+    s = dev(dec["signs"])
+    ac, sa, za, xr = rq.fwht_quant_asym(dev(dec["x"]), s, debug=True)
+    torch.cuda.synchronize()
+    check_asym_result(dec["x"], dec["signs"], host(ac), host(sa), host(za), host(xr),
+                      what="asym decode activations")
+    for k, wt in dec["wts"].items():
+        wc, ws, _ = rq.fold_weights(dev(wt), s)
+        wsum = rq.weight_code_sums(wc)
+        for m in (1, 4, 16):
+            say(f"asym decode linear m={m} k={k}")
+            y, acc = rq.w4a4_gemm_asym(ac[:m].contiguous(), sa[:m].contiguous(),
+                                       za[:m].contiguous(), wc, ws, wsum, debug=True)
+            torch.cuda.synchronize()
+            check_gemm_asym(host(ac[:m]), host(sa[:m]), host(za[:m]), host(wc), host(ws), host(y),
+                            host(acc), f"asym decode m={m} k={k}")
+
+
+def test_asym_empty(rq):
+    c, s, z, _ = rq.fwht_quant_asym(torch.zeros((0, 512), dtype=torch.float16, device="cuda"))
+    assert c.shape == (0, 256) and z.shape == (0,)
+    torch.cuda.synchronize()
