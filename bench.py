@@ -433,6 +433,49 @@ def main():
                     log(f"[bench] {key}: {sec[key]}")
                 del wcs, wc
 
+        if want("grouped"):
+            # per-group (128) INT4 weight scales on the decode and prefill GEMMs
+            dec = datagen.decode_linear(0)
+            s = torch.from_numpy(dec["signs"]).to(dev)
+            acg, sag, _ = rq.fwht_quant(torch.from_numpy(dec["x"]).to(dev), s)
+            for k, wt in dec["wts"].items():
+                wc, wsg = rq.fold_weights_grouped(torch.from_numpy(wt).to(dev), s, 128)
+                nsets = max(2, -(-2 * MALL_BYTES // wc.numel()) + 1)
+                wcs = [wc.clone() for _ in range(nsets)]
+                for mm in (1, 4, 16):
+                    y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+                    a_m, s_m = acg[:mm].contiguous(), sag[:mm].contiguous()
+
+                    def gg(i, a_m=a_m, s_m=s_m, y=y):
+                        rq.w4a4_gemm_grouped(a_m, s_m, wcs[i], wsg, out=y)
+
+                    msg = time_launches(torch, gg, nsets, steps2, warm2)
+                    bb = gemm_bytes(mm, k, 4096) - 2 * k + 2 * k * (4096 // 128)
+                    key = f"gemm_grouped_decode_m{mm}_k{k}"
+                    sec[key] = {"us": round(msg * 1e3, 3), "GB/s": round(bb / (msg * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(bb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    log(f"[bench] {key}: {sec[key]}")
+                del wcs, wc
+            pf = datagen.prefill_linear(0)
+            sp = torch.from_numpy(pf["signs"]).to(dev)
+            wc, wsg = rq.fold_weights_grouped(torch.from_numpy(pf["wt"]).to(dev), sp, 128)
+            del pf["wt"]
+            mm, d, k = pf["m"], pf["d"], pf["k"]
+            acp, sap, _ = rq.fwht_quant(torch.from_numpy(pf["x"]).to(dev), sp)
+            y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+            wcs = [wc, wc.clone()]
+
+            def gpg(i):
+                rq.w4a4_gemm_grouped(acp, sap, wcs[i], wsg, out=y)
+
+            msp = time_launches(torch, gpg, 2, max(5, steps2 // 4), warm2)
+            tops = 2 * mm * d * k / (msp * 1e-3) / 1e12
+            sec["gemm_grouped_prefill_2048x8192x28672"] = {
+                "us": round(msp * 1e3, 2), "TOPS": round(tops, 1),
+                "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+            log(f"[bench] grouped prefill gemm: {sec['gemm_grouped_prefill_2048x8192x28672']}")
+            del wcs, wc, y, acp
+
         if want("kv"):
             kv = datagen.kv_cache(0)
             kt = torch.from_numpy(kv["k"]).to(dev)

@@ -319,6 +319,47 @@ int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const ui
                       const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
                       void* stream);
 
+/*
+ * rq_quantize_groups -- symmetric INT4 with one scale per group of `group`
+ * consecutive elements of each fp32 row (per-group weight scales).
+ *
+ * [SpinQuant] "End-to-end flow" (the rotated weights are mapped to INT4 with
+ * per-channel or per-group scales).  Offline use: the rows are the folded
+ * weights W~^T that rq_fold_weights writes to w_rot.  Per group: scale =
+ * fp16(max |x| / 7) rounded once, code = clamp(rne(x * fp32(1 / scale)),
+ * -8, 7); a zero or infinite scale gives zero codes.
+ *
+ *   x       [rows][n] float32, 16-byte aligned.
+ *   group   32, 64, 128 or 256; n a multiple of group, n <= 2^20.
+ *   codes   [rows][n/2] uint8 output (packed like rq_fwht_quant), 16-byte
+ *           aligned.
+ *   scales  [rows][n / group] fp16 output.
+ */
+int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, uint8_t* codes,
+                       uint16_t* scales, void* stream);
+
+/*
+ * rq_w4a4_gemm_grouped -- W4A4 linear with per-token activation scales and
+ * per-group weight scales (group 128):
+ * y[m][j] = fp16(sa[m] * sum_g sw[j][g] * acc[m][j][g]),
+ * acc[m][j][g] = sum over the 128 codes of group g of qa[m][i] * qw[j][i].
+ *
+ * [SpinQuant] "The architecture: every piece explained" and "End-to-end
+ * flow" (INT4 weights with per-group scales, integer matmul).  Each group's
+ * integer dot product is exact in int32 (int8 MFMA on widened codes) and
+ * turns into fp32 with its group scale; the sum over groups is fp32.
+ *
+ *   a_codes         [m][d/2] (rq_fwht_quant), 16-byte aligned; a_scales [m].
+ *   w_codes         [k][d/2] (rq_quantize_groups on the folded weights),
+ *                   16-byte aligned.
+ *   w_group_scales  [k][d / 128] fp16.
+ *   m >= 0; k >= 1 when m > 0; d a multiple of 128 in [128, 16384].
+ *   y               [m][k] fp16 output.
+ */
+int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                         const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
+                         int64_t d, uint16_t* y, void* stream);
+
 /* Text for an rq_status value (static storage, never NULL). */
 const char* rq_status_string(int status);
 

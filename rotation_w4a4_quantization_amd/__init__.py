@@ -10,18 +10,21 @@ from .binding import (  # noqa: F401
     EXPORTED,
     RQError,
     fold_weights,
+    fold_weights_grouped,
     fwht_quant,
     fwht_quant8,
     fwht_quant_asym,
     kv_rotate_quant,
     linear_decode,
     linear_decode_workspace,
+    quantize_groups,
     load_library,
     status_string,
     version,
     weight_code_sums,
     w4a4_gemm,
     w4a4_gemm_asym,
+    w4a4_gemm_grouped,
     w4a4_linear,
     w4a4_linear_asym,
     w4a8_gemm,

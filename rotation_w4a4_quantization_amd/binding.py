@@ -32,6 +32,8 @@ EXPORTED = (
     "rq_fwht_quant_asym",
     "rq_weight_code_sums",
     "rq_w4a4_gemm_asym",
+    "rq_quantize_groups",
+    "rq_w4a4_gemm_grouped",
     "rq_status_string",
     "rq_version",
 )
@@ -80,6 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_weight_code_sums.restype = i32
     lib.rq_w4a4_gemm_asym.argtypes = [p, p, p, i64, p, p, p, i64, i64, p, p, p]
     lib.rq_w4a4_gemm_asym.restype = i32
+    lib.rq_quantize_groups.argtypes = [p, i64, i64, i64, p, p, p]
+    lib.rq_quantize_groups.restype = i32
+    lib.rq_w4a4_gemm_grouped.argtypes = [p, p, i64, p, p, i64, i64, p, p]
+    lib.rq_w4a4_gemm_grouped.restype = i32
     lib.rq_status_string.argtypes = [i32]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_version.argtypes = []
@@ -356,4 +362,49 @@ def w4a4_linear_asym(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch
     """Online rotation + asymmetric INT4 quantisation of x, then the GEMM."""
     codes, scales, zeros, _ = fwht_quant_asym(x, signs)
     y, _ = w4a4_gemm_asym(codes, scales, zeros, w_codes, w_scales, w_sums)
+    return y
+
+
+def quantize_groups(x: torch.Tensor, group: int = 128):
+    """rq_quantize_groups on fp32 rows: returns (codes uint8 [rows, n/2],
+    scales fp16 [rows, n / group])."""
+    _need_cuda("x", x)
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be a float32 [rows, n] tensor")
+    rows, n = x.shape
+    codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, max(1, n // group)), dtype=torch.float16, device=x.device)
+    st = load_library().rq_quantize_groups(_ptr(x), rows, n, group, _ptr(codes), _ptr(scales),
+                                           _stream())
+    _check("rq_quantize_groups", st)
+    return codes, scales
+
+
+def fold_weights_grouped(wt: torch.Tensor, signs: torch.Tensor | None = None, group: int = 128):
+    """Offline fold W~^T = W^T R (rq_fold_weights, fp32 rotated rows) followed
+    by per-group INT4 (rq_quantize_groups): returns (codes [k, d/2],
+    group scales [k, d / group])."""
+    _, _, w_rot = fold_weights(wt, signs, debug=True)
+    return quantize_groups(w_rot, group)
+
+
+def w4a4_gemm_grouped(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+                      w_group_scales: torch.Tensor, out: torch.Tensor | None = None):
+    """rq_w4a4_gemm_grouped (group 128): returns y fp16 [m, k]."""
+    for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes),
+                    ("w_group_scales", w_group_scales)):
+        _need_cuda(name, t)
+    if a_codes.dtype != torch.uint8 or w_codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
+    if a_scales.dtype != torch.float16 or w_group_scales.dtype != torch.float16:
+        raise ValueError("scales must be float16")
+    m, half_d = a_codes.shape
+    k, half_d2 = w_codes.shape
+    d = 2 * half_d
+    if half_d != half_d2 or a_scales.numel() != m or w_group_scales.numel() != k * (d // 128):
+        raise ValueError("shapes do not match")
+    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
+    st = load_library().rq_w4a4_gemm_grouped(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes),
+                                             _ptr(w_group_scales), k, d, _ptr(y), _stream())
+    _check("rq_w4a4_gemm_grouped", st)
     return y

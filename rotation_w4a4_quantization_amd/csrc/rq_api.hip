@@ -159,6 +159,34 @@ int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const ui
                                             static_cast<hipStream_t>(stream)));
 }
 
+int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, uint8_t* codes,
+                       uint16_t* scales, void* stream) {
+  if (group != 32 && group != 64 && group != 128 && group != 256) return RQ_ERR_SHAPE;
+  if (rows < 0 || rows >= kMaxRows || n < group || n % group != 0 || n > (1 << 20))
+    return RQ_ERR_SHAPE;
+  if (rows == 0) return RQ_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return RQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_quantize_groups(x, rows, n, (int)group, codes, scales,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                         const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
+                         int64_t d, uint16_t* y, void* stream) {
+  if (m < 0 || k < 0 || d < 128 || d > 16384 || d % 128 != 0) return RQ_ERR_SHAPE;
+  if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (k == 0) return RQ_ERR_SHAPE;
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr ||
+      w_group_scales == nullptr || y == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_w4a4_gemm_grouped(a_codes, a_scales, m, w_codes, w_group_scales, k,
+                                               d, y, static_cast<hipStream_t>(stream)));
+}
+
 size_t rq_linear_decode_workspace_size(int64_t m, int64_t d) {
   if (m < 0 || m > 16 || d < 0) return 0;
   return rq::linear_decode_workspace_bytes(m, d);

@@ -52,6 +52,15 @@ hipError_t launch_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scale
 hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
                                    hipStream_t stream);
 
+// Per-group INT4 weights: symmetric INT4 with one scale per `group`
+// elements of fp32 rows (group 32, 64, 128 or 256), and the W4A4 GEMM with
+// per-group weight scales (group 128, wg_scales [k][d / 128]).
+hipError_t launch_quantize_groups(const float* x, int64_t rows, int64_t n, int group,
+                                  uint8_t* codes, uint16_t* scales, hipStream_t stream);
+hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                                    const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
+                                    int64_t d, uint16_t* y, hipStream_t stream);
+
 // Fused decode linear (m <= 16, fp16 x, d in 512..8192 a power of two):
 // rotation + INT4 quantisation of x as the prologue of the decode GEMM.
 size_t linear_decode_workspace_bytes(int64_t m, int64_t d);

@@ -30,6 +30,11 @@ namespace rq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Per-group weight scales: one fp16 scale per WG consecutive codes of a
+// weight row, stored [k][d / WG].
+constexpr int WG = 128;
 
 // Activation code formats: packed signed INT4 (W4A4), INT8 bytes (W4A8), and
 // packed unsigned INT4 with a per-row zero point (asymmetric activations).
@@ -90,7 +95,10 @@ constexpr int PITCH8 = TK + 16;   // INT8 activation rows (64 bytes per step), 1
 
 // AM: the activation code format (kA4, kA8: INT8 bytes [m][d], kAU4:
 // unsigned INT4 with zero points a_zeros and weight code sums w_sums).
-template <int AM = kA4>
+// GROUPED (with kA4): w_scales holds per-group scales [k][d / WG]; every
+// two 64-code steps (one group) the int32 tile turns into fp32 with its
+// group scale.
+template <int AM = kA4, bool GROUPED = false>
 __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restrict__ a_codes,
                                                         const uint16_t* __restrict__ a_scales,
                                                         const uint8_t* __restrict__ w_codes,
@@ -115,10 +123,15 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
   const int64_t rowb = d / 2;
 
   v4i acc[4][4];
+  v4f facc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = v4i{0, 0, 0, 0};
+      facc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  const int64_t ngroups = d / WG;
 
   const int lrow = tid >> 1;   // 0..127: row this thread stages
   const int lhalf = tid & 1;   // which 16-byte half of the 32-byte step
@@ -164,6 +177,22 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    if constexpr (GROUPED) {
+      if ((kb / ROWB) & 1) {  // the step that completes group kb / (WG / 2)
+        const int64_t grp = kb / (WG / 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = n0 + wn * 64 + j * 16 + r16;
+          const float sg = h2f(w_scales[(col < k ? col : k - 1) * ngroups + grp]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) facc[i][j][e] = __builtin_fmaf((float)acc[i][j][e], sg, facc[i][j][e]);
+            acc[i][j] = v4i{0, 0, 0, 0};
+          }
+        }
+      }
+    }
   }
 
   // C layout of 16x16 MFMA: lane l, element e -> row 4*(l/16) + e, column l % 16
@@ -178,7 +207,10 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = n0 + wn * 64 + j * 16 + r16;
-        if (col < k)
+        if (col >= k) continue;
+        if constexpr (GROUPED)
+          y[row * k + col] = f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa);
+        else
           epilogue_store<AM == kA4 ? 8 : 4>(acc[i][j][e], sa, h2f(w_scales[col]), row * k + col,
                                             y, acc_out, AM == kAU4 ? z * w_sums[col] : 0);
       }
@@ -448,6 +480,100 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
                                           a_scales, w_scales, y, acc_out,
                                           AM == kAU4 ? a_zeros : nullptr,
                                           AM == kAU4 ? w_sums : nullptr);
+}
+
+// ------------------------------------------- decode GEMM, per-group scales
+// A wave's part (segment seg, half h) of the decode tile is the 128 codes
+// 256 seg + 128 h ... + 127, i.e. exactly weight group 2 seg + h: the two
+// MFMAs of the part give the group's integer dot product (times 256), which
+// turns into fp32 with the group's scale.  The scales load with the
+// activation fragments, before the chunk's wait.
+template <int RG>
+__device__ __forceinline__ void dec_mma_chunk_grouped(const DecLane<RG>& t,
+                                                      const unsigned char* wl,
+                                                      const uint8_t* a_src, bool a_ok,
+                                                      int64_t c0,
+                                                      const uint16_t* __restrict__ wg_scales,
+                                                      int64_t ngroups, int64_t k,
+                                                      v4f (&facc)[RG]) {
+  constexpr int SEGB = 16 * RG * DSEG;
+  uint4 av[2][2];
+  uint16_t sc[2][2][RG];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    const int64_t seg = c0 + 2 * t.wave + sl;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      av[sl][h] = make_uint4(0, 0, 0, 0);
+      if (a_ok && seg < t.nseg)
+        av[sl][h] = *reinterpret_cast<const uint4*>(a_src + seg * DSEG + 64 * h);
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        const int64_t col = t.n0 + 16 * q + t.r16;
+        sc[sl][h][q] = 0;
+        if (seg < t.nseg) sc[sl][h][q] = wg_scales[(col < k ? col : k - 1) * ngroups + 2 * seg + h];
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (c0 + 2 * t.wave + sl >= t.nseg) continue;  // uniform per wave
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i a0 = widen(av[sl][h].x, av[sl][h].y), a1 = widen(av[sl][h].z, av[sl][h].w);
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            wl + (2 * t.wave + sl) * SEGB + (16 * q + t.r16) * DSEG +
+            16 * ((4 * h + t.g) ^ (t.r16 & 7)));
+        v4i pg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, widen(w.x, w.y), v4i{0, 0, 0, 0}, 0, 0, 0);
+        pg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, widen(w.z, w.w), pg, 0, 0, 0);
+        const float sg = h2f(sc[sl][h][q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) facc[q][e] = __builtin_fmaf((float)pg[e], sg, facc[q][e]);
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <int RG>
+__global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
+    const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ wg_scales, int64_t m,
+    int64_t k, int64_t d, uint16_t* __restrict__ y) {
+  __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];
+  __shared__ v4f partial[DEC_WAVES][RG][64];
+  const int64_t rowb = d / 2;
+  const DecLane<RG> t = dec_lane<RG>(w_codes, k, rowb, wl);
+  const bool a_ok = t.r16 < m;
+  const uint8_t* a_src = a_codes + (int64_t)(a_ok ? t.r16 : 0) * rowb + 16 * t.g;
+  const int64_t ngroups = d / WG;
+
+  v4f facc[RG];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) facc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
+    dec_issue_w(t, c0);
+    dec_mma_chunk_grouped<RG>(t, wl, a_src, a_ok, c0, wg_scales, ngroups, k, facc);
+  }
+#pragma unroll
+  for (int q = 0; q < RG; ++q) partial[t.wave][q][t.lane] = facc[q];
+  __syncthreads();
+  if (t.wave < RG) {
+    v4f sum = partial[0][t.wave][t.lane];
+#pragma unroll
+    for (int w = 1; w < DEC_WAVES; ++w) sum += partial[w][t.wave][t.lane];
+    const int64_t col = t.n0 + 16 * t.wave + t.r16;
+    if (col < k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = 4 * t.g + e;
+        if (row < m) y[row * k + col] = f2h_rn((sum[e] * (1.0f / 256.0f)) * h2f(a_scales[row]));
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------- fused decode linear
@@ -754,6 +880,51 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 }
 #undef RQ_DMA
 
+// Symmetric INT4 with one scale per group of G elements of fp32 rows: each
+// thread owns 32 consecutive elements, the G / 32 threads of a group meet
+// in a max across neighbouring lanes, and every thread writes its 16 code
+// bytes.  scale = fp16(max / 7) rounded once, code = clamp(rne(x * fp32(1 /
+// scale)), -8, 7).
+template <int G>
+__global__ __launch_bounds__(256) void quantize_groups_kernel(const float* __restrict__ x,
+                                                              int64_t chunks, int64_t n,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint16_t* __restrict__ scales) {
+  constexpr int TPG = G / 32;  // threads per group
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // every lane of a wavefront runs the same number of iterations (the
+  // cross-lane max needs all of them): chunks is padded up to the stride
+  const int64_t trips = (chunks + stride - 1) / stride;
+  for (int64_t it = 0; it < trips; ++it) {
+    const int64_t c = it * stride + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = c < chunks;
+    const int64_t cc = live ? c : chunks - 1;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 f = *reinterpret_cast<const float4*>(x + cc * 32 + 4 * i);
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int off = 1; off < TPG; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const uint16_t hb = scale_fp16<7>(amax);
+    const float mult = (hb == 0 || hb == 0x7C00u) ? 0.0f : 1.0f / h2f(hb);
+    uint32_t wv[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], mult, kMagic), kMagicLo, kMagicHi);
+      wv[i / 8] |= ((f2u(t) & 15u) ^ 8u) << (4 * (i % 8));
+    }
+    if (live) {
+      *reinterpret_cast<uint4*>(codes + cc * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      if (cc % TPG == 0) scales[cc / TPG] = hb;
+    }
+  }
+}
+
 // sums[j] = sum_i qw[j][i] over the packed signed INT4 codes of weight row j
 // (one wavefront per row; an offline companion of the folded weights).
 __global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __restrict__ w_codes,
@@ -782,6 +953,22 @@ __global__ __launch_bounds__(256) void weight_code_sums_kernel(const uint8_t* __
 }
 
 }  // namespace
+
+hipError_t launch_quantize_groups(const float* x, int64_t rows, int64_t n, int group,
+                                  uint8_t* codes, uint16_t* scales, hipStream_t stream) {
+  const int64_t chunks = rows * (n / 32);
+  const int64_t blocks = (chunks + 255) / 256;
+  const int64_t cap = (int64_t)cu_count() * 16;
+  const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
+  switch (group) {
+    case 32: hipLaunchKernelGGL(quantize_groups_kernel<32>, grid, dim3(256), 0, stream, x, chunks, n, codes, scales); break;
+    case 64: hipLaunchKernelGGL(quantize_groups_kernel<64>, grid, dim3(256), 0, stream, x, chunks, n, codes, scales); break;
+    case 128: hipLaunchKernelGGL(quantize_groups_kernel<128>, grid, dim3(256), 0, stream, x, chunks, n, codes, scales); break;
+    case 256: hipLaunchKernelGGL(quantize_groups_kernel<256>, grid, dim3(256), 0, stream, x, chunks, n, codes, scales); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
                                    hipStream_t stream) {
@@ -851,6 +1038,26 @@ hipError_t launch_gemm_variant(const uint8_t* a, const uint16_t* a_scales, const
     const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
     hipLaunchKernelGGL(w4a4_tile_kernel<AM>, grid, dim3(256), 0, stream, a, a_scales, w_codes,
                        w_scales, m, k, d, y, acc, a_zeros, w_sums);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
+                                    const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
+                                    int64_t d, uint16_t* y, hipStream_t stream) {
+  if (m <= 16 && d % (2 * DSEG) == 0) {
+    if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
+      hipLaunchKernelGGL(w4a4_decode_grouped_kernel<2>, dim3((unsigned)((k + 31) / 32)),
+                         dim3(64 * DEC_WAVES), 0, stream, a_codes, a_scales, w_codes, wg_scales, m,
+                         k, d, y);
+    else
+      hipLaunchKernelGGL(w4a4_decode_grouped_kernel<1>, dim3((unsigned)((k + 15) / 16)),
+                         dim3(64 * DEC_WAVES), 0, stream, a_codes, a_scales, w_codes, wg_scales, m,
+                         k, d, y);
+  } else {
+    const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
+    hipLaunchKernelGGL((w4a4_tile_kernel<kA4, true>), grid, dim3(256), 0, stream, a_codes,
+                       a_scales, w_codes, wg_scales, m, k, d, y, nullptr, nullptr, nullptr);
   }
   return hipGetLastError();
 }

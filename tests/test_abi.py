@@ -199,6 +199,22 @@ def test_asym_argument_errors(lib):
     assert gemm(a=MIS) == binding.RQ_ERR_ALIGN
 
 
+def test_grouped_argument_errors(lib):
+    q = lib.rq_quantize_groups
+    assert q(A16, 0, 4096, 128, A16b, A16b, None) == binding.RQ_OK
+    assert q(None, 4, 4096, 128, A16b, A16b, None) == binding.RQ_ERR_NULL
+    assert q(A16, 4, 4096, 96, A16b, A16b, None) == binding.RQ_ERR_SHAPE
+    assert q(A16, 4, 4000, 128, A16b, A16b, None) == binding.RQ_ERR_SHAPE
+    assert q(A16, 4, 64, 128, A16b, A16b, None) == binding.RQ_ERR_SHAPE
+    assert q(MIS, 4, 4096, 128, A16b, A16b, None) == binding.RQ_ERR_ALIGN
+    g = lib.rq_w4a4_gemm_grouped
+    assert g(A16, A16b, 0, A16, A16b, 64, 4096, A16b, None) == binding.RQ_OK
+    assert g(A16, A16b, 4, A16, None, 64, 4096, A16b, None) == binding.RQ_ERR_NULL
+    assert g(A16, A16b, 4, A16, A16b, 64, 192, A16b, None) == binding.RQ_ERR_SHAPE
+    assert g(A16, A16b, 4, A16, A16b, 0, 4096, A16b, None) == binding.RQ_ERR_SHAPE
+    assert g(MIS, A16b, 4, A16, A16b, 64, 4096, A16b, None) == binding.RQ_ERR_ALIGN
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

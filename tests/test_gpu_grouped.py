@@ -1,0 +1,142 @@
+"""GPU parity of per-group INT4 weight scales (group 128): rq_quantize_groups
+and rq_w4a4_gemm_grouped through the C ABI against the CPU oracle.
+
+Codes: the kernel rounds x * fp32(1/scale), the oracle x / scale in float64;
+the pre-round values differ by at most 2^-24 |v| <= 4.5e-7 (|v| <= 7.5), so
+codes must match except within the 1e-6 band, and scales bit for bit.  GEMM:
+the per-group integer dot products are exact; the sum over groups is fp32, so
+y is held to 1e-2 relative plus the fp32 summation bound
+2^-17 * sa * sum_g |sw_g acc_g| (64 ulps of the absolute sum).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import rq_oracle as O
+from rotation_w4a4_quantization_amd import datagen
+from tests.parity import BAND, Y_TOL, dist_to_half_integer
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rq():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import rotation_w4a4_quantization_amd as rq
+    rq.load_library()
+    return rq
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def check_groups(x, group, codes, scales, what):
+    q_ref, s_ref, v = O.quantize_groups(x, group)
+    assert np.array_equal(scales.view(np.uint16), s_ref.view(np.uint16)), f"{what}: scales differ"
+    q = O.unpack_int4(codes)
+    bad = q != q_ref
+    if bad.any():
+        assert np.all(np.abs(q[bad].astype(np.int16) - q_ref[bad]) == 1), f"{what}: code off by >1"
+        assert np.all(dist_to_half_integer(v[bad]) <= BAND), f"{what}: mismatch outside the band"
+    return int(bad.sum())
+
+
+def check_gemm_grouped(ac, sa, wc, sw, y, what):
+    y_ref, acc = O.w4a4_gemm_grouped(ac, sa, wc, sw)
+    k = wc.shape[0]
+    ng = acc.shape[-1]
+    absum = np.abs(acc.astype(np.float64) * sw.astype(np.float64).reshape(k, ng)[None]).sum(-1)
+    bound = 2.0 ** -17 * sa.astype(np.float64)[:, None] * absum
+    yr, yg = y_ref.astype(np.float64), y.astype(np.float64)
+    both_inf = np.isinf(yr) & np.isinf(yg) & (np.sign(yr) == np.sign(yg))
+    ok = (np.abs(yg - yr) <= Y_TOL * np.maximum(np.abs(yr), 2.0 ** -14) + bound) | both_inf
+    assert ok.all(), f"{what}: {int((~ok).sum())} outputs outside the tolerance"
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+def test_quantize_groups_random_rows(rq, group):
+    rng = np.random.default_rng(1000 + group)
+    rows, n = 37, 1024
+    x = (rng.standard_normal((rows, n)) * np.repeat(10.0 ** rng.uniform(-3, 1, (rows, n // group)), group, 1)).astype(np.float32)
+    x[0, :group] = 0.0                    # a zero group
+    x[1, :group] = 1e-9                   # a group whose scale underflows
+    x[2, :4] = [3e-5, -3e-5, 1e-5, 0.0]   # an fp16-subnormal scale in group 0
+    x[2, 4:group] = 0.0
+    say(f"quantize_groups group={group}")
+    c, s = rq.quantize_groups(dev(x), group)
+    torch.cuda.synchronize()
+    check_groups(x, group, host(c), host(s), f"groups {group}")
+
+
+def test_fold_weights_grouped_decode_weights(rq):
+    dec = datagen.decode_linear(0)
+    for k, wt in dec["wts"].items():
+        say(f"fold grouped {k}x4096")
+        c, s = rq.fold_weights_grouped(dev(wt), dev(dec["signs"]), 128)
+        torch.cuda.synchronize()
+        w_rot = O.rotate(wt, dec["signs"], "f32")
+        check_groups(w_rot, 128, host(c), host(s), f"fold grouped {k}")
+
+
+GROUPED_SHAPES = [(1, 1, 256), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
+                  (5, 33, 384), (17, 33, 128), (130, 129, 256), (300, 260, 1024)]
+
+
+@pytest.mark.parametrize("m,k,d", GROUPED_SHAPES)
+def test_w4a4_gemm_grouped_random_codes(rq, m, k, d):
+    rng = np.random.default_rng(m * 1000 + k + d + 32)
+    ac = datagen.random_codes(rng, m, d)
+    wc = datagen.random_codes(rng, k, d)
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k * (d // 128)).reshape(k, d // 128)
+    say(f"grouped gemm m={m} k={k} d={d}")
+    y = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw))
+    torch.cuda.synchronize()
+    check_gemm_grouped(ac, sa, wc, sw, host(y), f"grouped {m}x{k}x{d}")
+    y2 = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw))
+    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
+
+
+def test_grouped_equal_scales_match_per_channel(rq):
+    # equal group scales in a row: the grouped GEMM is the per-channel GEMM
+    # up to fp32 summation order; with power-of-two scales every product and
+    # partial sum is exact, so the two agree bit for bit
+    rng = np.random.default_rng(33)
+    m, k, d = 4, 64, 4096
+    ac = datagen.random_codes(rng, m, d)
+    wc = datagen.random_codes(rng, k, d)
+    sa = (2.0 ** rng.integers(-12, -6, m)).astype(np.float16)
+    sw1 = (2.0 ** rng.integers(-12, -6, k)).astype(np.float16)
+    say("grouped vs per-channel")
+    yg = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(np.repeat(sw1[:, None], d // 128, 1)))
+    yc, _ = rq.w4a4_gemm(dev(ac), dev(sa), dev(wc), dev(sw1))
+    assert np.array_equal(host(yg).view(np.uint16), host(yc).view(np.uint16))
+
+
+def test_grouped_decode_linear_end_to_end(rq):
+    dec = datagen.decode_linear(0)
+    s = dev(dec["signs"])
+    ac, sa, _ = rq.fwht_quant(dev(dec["x"]), s)
+    for k, wt in dec["wts"].items():
+        wc, ws = rq.fold_weights_grouped(dev(wt), s, 128)
+        for m in (1, 4, 16):
+            say(f"grouped decode linear m={m} k={k}")
+            y = rq.w4a4_gemm_grouped(ac[:m].contiguous(), sa[:m].contiguous(), wc, ws)
+            torch.cuda.synchronize()
+            check_gemm_grouped(host(ac[:m]), host(sa[:m]), host(wc), host(ws), host(y),
+                               f"grouped decode m={m} k={k}")
