@@ -45,6 +45,8 @@ on tiny inputs, worked examples from the pages).
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -70,6 +72,9 @@ __all__ = [
     "w4a4_gemm_asym",
     "quantize_groups",
     "w4a4_gemm_grouped",
+    "inverse_rotate",
+    "decode_attention",
+    "decode_attention_int4",
 ]
 
 QMIN, QMAX = -8, 7
@@ -589,3 +594,69 @@ def w4a4_gemm_grouped(a_codes: np.ndarray, a_scales: np.ndarray, w_codes: np.nda
     sa = np.asarray(a_scales).astype(np.float64)
     y = fp16_rne(sa[:, None] * np.einsum("mkg,kg->mk", acc.astype(np.float64), sw))
     return y, acc
+
+
+# ------------------------------------------- attention over the INT4 KV cache
+def inverse_rotate(y: np.ndarray, signs: np.ndarray | None) -> np.ndarray:
+    """y R^T for R = diag(s) H_n / sqrt(n) (float64): H is symmetric, so
+    y R^T = (y H_n / sqrt(n)) * s, the transform that undoes :func:`rotate`
+    ([RQ] "The Principle of Computational Invariance": R R^T = I)."""
+    y = np.asarray(y, dtype=np.float64)
+    n = y.shape[-1]
+    out = hadamard_transform(y) / math.sqrt(n)
+    if signs is not None:
+        out = out * np.asarray(signs).astype(np.float64)
+    return out
+
+
+def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, lengths=None,
+                     sm_scale: float | None = None) -> np.ndarray:
+    """Single-token (decode) attention, the plain definition in float64.
+
+    q [B, Hq, D] (the new token's queries), k, v [B, H, S, D] (the cache);
+    query head j reads KV head j // (Hq / H) (grouped-query attention).  For
+    batch entry b only positions < lengths[b] take part (all S when lengths
+    is None); a length of 0 gives a zero output.
+    o = softmax(q k^T * sm_scale) v with sm_scale = 1 / sqrt(D) by default.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, D = q.shape
+    H, S = k.shape[1], k.shape[2]
+    if Hq % H:
+        raise ValueError("query heads must be a multiple of the KV heads")
+    group = Hq // H
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = S if lengths is None else int(lengths[b])
+        if L == 0:
+            continue
+        for j in range(Hq):
+            h = j // group
+            scores = k[b, h, :L] @ q[b, j] * scale
+            p = np.exp(scores - scores.max())
+            out[b, j] = (p / p.sum()) @ v[b, h, :L]
+    return out
+
+
+def decode_attention_int4(q: np.ndarray, k_codes: np.ndarray, k_scales: np.ndarray,
+                          v_codes: np.ndarray, v_scales: np.ndarray, signs: np.ndarray | None,
+                          lengths=None, sm_scale: float | None = None) -> dict:
+    """Decode attention that reads the 4-bit rotated KV cache.
+
+    [QuaRot] "End-to-end flow" (a later token's attention reads the
+    four-bit rotated cache; rotation invariance keeps the scores) and
+    [RQ] "The Principle of Computational Invariance" (q k^T = (qR)(kR)^T).
+    The cache holds rotated, quantised rows (:func:`kv_rotate_quant`:
+    codes [B, H, S, D/2], scales [B, H, S]); the query is rotated with the
+    same R, attention runs on the dequantised cache in the rotated basis, and
+    the output is rotated back: o = softmax(q~ K^_rot^T * sm_scale) V^_rot R^T.
+    Returns {"o": o, "o_rot": output before the inverse rotation, "q_rot"}.
+    """
+    kh = dequantize(unpack_int4(k_codes), k_scales)
+    vh = dequantize(unpack_int4(v_codes), v_scales)
+    q_rot = rotate(np.asarray(q), signs, "f64")
+    o_rot = decode_attention(q_rot, kh, vh, lengths, sm_scale)
+    return {"o": inverse_rotate(o_rot, signs), "o_rot": o_rot, "q_rot": q_rot}

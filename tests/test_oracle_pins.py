@@ -758,3 +758,97 @@ def test_groups_cut_weight_error_when_group_ranges_differ():
     eg = np.abs(np.repeat(sg.astype(np.float64), 128, axis=1) * qg - w).mean()
     ec = np.abs(sc.astype(np.float64)[:, None] * qc - w).mean()
     assert eg < 0.5 * ec
+
+
+# ------------------------------------ attention over the 4-bit cache (f3)
+
+def _attn_loops(q, k, v, lengths, sm):
+    """Decode attention by explicit Python loops (tiny sizes)."""
+    B, Hq, D = q.shape
+    H, S = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = S if lengths is None else lengths[b]
+        for j in range(Hq):
+            h = j // (Hq // H)
+            if L == 0:
+                continue
+            sc = [sum(q[b, j, i] * k[b, h, t, i] for i in range(D)) * sm for t in range(L)]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            tot = sum(e)
+            for i in range(D):
+                out[b, j, i] = sum(e[t] * v[b, h, t, i] for t in range(L)) / tot
+    return out
+
+
+def test_inverse_rotate_undoes_rotate():
+    rng = np.random.default_rng(50)
+    for n in (4, 128):
+        x = rng.standard_normal((3, n))
+        signs = datagen.rademacher(rng, n)
+        for s in (signs, None):
+            np.testing.assert_allclose(O.inverse_rotate(O.rotate(x, s, "f64"), s), x, atol=1e-13)
+        # and against the explicit matrix: R = diag(s) H / sqrt(n), y R^T
+        h = sylvester_block(n).astype(np.float64)
+        r = np.diag(signs.astype(np.float64)) @ h / math.sqrt(n)
+        y = rng.standard_normal((2, n))
+        np.testing.assert_allclose(O.inverse_rotate(y, signs), y @ r.T, atol=1e-13)
+
+
+def test_decode_attention_brute_force_gqa_and_lengths():
+    rng = np.random.default_rng(51)
+    B, H, G, S, D = 2, 2, 3, 5, 4
+    q = rng.standard_normal((B, H * G, D))
+    k = rng.standard_normal((B, H, S, D))
+    v = rng.standard_normal((B, H, S, D))
+    lengths = [3, 0]
+    got = O.decode_attention(q, k, v, lengths, 0.7)
+    np.testing.assert_allclose(got, _attn_loops(q, k, v, lengths, 0.7), atol=1e-13)
+    np.testing.assert_allclose(O.decode_attention(q, k, v, None),
+                               _attn_loops(q, k, v, None, 1 / math.sqrt(D)), atol=1e-13)
+    # a single position returns its value row; a zero query averages the values
+    one = O.decode_attention(q, k[:, :, :1], v[:, :, :1])
+    np.testing.assert_allclose(one, np.repeat(v[:, :, 0], G, axis=1), atol=1e-14)
+    avg = O.decode_attention(np.zeros_like(q), k, v)
+    np.testing.assert_allclose(avg, np.repeat(v.mean(axis=2), G, axis=1), atol=1e-14)
+
+
+def test_decode_attention_int4_is_exact_on_grid_representable_caches():
+    # Build caches whose rotated rows lie exactly on the INT4 grid
+    # (k~ = codes * scale), set K = K~ R^T; then the INT4 path (dequantise in
+    # the rotated basis, rotate q, rotate the output back) must equal plain
+    # attention on K, V: rotation invariance, the GQA head mapping and the
+    # inverse rotation all enter.
+    rng = np.random.default_rng(52)
+    B, H, G, S, D = 2, 2, 2, 6, 128
+    signs = datagen.rademacher(rng, D)
+    caches = {}
+    for name in ("k", "v"):
+        qc = rng.integers(-8, 8, (B, H, S, D))
+        sc = rng.uniform(0.01, 0.2, (B, H, S)).astype(np.float16)
+        caches[name] = (O.pack_int4(qc), sc, O.inverse_rotate(O.dequantize(qc, sc), signs))
+    q = rng.standard_normal((B, H * G, D))
+    lengths = [6, 4]
+    r = O.decode_attention_int4(q, caches["k"][0], caches["k"][1], caches["v"][0], caches["v"][1],
+                                signs, lengths)
+    ref = O.decode_attention(q, caches["k"][2], caches["v"][2], lengths)
+    np.testing.assert_allclose(r["o"], ref, atol=1e-11)
+
+
+def test_rotated_int4_cache_attention_beats_unrotated():
+    # Outlier channels in K and V: the rotated 4-bit cache keeps attention
+    # closer to full precision than a 4-bit cache of the raw rows.
+    rng = np.random.default_rng(53)
+    kv = datagen.kv_cache(0, batch=1, heads=2, seq=256)
+    k, v = kv["k"].astype(np.float64), kv["v"].astype(np.float64)
+    q = rng.standard_normal((1, 8, 128))
+    ref = O.decode_attention(q, k, v)
+    r = O.kv_rotate_quant(kv["k"], kv["v"], None)
+    rot = O.decode_attention_int4(q, r["k_codes"], r["k_scales"], r["v_codes"], r["v_scales"], None)["o"]
+    kq, ks, _ = O.quantize_rows(k)
+    vq, vs, _ = O.quantize_rows(v)
+    raw = O.decode_attention(q, O.dequantize(kq, ks), O.dequantize(vq, vs))
+    e_rot = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
+    e_raw = np.linalg.norm(raw - ref) / np.linalg.norm(ref)
+    assert e_rot < 0.5 * e_raw, (e_rot, e_raw)
