@@ -498,6 +498,24 @@ def main():
                                                     "GB/s": round(b / (mk * 1e-3) / 1e9, 1),
                                                     "hbm_frac": round(b / (mk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"[bench] kv: {sec['kv_rotate_quant_32x8x4096x128']}")
+            # decode attention reading that cache: 4 query heads per KV head
+            B_, H_, S_, G_ = 32, 8, 4096, 4
+            kc4, ks4 = kc.view(B_, H_, S_, 64), ks.view(B_, H_, S_)
+            vc4, vs4 = vc.view(B_, H_, S_, 64), vs.view(B_, H_, S_)
+            qa = torch.from_numpy(np.random.default_rng(5).standard_normal(
+                (B_, H_ * G_, 128)).astype(np.float16)).to(dev)
+            oa = torch.empty_like(qa)
+            wsa = rq.decode_attention_workspace(B_, H_, G_, S_, dev)
+
+            def fat(i):
+                rq.decode_attention(qa, kc4, ks4, vc4, vs4, None, workspace=wsa, out=oa)
+
+            mat = time_launches(torch, fat, 1, max(5, steps2 // 2), warm2)
+            ba = B_ * H_ * S_ * (64 + 64 + 2 + 2) + 2 * (B_ * H_ * G_ * 128 * 2)
+            sec["decode_attention_32x8x4096_g4"] = {
+                "us": round(mat * 1e3, 2), "GB/s": round(ba / (mat * 1e-3) / 1e9, 1),
+                "hbm_frac": round(ba / (mat * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] decode attention: {sec['decode_attention_32x8x4096_g4']}")
             del kt, vt
     result["secondary"] = sec
 

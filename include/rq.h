@@ -360,6 +360,52 @@ int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64
                          const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
                          int64_t d, uint16_t* y, void* stream);
 
+/*
+ * rq_decode_attention_workspace_size -- bytes of device workspace that
+ * rq_decode_attention needs for this shape on the current device (one
+ * fp32 record of 132 values per query head and split of the cache).
+ */
+size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64_t group,
+                                          int64_t seq);
+
+/*
+ * rq_decode_attention -- single-token attention that reads the 4-bit rotated
+ * KV cache written by rq_kv_rotate_quant.
+ *
+ * [QuaRot] "End-to-end flow" (a later token's attention reads the four-bit
+ * rotated cache; rotation invariance keeps the scores) and [RQ] "The
+ * Principle of Computational Invariance" (q k^T = (q R)(k R)^T).  For batch
+ * entry b and query head j (KV head h = j / group):
+ *   q~ = q R with the cache's rotation R = diag(signs) H_128 / sqrt(128),
+ *   s_t = (q~ . k^_t) * sm_scale for t < len_b, k^_t = code_t * kscale_t,
+ *   p = softmax(s), o = (sum_t p_t v^_t) R^T.
+ * The scores use f16 MFMA on the exact key codes with the query split into
+ * two f16 parts (about 22 significant bits) and fp32 accumulation; the
+ * weighted sum, the softmax and the inverse rotation are fp32.  A length of
+ * 0 gives a zero output.
+ *
+ *   q          [batch][kv_heads * group][128] fp16 queries of the new token,
+ *              16-byte aligned.
+ *   k_codes, v_codes    [batch][kv_heads][seq][64] uint8 (rq_kv_rotate_quant),
+ *              16-byte aligned; k_scales, v_scales [batch][kv_heads][seq] fp16.
+ *   lengths    optional device int32 [batch] valid positions per entry
+ *              (values are clamped to [0, seq]); NULL means seq for all.
+ *   batch >= 0; kv_heads >= 1; 1 <= group <= 8; seq >= 1;
+ *   batch * kv_heads <= 65535; head_dim must be 128.
+ *   signs      the [128] int8 +-1 signs the cache was rotated with, or NULL.
+ *   sm_scale   softmax scale (> 0), normally 1 / sqrt(128).
+ *   out        [batch][kv_heads * group][128] fp16 output; out_f32 optional
+ *              fp32 copy (debug) or NULL.
+ *   workspace  device memory of at least rq_decode_attention_workspace_size
+ *              bytes, 16-byte aligned (any contents; calls that may overlap
+ *              in time need separate workspaces).
+ */
+int rq_decode_attention(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                        const uint8_t* v_codes, const uint16_t* v_scales, const int32_t* lengths,
+                        int64_t batch, int64_t kv_heads, int64_t group, int64_t seq,
+                        int64_t head_dim, const int8_t* signs, float sm_scale, uint16_t* out,
+                        float* out_f32, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for an rq_status value (static storage, never NULL). */
 const char* rq_status_string(int status);
 

@@ -9,6 +9,8 @@ binds it.  ``datagen`` holds the seeded synthetic input generators.
 from .binding import (  # noqa: F401
     EXPORTED,
     RQError,
+    decode_attention,
+    decode_attention_workspace,
     fold_weights,
     fold_weights_grouped,
     fwht_quant,

@@ -34,6 +34,8 @@ EXPORTED = (
     "rq_w4a4_gemm_asym",
     "rq_quantize_groups",
     "rq_w4a4_gemm_grouped",
+    "rq_decode_attention_workspace_size",
+    "rq_decode_attention",
     "rq_status_string",
     "rq_version",
 )
@@ -86,6 +88,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_quantize_groups.restype = i32
     lib.rq_w4a4_gemm_grouped.argtypes = [p, p, i64, p, p, i64, i64, p, p]
     lib.rq_w4a4_gemm_grouped.restype = i32
+    lib.rq_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.rq_decode_attention_workspace_size.restype = sz
+    lib.rq_decode_attention.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, p,
+                                        ctypes.c_float, p, p, p, sz, p]
+    lib.rq_decode_attention.restype = i32
     lib.rq_status_string.argtypes = [i32]
     lib.rq_status_string.restype = ctypes.c_char_p
     lib.rq_version.argtypes = []
@@ -408,3 +415,50 @@ def w4a4_gemm_grouped(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: to
                                              _ptr(w_group_scales), k, d, _ptr(y), _stream())
     _check("rq_w4a4_gemm_grouped", st)
     return y
+
+
+def decode_attention_workspace(batch: int, kv_heads: int, group: int, seq: int,
+                               device) -> torch.Tensor:
+    """A workspace for decode_attention (reusable across calls that do not
+    overlap in time)."""
+    nbytes = int(load_library().rq_decode_attention_workspace_size(batch, kv_heads, group, seq))
+    return torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
+
+
+def decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                     v_codes: torch.Tensor, v_scales: torch.Tensor,
+                     signs: torch.Tensor | None = None, lengths: torch.Tensor | None = None,
+                     sm_scale: float | None = None, debug: bool = False,
+                     workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """rq_decode_attention: q fp16 [B, H * G, 128] against the 4-bit rotated
+    cache (codes [B, H, S, 64], scales [B, H, S] from kv_rotate_quant).
+    Returns (out fp16 [B, H * G, 128], out fp32 or None)."""
+    for name, t in (("q", q), ("k_codes", k_codes), ("k_scales", k_scales),
+                    ("v_codes", v_codes), ("v_scales", v_scales)):
+        _need_cuda(name, t)
+    if q.dtype != torch.float16 or q.dim() != 3 or q.shape[-1] != 128:
+        raise ValueError("q must be float16 [batch, query_heads, 128]")
+    if k_codes.dtype != torch.uint8 or k_codes.dim() != 4 or k_codes.shape[-1] != 64:
+        raise ValueError("k_codes must be uint8 [batch, kv_heads, seq, 64]")
+    if v_codes.shape != k_codes.shape or k_scales.shape != k_codes.shape[:3] or \
+            v_scales.shape != k_codes.shape[:3]:
+        raise ValueError("cache shapes do not match")
+    B, H, S, _ = k_codes.shape
+    if q.shape[0] != B or q.shape[1] % H:
+        raise ValueError("query heads must be a multiple of the KV heads")
+    G = q.shape[1] // H
+    s = _signs(signs, 128, q.device)
+    if lengths is not None:
+        _need_cuda("lengths", lengths)
+        if lengths.dtype != torch.int32 or lengths.numel() != B:
+            raise ValueError("lengths must be int32 [batch]")
+    ws = workspace if workspace is not None else decode_attention_workspace(B, H, G, S, q.device)
+    y = out if out is not None else torch.empty_like(q)
+    y32 = torch.empty(q.shape, dtype=torch.float32, device=q.device) if debug else None
+    scale = (1.0 / 128 ** 0.5) if sm_scale is None else float(sm_scale)
+    st = load_library().rq_decode_attention(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                            _ptr(v_scales), _ptr(lengths), B, H, G, S, 128, _ptr(s),
+                                            scale, _ptr(y), _ptr(y32), _ptr(ws), ws.numel(),
+                                            _stream())
+    _check("rq_decode_attention", st)
+    return y, y32

@@ -209,6 +209,36 @@ int rq_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* sign
                                            static_cast<hipStream_t>(stream)));
 }
 
+size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64_t group,
+                                          int64_t seq) {
+  if (batch < 1 || kv_heads < 1 || group < 1 || seq < 1) return 0;
+  return rq::decode_attention_workspace_bytes(batch, kv_heads, group, seq);
+}
+
+int rq_decode_attention(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                        const uint8_t* v_codes, const uint16_t* v_scales, const int32_t* lengths,
+                        int64_t batch, int64_t kv_heads, int64_t group, int64_t seq,
+                        int64_t head_dim, const int8_t* signs, float sm_scale, uint16_t* out,
+                        float* out_f32, void* workspace, size_t workspace_bytes, void* stream) {
+  if (head_dim != 128) return RQ_ERR_SHAPE;
+  if (batch < 0 || kv_heads < 1 || kv_heads > 65535 || group < 1 || group > 8 || seq < 1)
+    return RQ_ERR_SHAPE;
+  if (batch * kv_heads > 65535 || seq >= kMaxRows) return RQ_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return RQ_ERR_SHAPE;
+  if (batch == 0) return RQ_OK;
+  if (q == nullptr || k_codes == nullptr || k_scales == nullptr || v_codes == nullptr ||
+      v_scales == nullptr || out == nullptr || workspace == nullptr)
+    return RQ_ERR_NULL;
+  if (workspace_bytes < rq::decode_attention_workspace_bytes(batch, kv_heads, group, seq))
+    return RQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(workspace))
+    return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_decode_attention(q, k_codes, k_scales, v_codes, v_scales, lengths,
+                                              batch, kv_heads, group, seq, signs, sm_scale, out,
+                                              out_f32, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* rq_status_string(int status) {
   switch (status) {
     case RQ_OK: return "ok";

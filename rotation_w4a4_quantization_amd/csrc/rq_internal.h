@@ -61,6 +61,17 @@ hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_sc
                                     const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
                                     int64_t d, uint16_t* y, hipStream_t stream);
 
+// Decode attention over the 4-bit rotated KV cache (head_dim 128, G <= 8
+// query heads per KV head); the workspace holds one (max, sum, output)
+// record per split and query.
+size_t decode_attention_workspace_bytes(int64_t batch, int64_t kv_heads, int64_t group,
+                                        int64_t seq);
+hipError_t launch_decode_attention(const uint16_t* q, const uint8_t* kc, const uint16_t* ks,
+                                   const uint8_t* vc, const uint16_t* vs, const int32_t* lengths,
+                                   int64_t B, int64_t H, int64_t G, int64_t S,
+                                   const int8_t* signs, float sm_scale, uint16_t* out,
+                                   float* out_f32, void* workspace, hipStream_t stream);
+
 // Fused decode linear (m <= 16, fp16 x, d in 512..8192 a power of two):
 // rotation + INT4 quantisation of x as the prologue of the decode GEMM.
 size_t linear_decode_workspace_bytes(int64_t m, int64_t d);

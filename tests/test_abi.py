@@ -215,6 +215,30 @@ def test_grouped_argument_errors(lib):
     assert g(MIS, A16b, 4, A16, A16b, 64, 4096, A16b, None) == binding.RQ_ERR_ALIGN
 
 
+def test_decode_attention_argument_errors(lib):
+    need = lib.rq_decode_attention_workspace_size(2, 8, 4, 4096)
+    assert need > 0 and need % 16 == 0
+
+    def call(q=A16, kc=A16, ks=A16b, vc=A16, vs=A16b, lens=None, B=2, H=8, G=4, S=4096, D=128,
+             signs=None, sm=0.088, out=A16b, out32=None, ws=A16b, nbytes=need):
+        return lib.rq_decode_attention(q, kc, ks, vc, vs, lens, B, H, G, S, D, signs, sm, out,
+                                       out32, ws, nbytes, None)
+
+    assert call(B=0) == binding.RQ_OK
+    assert call(D=64) == binding.RQ_ERR_SHAPE
+    assert call(G=9) == binding.RQ_ERR_SHAPE
+    assert call(G=0) == binding.RQ_ERR_SHAPE
+    assert call(S=0) == binding.RQ_ERR_SHAPE
+    assert call(sm=0.0) == binding.RQ_ERR_SHAPE
+    assert call(sm=float("nan")) == binding.RQ_ERR_SHAPE
+    assert call(nbytes=need - 1) == binding.RQ_ERR_SHAPE
+    assert call(B=65536, H=1) == binding.RQ_ERR_SHAPE
+    assert call(q=None) == binding.RQ_ERR_NULL
+    assert call(ws=None) == binding.RQ_ERR_NULL
+    assert call(kc=MIS) == binding.RQ_ERR_ALIGN
+    assert call(q=MIS) == binding.RQ_ERR_ALIGN
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
