@@ -38,19 +38,42 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+# Extra flags per source.  The attention kernel keeps its MFMA accumulators
+# in VGPRs (its loop also scales them with VALU instructions; in AGPRs the
+# compiler copies them back and forth every iteration).
+FILE_FLAGS = {"decode_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object (in parallel), then link librq.so."""
+    objdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    noise = "is not a recognized feature for this target"
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-shared"], *FILE_FLAGS.get(src, []),
+               "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.PIPE, text=True)))
+    objs = []
+    for src, obj, pr in procs:
+        _, err = pr.communicate()
+        err = "\n".join(l for l in err.splitlines() if noise not in l)
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({pr.returncode}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        objs.append(obj)
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

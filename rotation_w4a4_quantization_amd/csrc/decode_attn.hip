@@ -15,15 +15,19 @@
 //
 // Work split (flash-decoding): workgroup (split, b*H + h) covers one chunk of
 // positions for the G query heads of KV head h; its 4 wavefronts take 16-
-// position tiles in turn and keep their own running max / sum / output.
-//   * Scores: S^T = K Q~^T on the f16 MFMA 16x16x32.  A key row (64 bytes of
-//     codes) is contiguous, so a lane loads 16 bytes and converts 8 nibbles
-//     per k-step to f16 exactly (1024 + code' - 1032).  The query is split
-//     into f16 hi + lo (about 22 significant bits) and both products
-//     accumulate in fp32, so the scores keep fp32-level accuracy.
-//   * The output: v^ is position-major, so the weighted sum runs on the VALU
-//     with lanes owning head dimensions (lane L: 8 dimensions, one of 4
-//     position slots), nibbles converted with v_cvt_f32_ubyte.
+// position tiles in turn and keep their own running max / sums / output.
+//   * Codes become f16 operands exactly, as the subnormals code * 2^-24
+//     (two masks, v_perm and a packed f16 subtraction per 8 codes); the MFMA
+//     keeps subnormal products exact, and the 2^-24 comes out per query.
+//   * Scores: S^T = K Q~^T on the f16 MFMA 16x16x32.  A key row (64 bytes)
+//     is contiguous, so a lane loads 16 bytes for 4 k-steps.  The query, with
+//     the softmax scale and log2(e), is split into f16 hi + lo (about 22
+//     significant bits); both products accumulate in fp32.
+//   * Output: o~^T = V^T (p vscale)^T on the f16 MFMA 16x16x16.  The value
+//     tile goes to LDS as f16 rows; ds_read_b64_tr_b16 reads it transposed
+//     (positions along k), and the weights p * vscale (hi + lo) are the other
+//     operand straight from the score layout.  The running output is
+//     rescaled only when some running max moved.
 // A second kernel merges the splits' (max, sum, output) records and applies
 // the inverse rotation.
 #include <hip/hip_fp16.h>
@@ -37,12 +41,15 @@ namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f_a __attribute__((ext_vector_type(4)));
 
 constexpr int AD = 128;          // head dimension
 constexpr int AW = 4;            // wavefronts per workgroup
 constexpr int AT = 16;           // positions per wavefront step
 constexpr int PREC = AD + 4;     // floats per split record: m, l, 2 pad, o~[128]
+constexpr int VPITCH = AD + 8;   // f16 row pitch of the value tile (272 bytes: rows start in different banks)
 constexpr float kNegInf = -__builtin_inff();
 
 // Sum / max with the lane 16 and lane 32 apart (lane bits 4 and 5).
@@ -63,26 +70,31 @@ __device__ __forceinline__ float pair32_max(float x) {
   return fmaxf(u2f(a[0]), u2f(a[1]));
 }
 
-// 8 two's-complement nibbles (dims 0..7 of a word) as f16 in the order
-// 0, 4, 1, 5, 2, 6, 3, 7: (w' >> 4k) & 0x000F000F puts nibbles k and k + 4
-// in the two halves, 0x6400 makes them 1024 + code', and 1032 is subtracted.
+// 8 two's-complement nibbles (dims 0..7 of a word, in order) as the exact
+// f16 subnormals code * 2^-24.  lo / hi hold the even / odd nibbles plus 8
+// as bytes; v_perm interleaves them with zero bytes into the f16 bit
+// patterns 0x00nn = (code + 8) * 2^-24, and a packed f16 subtraction of
+// 8 * 2^-24 (exact: f16 denormals are kept) leaves code * 2^-24.  The MFMA
+// products are exact for subnormal inputs as well; the kernel takes the 2^-24
+// out per query.
 __device__ __forceinline__ v8h nibbles_f16(uint32_t w) {
   const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  const _Float16 eight = __builtin_bit_cast(_Float16, (uint16_t)8);  // 8 * 2^-24
   v8h r;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t pair = ((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
-    v2h h = __builtin_bit_cast(v2h, pair) - v2h{(_Float16)1032.0f, (_Float16)1032.0f};
+    const v2h h = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * k)) -
+                  v2h{eight, eight};
     r[2 * k] = h[0];
     r[2 * k + 1] = h[1];
   }
   return r;
 }
+constexpr float kTwo24 = 16777216.0f;
 
 // Head dimension of element e of a k-step-t operand in lane group g.
-__device__ __forceinline__ int qk_dim(int g, int t, int e) {
-  return 32 * g + 8 * t + ((e & 1) << 2) + (e >> 1);
-}
+__device__ __forceinline__ int qk_dim(int g, int t, int e) { return 32 * g + 8 * t + e; }
 
 template <int GM, bool HAS_SIGNS>
 __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
@@ -90,10 +102,9 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const int32_t* __restrict__ lengths, int H, int G, int64_t S, int64_t chunk, float qscale,
     const int8_t* __restrict__ signs, float* __restrict__ part) {
-  __shared__ float qs[GM][AD];            // rotated queries
-  __shared__ float pt[AW][AT][GM];        // p * vscale of the wavefront's tile, [position][query]
-  __shared__ float ar[AW][GM];            // rescale factor of the tile, per query
-  __shared__ float red[AW][GM][PREC];     // per-wavefront (m, l, o~) records
+  __shared__ float qs[GM][AD];                                  // rotated queries
+  __shared__ __align__(16) _Float16 vt[AW][AT][VPITCH];         // the tile's values, f16
+  __shared__ float red[AW][GM][PREC];                           // per-wavefront records
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -131,55 +142,66 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     __syncthreads();
   }
 
-  // ---- MFMA B operand (Q~^T): lane (query r16, group g), k-step t holds the
-  // dims qk_dim(g, t, .) of q~ * qscale as f16 hi + lo
+  // ---- MFMA B operand of the scores (Q~^T): lane (query r16, group g),
+  // k-step t holds the dims qk_dim(g, t, .) of q~ * qscale as f16 hi + lo
   v8h qh[4], ql[4];
+  const int qrow = r16 < G ? r16 : 0;
+  const float qmask = r16 < G ? qscale : 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = r16 < G ? qs[r16][qk_dim(g, t, e)] * qscale : 0.0f;
+      const float v = qs[qrow][qk_dim(g, t, e)] * qmask;
       const _Float16 hv = (_Float16)v;
       qh[t][e] = hv;
       ql[t][e] = (_Float16)(v - (float)hv);
     }
 
-  // ---- per-wavefront running state
-  float m_run = kNegInf, l_run = 0.0f;  // of query r16 (score layout)
-  float o[GM][8], corr[GM];             // output dims 8 (lane & 15) .., slot lane >> 4
+  // ---- per-wavefront running state, all in the layout of query r16
+  float m_run = kNegInf, l_run = 0.0f;
+  v4f_a acc[AD / 16];  // o~^T: m-tile mt, element e = value column 16 mt + 4 g + e
 #pragma unroll
-  for (int qi = 0; qi < GM; ++qi) {
-    corr[qi] = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[qi][d] = 0.0f;
-  }
-  const int slot = lane >> 4, dblk = lane & 15;
-  const uint8_t* kbase = kc + bh * S * (AD / 2);
-  const uint8_t* vbase = vc + bh * S * (AD / 2);
+  for (int mt = 0; mt < AD / 16; ++mt) acc[mt] = v4f_a{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* kbase = kc + bh * S * (AD / 2) + 16 * g;
+  const uint8_t* vbase = vc + bh * S * (AD / 2) + 16 * g;
   const uint16_t* ksb = ks + bh * S;
   const uint16_t* vsb = vs + bh * S;
+  const bool sc_vec = (S & 3) == 0;  // 8-byte scale loads stay aligned
+  _Float16* vrow = &vt[wave][r16][32 * g];
+  // transposing read of the value tile: lane (j, g) points at row 4 g + j / 4,
+  // column 4 (j % 4) of each 16-column block
+  const _Float16* vtr = &vt[wave][4 * g + (r16 >> 2)][4 * (r16 & 3)];
 
   for (int64_t P = p0 + AT * wave; P < p1; P += AT * AW) {
-    // keys: lane (position r16, group g) takes bytes 16g .. 16g + 15
-    const int64_t kpos = P + r16;
-    uint4 kw = make_uint4(0, 0, 0, 0);
-    if (kpos < p1) kw = *reinterpret_cast<const uint4*>(kbase + kpos * (AD / 2) + 16 * g);
-    // values: lane (dims 8 dblk .., slot) takes 4 bytes of positions P + 4i + slot
-    uint32_t vw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t vpos = P + 4 * i + slot;
-      vw[i] = 0;
-      if (vpos < p1) vw[i] = *reinterpret_cast<const uint32_t*>(vbase + vpos * (AD / 2) + 4 * dblk);
+    const int lim = (int)(p1 - P < AT ? p1 - P : AT);  // valid positions in the tile
+    // keys and values: lane (position r16, group g) takes bytes 16g .. 16g + 15
+    uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
+    if (r16 < lim) {
+      kw = *reinterpret_cast<const uint4*>(kbase + (P + r16) * (AD / 2));
+      vw = *reinterpret_cast<const uint4*>(vbase + (P + r16) * (AD / 2));
     }
     // scales of positions P + 4g + e (score layout)
     float ksc[4], vsc[4];
+    if (sc_vec && lim == AT) {
+      const uint2 k2 = *reinterpret_cast<const uint2*>(ksb + P + 4 * g);
+      const uint2 v2 = *reinterpret_cast<const uint2*>(vsb + P + 4 * g);
+      ksc[0] = h2f((uint16_t)k2.x); ksc[1] = h2f((uint16_t)(k2.x >> 16));
+      ksc[2] = h2f((uint16_t)k2.y); ksc[3] = h2f((uint16_t)(k2.y >> 16));
+      vsc[0] = h2f((uint16_t)v2.x); vsc[1] = h2f((uint16_t)(v2.x >> 16));
+      vsc[2] = h2f((uint16_t)v2.y); vsc[3] = h2f((uint16_t)(v2.y >> 16));
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t sp = P + 4 * g + e;
-      ksc[e] = sp < p1 ? h2f(ksb[sp]) : 0.0f;
-      vsc[e] = sp < p1 ? h2f(vsb[sp]) : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = 4 * g + e < lim;
+        ksc[e] = ok ? h2f(ksb[P + 4 * g + e]) : 0.0f;
+        vsc[e] = ok ? h2f(vsb[P + 4 * g + e]) : 0.0f;
+      }
     }
+
+    // the value tile to LDS as f16 codes (row r16, columns 32g .. 32g + 31)
+    const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) *reinterpret_cast<v8h*>(vrow + 8 * w) = nibbles_f16(vwa[w]);
 
     // S^T = K Q~^T: C lane (query r16, group g), element e = position 4g + e
     v4f_a c = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -190,81 +212,64 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[t], c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[t], c, 0, 0, 0);
     }
-    float s[4];
+    float sv[4];
     float tmax = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s[e] = P + 4 * g + e < p1 ? c[e] * ksc[e] : kNegInf;
-      tmax = fmaxf(tmax, s[e]);
+      sv[e] = 4 * g + e < lim ? (c[e] * kTwo24) * ksc[e] : kNegInf;
+      tmax = fmaxf(tmax, sv[e]);
     }
     tmax = pair32_max(pair16_max(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const bool none = m_new == kNegInf;  // nothing seen yet (uniform per query)
-    const float alpha = none ? 1.0f : exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, tmax);  // finite: position P is valid
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.0f;
+    v4h ph, pl;  // B operand of the output product: p * vscale, f16 hi + lo
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = none ? 0.0f : exp2f(s[e] - m_new);
+      const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
       psum += p;
-      if (r16 < GM) pt[wave][4 * g + e][r16] = r16 < G ? p * vsc[e] : 0.0f;
+      const float pv = p * vsc[e];
+      const _Float16 hv = (_Float16)pv;
+      ph[e] = hv;
+      pl[e] = (_Float16)(pv - (float)hv);
     }
     psum = pair32_add(pair16_add(psum));
-    l_run = l_run * alpha + psum;
+    l_run = __builtin_fmaf(l_run, alpha, psum);
     m_run = m_new;
-    if (g == 0 && r16 < GM) ar[wave][r16] = alpha;
-    // LDS operations of one wavefront execute in order: fence the compiler only
+    // rescale only when some query's running max moved (rare after the first tiles)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int mt = 0; mt < AD / 16; ++mt) acc[mt] *= alpha;
+    }
+
+    // the tile's values are in LDS (one wavefront: its LDS operations are in order)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // o~ += p v^ on the VALU (codes as code' = code + 8; corr keeps sum p for the -8)
+    // o~^T += V^T (p vscale)^T: A = transposing read (dims x positions)
 #pragma unroll
-    for (int qi = 0; qi < GM; ++qi) {
-      const float al = ar[wave][qi];
-      corr[qi] *= al;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[qi][d] *= al;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t x = vw[i] ^ 0x88888888u;
-      const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-      float f[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {  // (float) of a byte field: v_cvt_f32_ubyte<k>
-        f[2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
-        f[2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
-      }
-#pragma unroll
-      for (int qi = 0; qi < GM; ++qi) {
-        const float pv = pt[wave][4 * i + slot][qi];
-        corr[qi] += pv;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[qi][d] = __builtin_fmaf(pv, f[d], o[qi][d]);
-      }
+    for (int mt = 0; mt < AD / 16; ++mt) {
+      const v4h a = __builtin_bit_cast(
+          v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) v4s*)(vtr + 16 * mt)));
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, ph, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pl, acc[mt], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- the wavefront's record: o~ = sum over the 4 slots of (o - 8 corr)
+  // ---- the wavefront's record: o~ = 2^24 acc
+  if (r16 < GM) {
 #pragma unroll
-  for (int qi = 0; qi < GM; ++qi)
+    for (int mt = 0; mt < AD / 16; ++mt)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const float v = __builtin_fmaf(-8.0f, corr[qi], o[qi][d]);
-      o[qi][d] = pair32_add(pair16_add(v));
+      for (int e = 0; e < 4; ++e) red[wave][r16][4 + 16 * mt + 4 * g + e] = acc[mt][e] * kTwo24;
+    if (g == 0) {
+      red[wave][r16][0] = m_run;
+      red[wave][r16][1] = l_run;
     }
-  if (slot == 0) {
-#pragma unroll
-    for (int qi = 0; qi < GM; ++qi)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) red[wave][qi][4 + 8 * dblk + d] = o[qi][d];
-  }
-  if (g == 0 && r16 < GM) {
-    red[wave][r16][0] = m_run;
-    red[wave][r16][1] = l_run;
   }
   __syncthreads();
 
@@ -275,17 +280,17 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < AW; ++w) mx = fmaxf(mx, red[w][qi][0]);
-    float acc = 0.0f;
+    float accv = 0.0f;
     if (c0 == 0) {
-      acc = mx;
+      accv = mx;
     } else if (mx != kNegInf) {
 #pragma unroll
       for (int w = 0; w < AW; ++w) {
-        const float f = exp2f(red[w][qi][0] - mx);
-        acc = __builtin_fmaf(f, red[w][qi][c0], acc);
+        const float f = __builtin_amdgcn_exp2f(red[w][qi][0] - mx);
+        accv = __builtin_fmaf(f, red[w][qi][c0], accv);
       }
     }
-    part[((bh * gridDim.x + blockIdx.x) * G + qi) * PREC + c0] = acc;
+    part[((bh * gridDim.x + blockIdx.x) * G + qi) * PREC + c0] = accv;
   }
 }
 
