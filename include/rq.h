@@ -387,10 +387,12 @@ size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64
  *   q          [batch][kv_heads * group][128] fp16 queries of the new token,
  *              16-byte aligned.
  *   k_codes, v_codes    [batch][kv_heads][seq][64] uint8 (rq_kv_rotate_quant),
- *              16-byte aligned; k_scales, v_scales [batch][kv_heads][seq] fp16.
+ *              16-byte aligned; k_scales, v_scales [batch][kv_heads][seq] fp16,
+ *              4-byte aligned (the scales move in pairs of positions).
  *   lengths    optional device int32 [batch] valid positions per entry
  *              (values are clamped to [0, seq]); NULL means seq for all.
- *   batch >= 0; kv_heads >= 1; 1 <= group <= 8; seq >= 1;
+ *   batch >= 0; kv_heads >= 1; 1 <= group <= 8; seq even and >= 2 (shorter
+ *              sequences use lengths);
  *   batch * kv_heads <= 65535; head_dim must be 128.
  *   signs      the [128] int8 +-1 signs the cache was rotated with, or NULL.
  *   sm_scale   softmax scale (> 0), normally 1 / sqrt(128).

@@ -49,7 +49,10 @@ constexpr int AD = 128;          // head dimension
 constexpr int AW = 4;            // wavefronts per workgroup
 constexpr int AT = 16;           // positions per wavefront step
 constexpr int PREC = AD + 4;     // floats per split record: m, l, 2 pad, o~[128]
-constexpr int VPITCH = AD + 8;   // f16 row pitch of the value tile (272 bytes: rows start in different banks)
+// f16 row pitch of the value tile: 288 bytes = 72 dwords, so the four rows
+// one 16-lane group of a transposing read touches start 8 banks apart and the
+// group's 16 x 8 bytes cover all 32 banks once
+constexpr int VPITCH = AD + 16;
 constexpr float kNegInf = -__builtin_inff();
 
 // Sum / max with the lane 16 and lane 32 apart (lane bits 4 and 5).
@@ -93,8 +96,77 @@ __device__ __forceinline__ v8h nibbles_f16(uint32_t w) {
 }
 constexpr float kTwo24 = 16777216.0f;
 
+// The same without the subtraction: (code + 8) * 2^-24.  Used for the keys,
+// whose MFMA sum is reset every tile: q~.k = 2^24 C - 8 sum q~ costs one fp32
+// rounding of a sum about twice the score, where the values' running output
+// would carry the offset's rounding across the whole sequence.
+__device__ __forceinline__ v8h nibbles_f16_offset(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * k);
+  return __builtin_bit_cast(v8h, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
 // Head dimension of element e of a k-step-t operand in lane group g.
 __device__ __forceinline__ int qk_dim(int g, int t, int e) { return 32 * g + 8 * t + e; }
+
+// Direct-to-LDS loads (the data never passes through VGPRs): lane L writes
+// its 16 (x4) or 4 (dword) bytes at LDS address m0 + 16 L (4 L).  The
+// compiler does not see these as loads; the kernel waits for them with
+// explicit s_waitcnt vmcnt(n), and the "memory" clobbers keep LDS reads after
+// the waits.
+// Addresses are a 32-bit per-lane byte offset against a 64-bit base in SGPRs.
+#define RQA_DMA16(M0, OFF, BASE)                                                 \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"    \
+               :                                                                 \
+               : "v"(OFF), "s"(M0), "s"(BASE)                                    \
+               : "memory", "m0")
+// The scales use a 64-bit per-lane address (lanes pick the key or the value
+// scales).
+#define RQA_DMA4(M0, ADDR)                                                       \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"     \
+               :                                                                 \
+               : "v"(ADDR), "s"(M0)                                              \
+               : "memory", "m0")
+#define RQA_WAIT_VM(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
+// One tile slot of a wavefront's LDS ring: 16 key rows, 16 value rows (64
+// bytes of codes each, row-major) and the 16 key then 16 value scales.
+constexpr int SLOT_K = 0, SLOT_V = AT * 64, SLOT_S = 2 * AT * 64;
+constexpr int SLOT = SLOT_S + 64;
+constexpr int NSLOT = 4;  // the tile in use and three in flight
+
+// The three DMA instructions of the tile at P into the slot at LDS address
+// slot: rows from p1 on re-read the split's last valid row (an L2 hit; their
+// weights are zero), so every call issues exactly three loads.  DMA lane L
+// fetches part (L + (L >> 3)) & 3 of row L / 4 (L >> 3 = r >> 1 for row r),
+// which puts part p of row r at 16-byte slot 4 r + ((p - (r >> 1)) & 3): the
+// eight lanes of one b128 read phase (rows r .. r + 7, one part) then hit
+// eight different bank groups.
+// The scales travel as 4-byte pairs of positions (S even keeps them aligned).
+// kb / vb / ksb / vsb are wave-uniform bases; offsets are 32-bit bytes.
+__device__ __forceinline__ void issue_tile(uint32_t slot, const uint8_t* kb, const uint8_t* vb,
+                                           const uint16_t* ksb, const uint16_t* vsb, int64_t P,
+                                           int64_t last, int lane) {
+  const int64_t r = P + (lane >> 2);
+  const uint32_t row = (uint32_t)(r < last ? r : last);
+  const uint32_t off = row * (AD / 2) + 16u * (uint32_t)((lane + (lane >> 3)) & 3);
+  RQA_DMA16(slot + SLOT_K, off, kb);
+  RQA_DMA16(slot + SLOT_V, off, vb);
+  if (lane < 16) {
+    const int64_t pos = P + 2 * (lane & 7);
+    const int64_t lst = last & ~(int64_t)1;
+    const uint16_t* src = lane < 8 ? ksb : vsb;
+    RQA_DMA4(slot + SLOT_S, src + (pos < lst ? pos : lst));
+  }
+}
+
+// LDS byte offset of part g of row r16 in a slot's key or value block
+__device__ __forceinline__ int ring_part(int r16, int g) {
+  return 16 * (4 * r16 + ((g - (r16 >> 1)) & 3));
+}
 
 template <int GM, bool HAS_SIGNS>
 __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
@@ -102,12 +174,21 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const int32_t* __restrict__ lengths, int H, int G, int64_t S, int64_t chunk, float qscale,
     const int8_t* __restrict__ signs, float* __restrict__ part) {
-  __shared__ float qs[GM][AD];                                  // rotated queries
-  __shared__ __align__(16) _Float16 vt[AW][AT][VPITCH];         // the tile's values, f16
-  __shared__ float red[AW][GM][PREC];                           // per-wavefront records
+  // ring[AW][NSLOT] tile slots, then the f16 value tiles; the queries rotate
+  // in the value-tile space before the first tile, and after the tile loop
+  // the per-wavefront records reuse the ring
+  constexpr int RING = AW * NSLOT * SLOT;
+  constexpr int VT = AW * AT * VPITCH * 2;
+  static_assert(AW * GM * PREC * 4 <= RING, "records fit in the ring");
+  static_assert(GM * AD * 4 <= VT, "queries fit in the value tiles");
+  __shared__ __align__(16) unsigned char smem[RING + VT];
+  float(*red)[GM][PREC] = reinterpret_cast<float(*)[GM][PREC]>(smem);
+  _Float16(*vt)[AT][VPITCH] = reinterpret_cast<_Float16(*)[AT][VPITCH]>(smem + RING);
+  float(*qs)[AD] = reinterpret_cast<float(*)[AD]>(smem + RING);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // wave is uniform per wavefront; readfirstlane lets the compiler see that
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / H, h = bh % H;
@@ -118,8 +199,10 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
   }
   const int64_t p0 = (int64_t)blockIdx.x * chunk;
   const int64_t p1 = p0 + chunk < len ? p0 + chunk : len;
+  const int64_t last = p1 > 0 ? p1 - 1 : 0;
 
-  // ---- the G queries of this KV head, rotated: (q * s) H_128 in LDS
+  // ---- the G queries of this KV head to LDS, (q * s) (their loads complete
+  // before the tile loads go out: waits count loads in issue order)
   for (int i = tid; i < GM * AD; i += 64 * AW) {
     const int qi = i / AD, d = i % AD;
     float v = 0.0f;
@@ -129,6 +212,22 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     }
     qs[qi][d] = v;
   }
+
+  // the wavefront's first three tiles go in flight while the queries rotate
+  const uint8_t* kb = kc + bh * S * (AD / 2);
+  const uint8_t* vb = vc + bh * S * (AD / 2);
+  const uint16_t* ksb = ks + bh * S;
+  const uint16_t* vsb = vs + bh * S;
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem +
+                        (uint32_t)(wave * NSLOT * SLOT);
+  const unsigned char* ringp = smem + wave * NSLOT * SLOT;
+  constexpr int64_t kStep = AT * AW;
+  const int64_t Pw = p0 + AT * wave;
+  issue_tile(ring, kb, vb, ksb, vsb, Pw, last, lane);
+  issue_tile(ring + SLOT, kb, vb, ksb, vsb, Pw + kStep, last, lane);
+  issue_tile(ring + 2 * SLOT, kb, vb, ksb, vsb, Pw + 2 * kStep, last, lane);
+
+  // ---- rotate the queries: (q * s) H_128 in LDS
   __syncthreads();
 #pragma unroll
   for (int hs = 1; hs < AD; hs <<= 1) {
@@ -157,46 +256,46 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
       ql[t][e] = (_Float16)(v - (float)hv);
     }
 
+  // 8 sum_d q~'_d over the f16 parts the MFMA sees: the score offset of the
+  // keys' +8 (query r16, every lane group)
+  float q8 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q8 += (float)qh[t][e] + (float)ql[t][e];
+  q8 = 8.0f * pair32_add(pair16_add(q8));
+  __syncthreads();  // every wavefront has its query operands: qs becomes value tiles
+
   // ---- per-wavefront running state, all in the layout of query r16
   float m_run = kNegInf, l_run = 0.0f;
   v4f_a acc[AD / 16];  // o~^T: m-tile mt, element e = value column 16 mt + 4 g + e
 #pragma unroll
   for (int mt = 0; mt < AD / 16; ++mt) acc[mt] = v4f_a{0.0f, 0.0f, 0.0f, 0.0f};
-  const uint8_t* kbase = kc + bh * S * (AD / 2) + 16 * g;
-  const uint8_t* vbase = vc + bh * S * (AD / 2) + 16 * g;
-  const uint16_t* ksb = ks + bh * S;
-  const uint16_t* vsb = vs + bh * S;
-  const bool sc_vec = (S & 3) == 0;  // 8-byte scale loads stay aligned
   _Float16* vrow = &vt[wave][r16][32 * g];
   // transposing read of the value tile: lane (j, g) points at row 4 g + j / 4,
   // column 4 (j % 4) of each 16-column block
   const _Float16* vtr = &vt[wave][4 * g + (r16 >> 2)][4 * (r16 & 3)];
 
-  for (int64_t P = p0 + AT * wave; P < p1; P += AT * AW) {
+  const int rpart = ring_part(r16, g);
+  int slot = 0;
+  for (int64_t P = Pw; P < p1; P += kStep) {
+    // the tile three steps ahead goes in flight, then this tile's loads are in
+    issue_tile(ring + ((slot + 3) & 3) * SLOT, kb, vb, ksb, vsb, P + 3 * kStep, last, lane);
+    RQA_WAIT_VM(9);
+    const unsigned char* sl = ringp + slot * SLOT;
+    slot = (slot + 1) & 3;
     const int lim = (int)(p1 - P < AT ? p1 - P : AT);  // valid positions in the tile
+
     // keys and values: lane (position r16, group g) takes bytes 16g .. 16g + 15
-    uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-    if (r16 < lim) {
-      kw = *reinterpret_cast<const uint4*>(kbase + (P + r16) * (AD / 2));
-      vw = *reinterpret_cast<const uint4*>(vbase + (P + r16) * (AD / 2));
-    }
-    // scales of positions P + 4g + e (score layout)
+    const uint4 kw = *reinterpret_cast<const uint4*>(sl + SLOT_K + rpart);
+    const uint4 vw = *reinterpret_cast<const uint4*>(sl + SLOT_V + rpart);
+    const uint2 k2 = *reinterpret_cast<const uint2*>(sl + SLOT_S + 8 * g);
+    const uint2 v2 = *reinterpret_cast<const uint2*>(sl + SLOT_S + 32 + 8 * g);
     float ksc[4], vsc[4];
-    if (sc_vec && lim == AT) {
-      const uint2 k2 = *reinterpret_cast<const uint2*>(ksb + P + 4 * g);
-      const uint2 v2 = *reinterpret_cast<const uint2*>(vsb + P + 4 * g);
-      ksc[0] = h2f((uint16_t)k2.x); ksc[1] = h2f((uint16_t)(k2.x >> 16));
-      ksc[2] = h2f((uint16_t)k2.y); ksc[3] = h2f((uint16_t)(k2.y >> 16));
-      vsc[0] = h2f((uint16_t)v2.x); vsc[1] = h2f((uint16_t)(v2.x >> 16));
-      vsc[2] = h2f((uint16_t)v2.y); vsc[3] = h2f((uint16_t)(v2.y >> 16));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = 4 * g + e < lim;
-        ksc[e] = ok ? h2f(ksb[P + 4 * g + e]) : 0.0f;
-        vsc[e] = ok ? h2f(vsb[P + 4 * g + e]) : 0.0f;
-      }
-    }
+    ksc[0] = h2f((uint16_t)k2.x); ksc[1] = h2f((uint16_t)(k2.x >> 16));
+    ksc[2] = h2f((uint16_t)k2.y); ksc[3] = h2f((uint16_t)(k2.y >> 16));
+    vsc[0] = h2f((uint16_t)v2.x); vsc[1] = h2f((uint16_t)(v2.x >> 16));
+    vsc[2] = h2f((uint16_t)v2.y); vsc[3] = h2f((uint16_t)(v2.y >> 16));
 
     // the value tile to LDS as f16 codes (row r16, columns 32g .. 32g + 31)
     const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
@@ -208,7 +307,7 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     const uint32_t kwa[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const v8h a = nibbles_f16(kwa[t]);
+      const v8h a = nibbles_f16_offset(kwa[t]);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[t], c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[t], c, 0, 0, 0);
     }
@@ -216,7 +315,7 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     float tmax = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sv[e] = 4 * g + e < lim ? (c[e] * kTwo24) * ksc[e] : kNegInf;
+      sv[e] = 4 * g + e < lim ? __builtin_fmaf(c[e], kTwo24, -q8) * ksc[e] : kNegInf;
       tmax = fmaxf(tmax, sv[e]);
     }
     tmax = pair32_max(pair16_max(tmax));
@@ -259,6 +358,10 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  // the loads of tiles past the end are still in flight: drain them before
+  // the ring is reused for the records
+  RQA_WAIT_VM(0);
+  __syncthreads();
 
   // ---- the wavefront's record: o~ = 2^24 acc
   if (r16 < GM) {
@@ -293,9 +396,14 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     part[((bh * gridDim.x + blockIdx.x) * G + qi) * PREC + c0] = accv;
   }
 }
+#undef RQA_DMA16
+#undef RQA_DMA4
+#undef RQA_WAIT_VM
 
 // One wavefront per (b * H + h, query): merge the splits, normalise, rotate
-// back (o~ H / sqrt(128), then the signs) and store fp16 (and fp32).
+// back (o~ H / sqrt(128), then the signs) and store fp16 (and fp32).  Lane sp
+// reads split sp's (max, sum); the output columns of 4 splits at a time
+// load together before they are summed.
 template <bool HAS_SIGNS>
 __global__ __launch_bounds__(256) void decode_attn_combine_kernel(
     const float* __restrict__ part, int64_t rows, int G, int nsplit,
@@ -304,17 +412,40 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // uniform per wavefront
   const int64_t bh = row / G, qi = row % G;
-  float mx = kNegInf;
-  for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, part[((bh * nsplit + sp) * G + qi) * PREC]);
-  float den = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  if (mx != kNegInf) {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* r = part + ((bh * nsplit + sp) * G + qi) * PREC;
-      const float f = exp2f(r[0] - mx);
-      den = __builtin_fmaf(f, r[1], den);
-      const float2 v = *reinterpret_cast<const float2*>(r + 4 + 2 * lane);
-      o0 = __builtin_fmaf(f, v.x, o0);
-      o1 = __builtin_fmaf(f, v.y, o1);
+  const float* rec0 = part + (bh * nsplit * G + qi) * PREC;  // split sp at rec0 + sp G PREC
+  const int64_t rstep = (int64_t)G * PREC;
+  // nsplit <= 64 (plan_splits): lane sp holds split sp's (max, sum).  The
+  // output columns of the first 4 splits load together with them, so that a
+  // row costs one round trip to memory when nsplit <= 4.
+  const float2 ml = lane < nsplit ? *reinterpret_cast<const float2*>(rec0 + lane * rstep)
+                                  : make_float2(kNegInf, 0.0f);
+  float2 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jj = u < nsplit ? u : nsplit - 1;
+    v[u] = *reinterpret_cast<const float2*>(rec0 + jj * rstep + 4 + 2 * lane);
+  }
+  float mx = ml.x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  const float f = lane < nsplit && mx != kNegInf ? __builtin_amdgcn_exp2f(ml.x - mx) : 0.0f;
+  float den = f * ml.y;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off, 64);
+  float o0 = 0.0f, o1 = 0.0f;
+  for (int j = 0; j < nsplit; j += 4) {
+    if (j > 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jj = j + u < nsplit ? j + u : nsplit - 1;
+        v[u] = *reinterpret_cast<const float2*>(rec0 + jj * rstep + 4 + 2 * lane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float fj = j + u < nsplit ? __shfl(f, j + u < nsplit ? j + u : 0, 64) : 0.0f;
+      o0 = __builtin_fmaf(fj, v[u].x, o0);
+      o1 = __builtin_fmaf(fj, v[u].y, o1);
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -344,12 +475,16 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(
   }
 }
 
-// Positions per split: enough splits for about 8 workgroups per CU, each a
-// multiple of 64 positions (4 wavefronts x 16).
+// Positions per split: about one full round of resident workgroups (3 per CU
+// at the split kernel's register use), so that every workgroup streams a long
+// chunk (the query rotation and the final merge are paid once per chunk) and
+// the combine kernel merges few records; each chunk a multiple of 64
+// positions (4 wavefronts x 16).
 void plan_splits(int64_t bh, int64_t S, int64_t* chunk, int* nsplit) {
-  const int64_t want = (int64_t)cu_count() * 8;
+  const int64_t want = (int64_t)cu_count() * 3;
   int64_t splits = (want + bh - 1) / bh;
-  const int64_t max_splits = (S + 63) / 64;
+  int64_t max_splits = (S + 63) / 64;
+  if (max_splits > 64) max_splits = 64;  // the combine kernel merges up to 64 splits
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int64_t c = (S + splits - 1) / splits;

@@ -221,7 +221,8 @@ int rq_decode_attention(const uint16_t* q, const uint8_t* k_codes, const uint16_
                         int64_t head_dim, const int8_t* signs, float sm_scale, uint16_t* out,
                         float* out_f32, void* workspace, size_t workspace_bytes, void* stream) {
   if (head_dim != 128) return RQ_ERR_SHAPE;
-  if (batch < 0 || kv_heads < 1 || kv_heads > 65535 || group < 1 || group > 8 || seq < 1)
+  if (batch < 0 || kv_heads < 1 || kv_heads > 65535 || group < 1 || group > 8 || seq < 2 ||
+      seq % 2 != 0)
     return RQ_ERR_SHAPE;
   if (batch * kv_heads > 65535 || seq >= kMaxRows) return RQ_ERR_SHAPE;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return RQ_ERR_SHAPE;
@@ -232,6 +233,8 @@ int rq_decode_attention(const uint16_t* q, const uint8_t* k_codes, const uint16_
   if (workspace_bytes < rq::decode_attention_workspace_bytes(batch, kv_heads, group, seq))
     return RQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(workspace))
+    return RQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(k_scales) & 3u) || (reinterpret_cast<uintptr_t>(v_scales) & 3u))
     return RQ_ERR_ALIGN;
   return from_hip(rq::launch_decode_attention(q, k_codes, k_scales, v_codes, v_scales, lengths,
                                               batch, kv_heads, group, seq, signs, sm_scale, out,

@@ -229,6 +229,8 @@ def test_decode_attention_argument_errors(lib):
     assert call(G=9) == binding.RQ_ERR_SHAPE
     assert call(G=0) == binding.RQ_ERR_SHAPE
     assert call(S=0) == binding.RQ_ERR_SHAPE
+    assert call(S=4095) == binding.RQ_ERR_SHAPE      # odd: the scales move in pairs
+    assert call(ks=ctypes.c_void_p(0x20002)) == binding.RQ_ERR_ALIGN
     assert call(sm=0.0) == binding.RQ_ERR_SHAPE
     assert call(sm=float("nan")) == binding.RQ_ERR_SHAPE
     assert call(nbytes=need - 1) == binding.RQ_ERR_SHAPE

@@ -111,12 +111,14 @@ def test_attention_lengths_edge_cases(rq):
                                atol=1e-5 * np.abs(v0).max())
 
 
-def test_attention_single_position_cache_and_sm_scale(rq):
+def test_attention_smallest_cache_and_sm_scale(rq):
     rng = np.random.default_rng(72)
-    kc, ks, vc, vs = random_cache(rng, 3, 2, 1)
+    kc, ks, vc, vs = random_cache(rng, 3, 2, 2)   # the smallest cache (seq even)
     q = rng.standard_normal((3, 4, 128)).astype(np.float16)
-    o16, o32 = run(rq, q, kc, ks, vc, vs, None, None, sm_scale=0.5)
-    check_attention(q, kc, ks, vc, vs, None, None, o16, o32, "S=1", sm_scale=0.5)
+    for lens in (None, [1, 2, 1]):
+        o16, o32 = run(rq, q, kc, ks, vc, vs, None, lens, sm_scale=0.5)
+        check_attention(q, kc, ks, vc, vs, None, lens, o16, o32, f"S=2 lengths={lens}",
+                        sm_scale=0.5)
     kc, ks, vc, vs = random_cache(rng, 2, 2, 300)
     q = (rng.standard_normal((2, 8, 128)) * 4).astype(np.float16)   # peaked softmax
     o16, o32 = run(rq, q, kc, ks, vc, vs, None, None, sm_scale=0.3)
