@@ -303,14 +303,17 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
     for (int w = 0; w < 4; ++w) *reinterpret_cast<v8h*>(vrow + 8 * w) = nibbles_f16(vwa[w]);
 
     // S^T = K Q~^T: C lane (query r16, group g), element e = position 4g + e
-    v4f_a c = {0.0f, 0.0f, 0.0f, 0.0f};
+    // two independent accumulation chains (hi and lo parts) halve the
+    // dependent MFMA latency of the tile
+    v4f_a ch = {0.0f, 0.0f, 0.0f, 0.0f}, cl = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t kwa[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const v8h a = nibbles_f16_offset(kwa[t]);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[t], c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[t], c, 0, 0, 0);
+      ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[t], ch, 0, 0, 0);
+      cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[t], cl, 0, 0, 0);
     }
+    const v4f_a c = ch + cl;
     float sv[4];
     float tmax = kNegInf;
 #pragma unroll
