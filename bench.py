@@ -189,7 +189,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("rotation_w4a4_quantization_amd/csrc/fwht_quant.hip",
                                                  "profiles/fwht_quant_4096x4096_traffic.json"),
-                     "kernel": "fwht_row_kernel<4096, true, 4>",
+                     "kernel": "fwht_row_kernel<4096, true, 4, false>",
                      "algorithmic_bytes_per_launch": nbytes},
         "wall_s_timed_region": round(wall, 3),
     }
