@@ -432,6 +432,27 @@ def main():
                                 "hbm_frac": round(bb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                     log(f"[bench] {key}: {sec[key]}")
                 del wcs, wc
+            # prefill: the persistent kernel with the zero-point epilogue
+            pf = datagen.prefill_linear(0)
+            sp = torch.from_numpy(pf["signs"]).to(dev)
+            wc, ws, _ = rq.fold_weights(torch.from_numpy(pf["wt"]).to(dev), sp)
+            del pf["wt"]
+            wsum = rq.weight_code_sums(wc)
+            mm, d, k = pf["m"], pf["d"], pf["k"]
+            acp, sap, zap, _ = rq.fwht_quant_asym(torch.from_numpy(pf["x"]).to(dev), sp)
+            y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+            wcs = [wc, wc.clone()]
+
+            def gpa(i):
+                rq.w4a4_gemm_asym(acp, sap, zap, wcs[i], ws, wsum, out=y)
+
+            msp = time_launches(torch, gpa, 2, max(5, steps2 // 4), warm2)
+            tops = 2 * mm * d * k / (msp * 1e-3) / 1e12
+            sec["gemm_asym_prefill_2048x8192x28672"] = {
+                "us": round(msp * 1e3, 2), "TOPS": round(tops, 1),
+                "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)}
+            log(f"[bench] asym prefill gemm: {sec['gemm_asym_prefill_2048x8192x28672']}")
+            del wcs, wc, y, acp
 
         if want("grouped"):
             # per-group (128) INT4 weight scales on the decode and prefill GEMMs

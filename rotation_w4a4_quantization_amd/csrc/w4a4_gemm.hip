@@ -673,6 +673,10 @@ __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); 
 // tiles in turn.  During the last K step of a tile it already loads step 0 of
 // its next tile, and the finished tile leaves through the buffer that step
 // does not use, so the next tile starts without a load ramp.
+// AM = kAU4: unsigned activation nibbles with zero points a_zeros and the
+// weight code sums w_sums (asymmetric activations); the MFMA sum is then
+// 16 * sum qa qw and the epilogue subtracts z * w_sums[col].
+template <int AM = kA4>
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
                                                               const uint8_t* __restrict__ w_codes,
@@ -680,7 +684,11 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
                                                               int64_t m, int64_t k, int64_t d,
                                                               int tiles_m, int tiles, bool wide_store,
                                                               uint16_t* __restrict__ y,
-                                                              int32_t* __restrict__ acc_out) {
+                                                              int32_t* __restrict__ acc_out,
+                                                              const uint8_t* __restrict__ a_zeros,
+                                                              const int32_t* __restrict__ w_sums) {
+  static_assert(AM == kA4 || AM == kAU4, "packed INT4 activations");
+  constexpr int SHIFT = AM == kA4 ? 8 : 4;
   __shared__ __align__(16) unsigned char lds[2 * LBUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -773,8 +781,13 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint4 q = *reinterpret_cast<const uint4*>(cur + (wm * 64 + i * 16) * LPK + fo);
-          af[0][i] = widen(q.x, q.y);
-          af[1][i] = widen(q.z, q.w);
+          if constexpr (AM == kAU4) {
+            af[0][i] = widen_u(q.x, q.y);
+            af[1][i] = widen_u(q.z, q.w);
+          } else {
+            af[0][i] = widen(q.x, q.y);
+            af[1][i] = widen(q.z, q.w);
+          }
         }
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
@@ -807,10 +820,12 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     asm volatile("" : "+v"(tid_o));
     const int g = (tid_o & 63) >> 4, r16 = tid_o & 15;
     float swv[7];
+    int32_t wsv[7];  // weight code sums (asymmetric activations only)
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       const int64_t col = n0 + wn * 112 + j * 16 + r16;
       swv[j] = col < k ? h2f(w_scales[col]) : 0.0f;
+      wsv[j] = AM == kAU4 && col < k ? w_sums[col] : 0;
     }
     const bool full = m0 + LM <= m && n0 + LN <= k;
     if (full && wide_store) {
@@ -830,10 +845,13 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int tr = wm * 32 + i2 * 16 + 4 * g + e;
-            const float sa = h2f(a_scales[m0 + wm * 64 + i * 16 + 4 * g + e]);
+            const int64_t arow = m0 + wm * 64 + i * 16 + 4 * g + e;
+            const float sa = h2f(a_scales[arow]);
+            const int32_t z = AM == kAU4 ? (int32_t)a_zeros[arow] : 0;
 #pragma unroll
             for (int j = 0; j < 7; ++j) {
-              const int32_t a = acc[i][j][e] >> 8;  // exact: the MFMA sum is 256 * acc
+              // exact: the MFMA sum is 2^SHIFT * sum qa qw
+              const int32_t a = (acc[i][j][e] >> SHIFT) - z * wsv[j];
               *reinterpret_cast<uint16_t*>(stg + tr * OP + 2 * (wn * 112 + j * 16 + r16)) =
                   f2h_rn(((float)a * sa) * swv[j]);
             }
@@ -859,11 +877,13 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
           if (!full && row >= m) continue;
           const float sa = h2f(a_scales[row]);
+          const int32_t z = AM == kAU4 ? (int32_t)a_zeros[row] : 0;
           const int64_t base = row * k + n0 + wn * 112 + r16;
 #pragma unroll
           for (int j = 0; j < 7; ++j) {
             if (full || n0 + wn * 112 + j * 16 + r16 < k)
-              epilogue_store(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out);
+              epilogue_store<SHIFT>(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out,
+                                    z * wsv[j]);
           }
         }
       }
@@ -989,9 +1009,9 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
     const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
     // 16-byte output stores need 16-byte aligned rows and no int32 output
     const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-    hipLaunchKernelGGL(w4a4_large_kernel, dim3((unsigned)grid), dim3(LTHREADS), 0, stream, a_codes,
-                       a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles, wide_store, y,
-                       acc);
+    hipLaunchKernelGGL(w4a4_large_kernel<kA4>, dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
+                       a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles,
+                       wide_store, y, acc, nullptr, nullptr);
   } else if (m <= 16) {
     const int64_t blocks = (k + 15) / 16;
     if (d % (2 * DSEG) == 0) {
@@ -1073,6 +1093,17 @@ hipError_t launch_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scale
                                  const uint8_t* a_zeros, int64_t m, const uint8_t* w_codes,
                                  const uint16_t* w_scales, const int32_t* w_sums, int64_t k,
                                  int64_t d, uint16_t* y, int32_t* acc, hipStream_t stream) {
+  if (m >= 128 && k >= 224 && d % LK == 0) {  // the persistent prefill kernel
+    const int tiles_m = (int)((m + LM - 1) / LM);
+    const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t grid = tiles < cu_count() ? tiles : cu_count();
+    const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
+    hipLaunchKernelGGL(w4a4_large_kernel<kAU4>, dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
+                       a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles,
+                       wide_store, y, acc, a_zeros, w_sums);
+    return hipGetLastError();
+  }
   return launch_gemm_variant<kAU4>(a_codes, a_scales, a_zeros, m, w_codes, w_scales, w_sums, k,
                                    d, y, acc, stream);
 }
