@@ -67,20 +67,35 @@ def kv_bytes(rows: int) -> int:
     return 2 * (rows * 128 * 2 + rows * 64 + rows * 2)
 
 
-def measured_traffic(kernel_source: str, summary: str):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the kernel source changed since it was measured."""
+KERNEL_SOURCES_MAIN = ["rotation_w4a4_quantization_amd/csrc/fwht_quant.hip",
+                       "rotation_w4a4_quantization_amd/csrc/rq_row_device.h"]
+
+
+def sources_sha256(paths) -> str:
+    """SHA-256 over the concatenated bytes of the files, in the given order."""
     import hashlib
 
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(root, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_sources, summary: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when any of the kernel's sources changed since it was
+    measured."""
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         with open(os.path.join(root, summary)) as f:
             rec = json.load(f)
-        with open(os.path.join(root, kernel_source), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = sources_sha256(kernel_sources)
     except OSError:
         return None
-    return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == sha else None
+    ok = rec.get("sources") == list(kernel_sources) and rec.get("source_sha256") == sha
+    return rec["traffic_bytes_per_launch"] if ok else None
 
 
 def time_launches(torch, fn, sets: int, steps: int, warmup: int):
@@ -187,7 +202,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("rotation_w4a4_quantization_amd/csrc/fwht_quant.hip",
+                     "traffic": measured_traffic(KERNEL_SOURCES_MAIN,
                                                  "profiles/fwht_quant_4096x4096_traffic.json"),
                      "kernel": "fwht_row_kernel<4096, true, 4, false>",
                      "algorithmic_bytes_per_launch": nbytes},

@@ -346,10 +346,18 @@ __global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_ke
   const RowLane rl = make_row_lane(L);
 
   for (;;) {
+    // The sign loads issue ahead of the row, except at n = 1024, where the
+    // row's two chunks came back sooner when issued first (measured).
+    constexpr bool kSignsFirst = N != 1024;
+    uint2 sg[NI];
+    if constexpr (HAS_SIGNS && kSignsFirst) load_signs(sg, signs, L);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 raw[NI];
     load_row(raw, static_cast<const __half*>(o.x) + row * N, L);
+    if constexpr (HAS_SIGNS && !kSignsFirst) load_signs(sg, signs, L);
+    __builtin_amdgcn_sched_barrier(0);  // every load issues before the first wait
     row_rotate_quant<N, HAS_SIGNS, false, BITS, ASYM>(
-        raw, signs, L, rl, c32, cb, o.codes + row * kCodeBytes, o.scales + row,
+        raw, sg, L, rl, c32, cb, o.codes + row * kCodeBytes, o.scales + row,
         o.xrot != nullptr ? o.xrot + row * N : nullptr, ASYM ? o.zeros + row : nullptr);
     const int64_t next = row + stride;
     if (next >= rows) break;

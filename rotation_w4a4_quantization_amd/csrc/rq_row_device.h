@@ -249,7 +249,8 @@ __device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl
 }
 
 // Rotates and quantises the row whose chunks `raw` holds (loaded by
-// load_row): lane 0 writes the fp16 scale to *scale_out, the wavefront writes
+// load_row, after the sign bytes `sg` were loaded by load_signs; sg is unused
+// without signs): lane 0 writes the fp16 scale to *scale_out, the wavefront writes
 // the code bytes (n/2 packed INT4 codes, or n INT8 codes for BITS == 8) to
 // codes_row through its LDS slice cb (as many bytes), or, with TO_LDS, leaves
 // them in cb (codes_row unused), and the fp32 rotated row goes to xrot_row
@@ -259,9 +260,25 @@ __device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl
 // widened to contain 0, the step is fp16(fp32(hi - lo) / 15) rounded once,
 // the zero point z = rne(-lo / step) (lane 0 writes it to *zero_out), and the
 // codes are the unsigned nibbles clamp(rne(x / step) + z, 0, 15).
+// Sign bytes 512 i + 8 L .. + 7 of each chunk, loaded before the row so that
+// the row's chunks can be waited for one at a time.  The pointer is made
+// opaque per row so that the loads are not hoisted into registers held across
+// the row loop.
+template <int NI>
+__device__ __forceinline__ void load_signs(uint2 (&sg)[NI], const int8_t* __restrict__ signs, int L) {
+  using gptr = const __attribute__((address_space(1))) uint64_t*;
+  gptr sp = (gptr)(signs + 8 * L);
+  asm volatile("" : "+v"(sp));
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint64_t v = sp[64 * i];
+    sg[i] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+  }
+}
+
 template <int N, bool HAS_SIGNS, bool TO_LDS = false, int BITS = 4, bool ASYM = false>
 __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
-                                                 const int8_t* __restrict__ signs, int L,
+                                                 const uint2 (&sg)[N / 512], int L,
                                                  const RowLane& rl, float c32, unsigned char* cb,
                                                  uint8_t* __restrict__ codes_row,
                                                  uint16_t* __restrict__ scale_out,
@@ -270,25 +287,25 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
   constexpr int R = N / 64;    // elements per lane
   constexpr int NI = N / 512;  // 16-byte loads per lane
   static_assert(N >= 512 && N <= 8192, "one row per wavefront covers 512..8192");
-  const float(&g)[4] = rl.g;
   const float sigma = rl.sigma;
   const int lane_pair = rl.lane_pair;
-  uint2 sg[NI];
-  if constexpr (HAS_SIGNS) {
-    const int8_t* sp = signs;
-    asm volatile("" : "+s"(sp));  // re-read per row, not hoisted into registers
-#pragma unroll
-    for (int i = 0; i < NI; ++i) sg[i] = *reinterpret_cast<const uint2*>(sp + 512 * i + 8 * L);
-  }
   // Opaque per iteration: keeps the compiler from hoisting one address
   // register per stored element out of the loop (they fold into immediate
   // offsets instead).
   int lp = lane_pair;
   asm volatile("" : "+v"(lp));
+  // e0: signs, then the fp16 pair's sum and difference.  From n = 4096 on the
+  // row is transformed chunk by chunk in load order (e0 .. e8 act within one
+  // 16-byte chunk per lane), so chunk i is worked on while later chunks are
+  // in flight; below that, stage by stage over all chunks, which schedules
+  // better when there are few chunks.  Both orders apply the same butterflies
+  // to the same operands.
+  constexpr bool kChunked = N >= 4096;
   float u[R];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    float* c = u + 8 * i;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint32_t w = w4[p];
@@ -298,40 +315,47 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
         const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
         w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;  // sign bits of s_2p, s_2p+1
       }
-      u[8 * i + 2 * p] = mix_add(w);
-      u[8 * i + 2 * p + 1] = mix_sub(w);
+      c[2 * p] = mix_add(w);
+      c[2 * p + 1] = mix_sub(w);
+    }
+    if constexpr (kChunked) {
+      chunk512_stages(*reinterpret_cast<float(*)[8]>(c), rl);
+      // keeps the next chunk's first use (and so its wait) after this chunk
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  butterfly_regs(u, 2);  // e1
-  butterfly_regs(u, 4);  // e2
+  if constexpr (!kChunked) {
+    const float(&g)[4] = rl.g;
+    butterfly_regs(u, 2);  // e1
+    butterfly_regs(u, 4);  // e2
 #pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[1,0,3,2]", u + b, g[0]);  // e3
+    for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[1,0,3,2]", u + b, g[0]);  // e3
 #pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[2,3,0,1]", u + b, g[1]);  // e4
+    for (int b = 0; b < R; b += 8) RQ_DPP8("quad_perm:[2,3,0,1]", u + b, g[1]);  // e4
 #pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("row_half_mirror", u + b, g[2]);      // e5
+    for (int b = 0; b < R; b += 8) RQ_DPP8("row_half_mirror", u + b, g[2]);      // e5
 #pragma unroll
-  for (int b = 0; b < R; b += 8) RQ_DPP8("row_ror:8", u + b, g[3]);            // e6
-
-  // lane bit 4 (e7) <-> register bit 2 (e2); lane bit 5 (e8) <-> register bit 1 (e1)
+    for (int b = 0; b < R; b += 8) RQ_DPP8("row_ror:8", u + b, g[3]);            // e6
+    // lane bit 4 (e7) <-> register bit 2 (e2); lane bit 5 (e8) <-> register bit 1 (e1)
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (!(r & 4)) {
-      const auto sw = __builtin_amdgcn_permlane16_swap(f2u(u[r]), f2u(u[r + 4]), false, false);
-      u[r] = u2f(sw[0]);
-      u[r + 4] = u2f(sw[1]);
+    for (int r = 0; r < R; ++r) {
+      if (!(r & 4)) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(f2u(u[r]), f2u(u[r + 4]), false, false);
+        u[r] = u2f(sw[0]);
+        u[r + 4] = u2f(sw[1]);
+      }
     }
-  }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (!(r & 2)) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(f2u(u[r]), f2u(u[r + 2]), false, false);
-      u[r] = u2f(sw[0]);
-      u[r + 2] = u2f(sw[1]);
+    for (int r = 0; r < R; ++r) {
+      if (!(r & 2)) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(f2u(u[r]), f2u(u[r + 2]), false, false);
+        u[r] = u2f(sw[0]);
+        u[r + 2] = u2f(sw[1]);
+      }
     }
+    butterfly_regs(u, 4);  // e7
+    butterfly_regs(u, 2);  // e8
   }
-  butterfly_regs(u, 4);  // e7
-  butterfly_regs(u, 2);  // e8
 #pragma unroll
   for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
 

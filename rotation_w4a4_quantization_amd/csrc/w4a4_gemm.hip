@@ -611,10 +611,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
   // that rotates a token loads it before its weights: loads return in order,
   // so the token does not wait behind the weight stream.
   if (t.wave < m) {
+    uint2 sg[N / 512];
+    if constexpr (HAS_SIGNS) load_signs(sg, signs, t.lane);
     uint4 raw[N / 512];
     load_row(raw, x + (int64_t)t.wave * N, t.lane);
     dec_issue_w(t, 0);
-    row_rotate_quant<N, HAS_SIGNS, true>(raw, signs, t.lane, make_row_lane(t.lane), c32,
+    row_rotate_quant<N, HAS_SIGNS, true>(raw, sg, t.lane, make_row_lane(t.lane), c32,
                                          acodes[t.wave], nullptr, ascales + t.wave, nullptr);
   } else {
     dec_issue_w(t, 0);
