@@ -301,6 +301,9 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
   // better when there are few chunks.  Both orders apply the same butterflies
   // to the same operands.
   constexpr bool kChunked = N >= 4096;
+  // e9.. between chunks as soon as their chunks are done (n = 4096; at 8192
+  // the compiler spills with it), else after the last chunk.
+  constexpr bool kProgressive = kChunked && NI <= 8;
   float u[R];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -320,6 +323,23 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
     }
     if constexpr (kChunked) {
       chunk512_stages(*reinterpret_cast<float(*)[8]>(c), rl);
+      // e9..: chunk j pairs with chunk j + h (h = 1, 2, 4, ...).  Once chunks
+      // i + 1 - 2h .. i have all had the stages below h, that block's stage
+      // for h runs, so little is left once the last chunk is in.
+#pragma unroll
+      for (int h = 1; h < NI; h <<= 1) {
+        if (kProgressive && (i + 1) % (2 * h) == 0) {
+#pragma unroll
+          for (int j = i + 1 - 2 * h; j < i + 1 - h; ++j) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              const float a = u[8 * j + r], b = u[8 * (j + h) + r];
+              u[8 * j + r] = a + b;
+              u[8 * (j + h) + r] = a - b;
+            }
+          }
+        }
+      }
       // keeps the next chunk's first use (and so its wait) after this chunk
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -356,8 +376,10 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
     butterfly_regs(u, 4);  // e7
     butterfly_regs(u, 2);  // e8
   }
+  if constexpr (!kProgressive) {
 #pragma unroll
-  for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
+    for (int h = 8; h < R; h <<= 1) butterfly_regs(u, h);  // e9..
+  }
 
   static_assert(BITS == 4 || BITS == 8, "INT4 or INT8 codes");
   static_assert(!ASYM || BITS == 4, "the asymmetric quantiser has INT4 codes");
