@@ -839,6 +839,20 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
       constexpr int HR = LM / 2;
       static_assert(HR * OP <= LBUF, "half the output tile fits in one step buffer");
       unsigned char* stg = lds + (par ^ 1) * LBUF;
+      // Every activation scale (and zero point) of both halves is loaded up
+      // front: loads issued after half 0's stores would wait for them
+      // (vector-memory counts drain in issue order).
+      float sav[4][4];
+      int32_t zv[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t arow = m0 + wm * 64 + i * 16 + 4 * g + e;
+          sav[i][e] = h2f(a_scales[arow]);
+          zv[i][e] = AM == kAU4 ? (int32_t)a_zeros[arow] : 0;
+        }
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -847,9 +861,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int tr = wm * 32 + i2 * 16 + 4 * g + e;
-            const int64_t arow = m0 + wm * 64 + i * 16 + 4 * g + e;
-            const float sa = h2f(a_scales[arow]);
-            const int32_t z = AM == kAU4 ? (int32_t)a_zeros[arow] : 0;
+            const float sa = sav[i][e];
+            const int32_t z = zv[i][e];
 #pragma unroll
             for (int j = 0; j < 7; ++j) {
               // exact: the MFMA sum is 2^SHIFT * sum qa qw
