@@ -678,6 +678,13 @@ __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); 
 // AM = kAU4: unsigned activation nibbles with zero points a_zeros and the
 // weight code sums w_sums (asymmetric activations); the MFMA sum is then
 // 16 * sum qa qw and the epilogue subtracts z * w_sums[col].
+// AM = kA8: INT8 activation bytes [m][d] (W4A8).  A step is then 128 codes:
+// A rows stay 128 bytes per step, B rows are 64 bytes (part p of row r at
+// part position p ^ ((r >> 1) & 3) of its 16-row group, so the 8-lane phases
+// of the fragment reads hit distinct bank groups), each lane reads two A
+// parts (order_a8 puts their bytes in widen's k order), the MFMA sum is
+// 16 * sum qa qw, and the output tile is staged in its own LDS region (a
+// 47 KB step buffer cannot hold a 59 KB half tile).
 template <int AM = kA4>
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
@@ -689,15 +696,25 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
                                                               int32_t* __restrict__ acc_out,
                                                               const uint8_t* __restrict__ a_zeros,
                                                               const int32_t* __restrict__ w_sums) {
-  static_assert(AM == kA4 || AM == kAU4, "packed INT4 activations");
+  static_assert(AM == kA4 || AM == kAU4 || AM == kA8, "activation format");
+  constexpr bool A8 = AM == kA8;
   constexpr int SHIFT = AM == kA4 ? 8 : 4;
-  __shared__ __align__(16) unsigned char lds[2 * LBUF];
+  constexpr int KSTEP = A8 ? LK / 2 : LK;       // codes per step
+  constexpr int APK = A8 ? KSTEP : KSTEP / 2;   // A bytes per row per step (128)
+  constexpr int BPK = KSTEP / 2;                // B bytes per row per step
+  constexpr int BUF = LM * APK + LN * BPK;      // one step buffer
+  constexpr int OP = 464;                       // LDS row pitch of the output tile (bytes)
+  constexpr int HR = LM / 2;                    // output rows staged at a time
+  constexpr int STAGE = A8 ? 2 * BUF : 0;       // A8: the staging region after both buffers
+  static_assert(APK == LPK, "A rows are 128 bytes per step");
+  static_assert(A8 ? 2 * BUF + HR * OP <= 160 * 1024 : HR * OP <= BUF, "the output staging fits");
+  __shared__ __align__(16) unsigned char lds[A8 ? 2 * BUF + HR * OP : 2 * BUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x 112
   const int g = lane >> 4, r16 = lane & 15;
-  const int64_t rowb = d / 2;
-  const int steps = (int)(rowb / LPK);
+  const int64_t rowa = A8 ? d : d / 2, rowb = d / 2;
+  const int steps = (int)(d / KSTEP);
   const uint32_t lds_base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
@@ -717,32 +734,45 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 
   // DMA rows of this lane: row 32 wave + 8 t + lane / 8 (t = 0..3) of the A
   // tile and (waves 0..6) of the B tile, 16-byte part drp of it; rows past the
-  // matrix edge re-read the last row (their results are never stored).
+  // matrix edge re-read the last row (their results are never stored).  With
+  // 64-byte B rows (A8) one DMA covers 16 B rows: row 32 wave + 16 t + lane / 4
+  // (t = 0, 1), part dbp.
+  constexpr int NBT = A8 ? 2 : 4;  // B DMA instructions per wave and step
   const int dr0 = 32 * wave + (lane >> 3);
   const int drp = 16 * part_pos(lane >> 3, lane & 7);  // (dr0 + 8 t) & 7 == (lane >> 3)
+  const int db0 = A8 ? 32 * wave + (lane >> 2) : dr0;
+  const int dbp = A8 ? 16 * ((lane & 3) ^ ((lane >> 3) & 3)) : drp;  // ((lane >> 2) >> 1) & 3
   const uint8_t* asrc[4];
-  const uint8_t* bsrc[4];
+  const uint8_t* bsrc[NBT];
 #define RQ_SET_SRC(M0_, N0_)                                                        \
   _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                   \
-    const int64_t ar_ = (M0_) + dr0 + 8 * t, br_ = (N0_) + dr0 + 8 * t;            \
-    asrc[t] = a_codes + (ar_ < m ? ar_ : m - 1) * rowb + drp;                       \
-    bsrc[t] = w_codes + (br_ < k ? br_ : k - 1) * rowb + drp;                       \
+    const int64_t ar_ = (M0_) + dr0 + 8 * t;                                        \
+    asrc[t] = a_codes + (ar_ < m ? ar_ : m - 1) * rowa + drp;                       \
+  }                                                                                 \
+  _Pragma("unroll") for (int t = 0; t < NBT; ++t) {                                 \
+    const int64_t br_ = (N0_) + db0 + (A8 ? 16 : 8) * t;                            \
+    bsrc[t] = w_codes + (br_ < k ? br_ : k - 1) * rowb + dbp;                       \
   }
-#define RQ_ISSUE_FROM(BUF, A_, B_, KB)                                              \
+  // loads of step S (codes S * KSTEP ..) into buffer BI_
+#define RQ_ISSUE_FROM(BI_, A_, B_, S)                                               \
   do {                                                                              \
-    const uint32_t buf_ = lds_base + (uint32_t)((BUF) * LBUF);                      \
+    const uint32_t buf_ = lds_base + (uint32_t)((BI_) * BUF);                       \
+    const int64_t ka_ = (int64_t)(S) * APK, kb_ = (int64_t)(S) * BPK;               \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
-      RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * LPK), (A_)[t] + (KB));         \
+      RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * APK), (A_)[t] + ka_);          \
     if (wave < LN / 32) {                                                           \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                 \
-        RQ_DMA(buf_ + (uint32_t)((LM + 32 * wave + 8 * t) * LPK), (B_)[t] + (KB));  \
+      _Pragma("unroll") for (int t = 0; t < NBT; ++t)                               \
+        RQ_DMA(buf_ + (uint32_t)(LM * APK + (32 * wave + (A8 ? 16 : 8) * t) * BPK), \
+               (B_)[t] + kb_);                                                      \
     }                                                                               \
   } while (0)
   RQ_SET_SRC(m0, n0);
 
   // fragment offsets of this lane inside a 16-row group, halves 0 and 1
-  const int frag_off0 = r16 * LPK + 16 * part_pos(r16, g);
-  const int frag_off1 = r16 * LPK + 16 * part_pos(r16, 4 + g);
+  // (A4 / AU4: the same for A and B); A8: A parts 2g and 2g + 1, B part g
+  const int frag_off0 = r16 * LPK + 16 * part_pos(r16, A8 ? 2 * g : g);
+  const int frag_off1 = r16 * LPK + 16 * part_pos(r16, A8 ? 2 * g + 1 : 4 + g);
+  const int frag_b8 = r16 * BPK + 16 * (g ^ ((r16 >> 1) & 3));
 
   int par = 0;  // buffer of the current step
   RQ_ISSUE_FROM(0, asrc, bsrc, 0);
@@ -763,37 +793,48 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 
     for (int s = 0; s < steps; ++s) {
       if (s + 1 < steps) {
-        RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, (int64_t)(s + 1) * LPK);
+        RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, s + 1);
       } else if (has_next) {
         const uint8_t* an[4];
-        const uint8_t* bn[4];
+        const uint8_t* bn[NBT];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int64_t ar = m0n + dr0 + 8 * t, br = n0n + dr0 + 8 * t;
-          an[t] = a_codes + (ar < m ? ar : m - 1) * rowb + drp;
-          bn[t] = w_codes + (br < k ? br : k - 1) * rowb + drp;
+          const int64_t ar = m0n + dr0 + 8 * t;
+          an[t] = a_codes + (ar < m ? ar : m - 1) * rowa + drp;
+        }
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+          const int64_t br = n0n + db0 + (A8 ? 16 : 8) * t;
+          bn[t] = w_codes + (br < k ? br : k - 1) * rowb + dbp;
         }
         RQ_ISSUE_FROM(par ^ 1, an, bn, 0);
       }
-      const unsigned char* cur = lds + par * LBUF;
+      const unsigned char* cur = lds + par * BUF;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < (A8 ? 1 : 2); ++u) {
         const int fo = u ? frag_off1 : frag_off0;
         v4i af[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint4 q = *reinterpret_cast<const uint4*>(cur + (wm * 64 + i * 16) * LPK + fo);
-          if constexpr (AM == kAU4) {
-            af[0][i] = widen_u(q.x, q.y);
-            af[1][i] = widen_u(q.z, q.w);
+          const unsigned char* ar = cur + (wm * 64 + i * 16) * APK;
+          if constexpr (A8) {
+            af[0][i] = order_a8(*reinterpret_cast<const uint4*>(ar + frag_off0));
+            af[1][i] = order_a8(*reinterpret_cast<const uint4*>(ar + frag_off1));
           } else {
-            af[0][i] = widen(q.x, q.y);
-            af[1][i] = widen(q.z, q.w);
+            const uint4 q = *reinterpret_cast<const uint4*>(ar + fo);
+            if constexpr (AM == kAU4) {
+              af[0][i] = widen_u(q.x, q.y);
+              af[1][i] = widen_u(q.z, q.w);
+            } else {
+              af[0][i] = widen(q.x, q.y);
+              af[1][i] = widen(q.z, q.w);
+            }
           }
         }
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
-          const uint4 q = *reinterpret_cast<const uint4*>(cur + (LM + wn * 112 + j * 16) * LPK + fo);
+          const uint4 q = *reinterpret_cast<const uint4*>(cur + LM * APK + (wn * 112 + j * 16) * BPK +
+                                                          (A8 ? frag_b8 : fo));
           const v4i b0 = widen(q.x, q.y), b1 = widen(q.z, q.w);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -831,14 +872,11 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     }
     const bool full = m0 + LM <= m && n0 + LN <= k;
     if (full && wide_store) {
-      // The fp16 tile goes through the free buffer in two halves of 128 rows
-      // (464-byte rows) and leaves as coalesced 16-byte stores.  Half h holds
-      // row groups 2h and 2h + 1 of every wave: staging row tr is tile row
-      // (tr / 32) * 64 + 32 h + tr % 32.
-      constexpr int OP = 464;  // LDS row pitch of the output tile (bytes)
-      constexpr int HR = LM / 2;
-      static_assert(HR * OP <= LBUF, "half the output tile fits in one step buffer");
-      unsigned char* stg = lds + (par ^ 1) * LBUF;
+      // The fp16 tile goes through the free buffer (A8: its own region) in
+      // two halves of 128 rows (464-byte rows) and leaves as coalesced 16-byte
+      // stores.  Half h holds row groups 2h and 2h + 1 of every wave: staging
+      // row tr is tile row (tr / 32) * 64 + 32 h + tr % 32.
+      unsigned char* stg = lds + (A8 ? STAGE : (par ^ 1) * BUF);
       // Every activation scale (and zero point) of both halves is loaded up
       // front: loads issued after half 0's stores would wait for them
       // (vector-memory counts drain in issue order).
@@ -1014,19 +1052,32 @@ hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d,
   return hipGetLastError();
 }
 
+// Shapes the persistent prefill kernel takes (d: whole 256-code steps).
+bool large_shape(int64_t m, int64_t k, int64_t d) { return m >= 128 && k >= 224 && d % LK == 0; }
+
+template <int AM>
+hipError_t launch_large(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
+                        int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
+                        const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
+                        hipStream_t stream) {
+  const int tiles_m = (int)((m + LM - 1) / LM);
+  const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
+  // 16-byte output stores need 16-byte aligned rows and no int32 output
+  const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
+  hipLaunchKernelGGL(w4a4_large_kernel<AM>, dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
+                     a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles, wide_store,
+                     y, acc, a_zeros, w_sums);
+  return hipGetLastError();
+}
+
 hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream) {
-  if (m >= 128 && k >= 224 && d % LK == 0) {
-    const int tiles_m = (int)((m + LM - 1) / LM);
-    const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
-    if (tiles > INT32_MAX) return hipErrorInvalidValue;
-    const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
-    // 16-byte output stores need 16-byte aligned rows and no int32 output
-    const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-    hipLaunchKernelGGL(w4a4_large_kernel<kA4>, dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
-                       a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles,
-                       wide_store, y, acc, nullptr, nullptr);
+  if (large_shape(m, k, d)) {
+    return launch_large<kA4>(a_codes, a_scales, nullptr, m, w_codes, w_scales, nullptr, k, d, y,
+                             acc, stream);
   } else if (m <= 16) {
     const int64_t blocks = (k + 15) / 16;
     if (d % (2 * DSEG) == 0) {
@@ -1100,25 +1151,21 @@ hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_sc
 hipError_t launch_w4a8_gemm(const int8_t* a_codes8, const uint16_t* a_scales, int64_t m,
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream) {
-  return launch_gemm_variant<kA8>(reinterpret_cast<const uint8_t*>(a_codes8), a_scales, nullptr,
-                                  m, w_codes, w_scales, nullptr, k, d, y, acc, stream);
+  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(a_codes8);
+  if (large_shape(m, k, d))  // the persistent prefill kernel, 128-code steps
+    return launch_large<kA8>(a8, a_scales, nullptr, m, w_codes, w_scales, nullptr, k, d, y, acc,
+                             stream);
+  return launch_gemm_variant<kA8>(a8, a_scales, nullptr, m, w_codes, w_scales, nullptr, k, d, y,
+                                  acc, stream);
 }
 
 hipError_t launch_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales,
                                  const uint8_t* a_zeros, int64_t m, const uint8_t* w_codes,
                                  const uint16_t* w_scales, const int32_t* w_sums, int64_t k,
                                  int64_t d, uint16_t* y, int32_t* acc, hipStream_t stream) {
-  if (m >= 128 && k >= 224 && d % LK == 0) {  // the persistent prefill kernel
-    const int tiles_m = (int)((m + LM - 1) / LM);
-    const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
-    if (tiles > INT32_MAX) return hipErrorInvalidValue;
-    const int64_t grid = tiles < cu_count() ? tiles : cu_count();
-    const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-    hipLaunchKernelGGL(w4a4_large_kernel<kAU4>, dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
-                       a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles,
-                       wide_store, y, acc, a_zeros, w_sums);
-    return hipGetLastError();
-  }
+  if (large_shape(m, k, d))  // the persistent prefill kernel
+    return launch_large<kAU4>(a_codes, a_scales, a_zeros, m, w_codes, w_scales, w_sums, k, d, y,
+                              acc, stream);
   return launch_gemm_variant<kAU4>(a_codes, a_scales, a_zeros, m, w_codes, w_scales, w_sums, k,
                                    d, y, acc, stream);
 }

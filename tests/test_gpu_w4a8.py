@@ -113,9 +113,13 @@ def test_fwht_quant8_ties_round_to_even(rq):
 
 # decode kernel (m <= 16, d a multiple of 256) with one and two 16-row weight
 # groups per workgroup, several 2 KB chunks, and the tile kernel (m > 16 or
-# d not a multiple of 256) with ragged edges
+# d not a multiple of 256) with ragged edges; the persistent prefill kernel
+# (m >= 128, k >= 224, d a multiple of 256) with full 256 x 224 tiles (the
+# LDS-staged store path on the second, non-debug call), edge tiles in both
+# dimensions, and one tile over 64 steps of 128 codes
 GEMM8_SHAPES = [(1, 1, 64), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
-                (5, 33, 192), (17, 33, 64), (130, 129, 256), (300, 260, 1024), (129, 257, 4160)]
+                (5, 33, 192), (17, 33, 64), (130, 129, 256), (300, 260, 1024), (129, 257, 4160),
+                (512, 448, 512), (300, 456, 512), (256, 224, 8192)]
 
 
 @pytest.mark.parametrize("m,k,d", GEMM8_SHAPES)
@@ -133,13 +137,13 @@ def test_w4a8_gemm_random_codes(rq, m, k, d):
     assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
 
 
-@pytest.mark.parametrize("m", [3, 64])
-def test_w4a8_gemm_closed_form_extremes(rq, m):
-    d, k = 16384, 40
+@pytest.mark.parametrize("m,k", [(3, 40), (64, 40), (256, 224)])
+def test_w4a8_gemm_closed_form_extremes(rq, m, k):
+    d = 16384
     a = np.full((m, d), -128, np.int8)
     w = O.pack_int4(np.full((k, d), -8))
     w[1::2] = O.pack_int4(np.full((1, d), 7))
-    say(f"w4a8 gemm extremes m={m}")
+    say(f"w4a8 gemm extremes m={m} k={k}")
     y, acc = rq.w4a8_gemm(dev(a), dev(np.full(m, 2.0 ** -10, np.float16)), dev(w),
                           dev(np.full(k, 2.0 ** -10, np.float16)), debug=True)
     acc = host(acc)
