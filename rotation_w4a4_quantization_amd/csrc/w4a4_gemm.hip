@@ -294,6 +294,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_kernel(
                :                                                                   \
                : "v"(ADDR), "s"(M0)                                                \
                : "memory", "m0")
+// One dword per lane: lane L's 4 bytes land at M0 + 4 L.
+#define RQ_DMA_D(M0, ADDR)                                                         \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"      \
+               :                                                                   \
+               : "v"(ADDR), "s"(M0)                                                \
+               : "memory", "m0")
 // The same with the nontemporal hint, for data read exactly once.
 #define RQ_DMA_NT(M0, ADDR)                                                        \
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"  \
@@ -685,7 +691,12 @@ __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); 
 // parts (order_a8 puts their bytes in widen's k order), the MFMA sum is
 // 16 * sum qa qw, and the output tile is staged in its own LDS region (a
 // 47 KB step buffer cannot hold a 59 KB half tile).
-template <int AM = kA4>
+// GROUPED (with kA4): w_scales holds per-group scales [k][d / 128], and a
+// half step (128 codes) is one group.  Each step's buffer also takes the two
+// group scales of its B rows (4 bytes a row, dword DMA by waves 0..3); per
+// half step every (i, j) tile's int32 sum over the group is two MFMAs from
+// zero, and it turns into fp32 with its column's group scale.
+template <int AM = kA4, bool GROUPED = false>
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
                                                               const uint8_t* __restrict__ w_codes,
@@ -697,18 +708,20 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
                                                               const uint8_t* __restrict__ a_zeros,
                                                               const int32_t* __restrict__ w_sums) {
   static_assert(AM == kA4 || AM == kAU4 || AM == kA8, "activation format");
+  static_assert(!GROUPED || AM == kA4, "group scales with symmetric INT4 activations");
   constexpr bool A8 = AM == kA8;
   constexpr int SHIFT = AM == kA4 ? 8 : 4;
   constexpr int KSTEP = A8 ? LK / 2 : LK;       // codes per step
   constexpr int APK = A8 ? KSTEP : KSTEP / 2;   // A bytes per row per step (128)
   constexpr int BPK = KSTEP / 2;                // B bytes per row per step
-  constexpr int BUF = LM * APK + LN * BPK;      // one step buffer
+  constexpr int BUF = LM * APK + LN * BPK;      // codes of one step
+  constexpr int BUFS = BUF + (GROUPED ? 4 * 256 : 0);  // + group scales: one buffer
   constexpr int OP = 464;                       // LDS row pitch of the output tile (bytes)
   constexpr int HR = LM / 2;                    // output rows staged at a time
   constexpr int STAGE = A8 ? 2 * BUF : 0;       // A8: the staging region after both buffers
   static_assert(APK == LPK, "A rows are 128 bytes per step");
   static_assert(A8 ? 2 * BUF + HR * OP <= 160 * 1024 : HR * OP <= BUF, "the output staging fits");
-  __shared__ __align__(16) unsigned char lds[A8 ? 2 * BUF + HR * OP : 2 * BUF];
+  __shared__ __align__(16) unsigned char lds[A8 ? 2 * BUF + HR * OP : 2 * BUFS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x 112
@@ -744,6 +757,13 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   const int dbp = A8 ? 16 * ((lane & 3) ^ ((lane >> 3) & 3)) : drp;  // ((lane >> 2) >> 1) & 3
   const uint8_t* asrc[4];
   const uint8_t* bsrc[NBT];
+  // GROUPED: group scales of B row 64 wave + lane (waves 0..3), from group 0
+  const int64_t gpitch = GROUPED ? d / WG * 2 : 0;  // bytes per row of group scales
+  const uint8_t* gsrc = nullptr;
+#define RQ_GSRC(N0_)                                                                \
+  (GROUPED ? reinterpret_cast<const uint8_t*>(w_scales) +                           \
+                 ((N0_) + 64 * wave + lane < k ? (N0_) + 64 * wave + lane : k - 1) * gpitch \
+           : nullptr)
 #define RQ_SET_SRC(M0_, N0_)                                                        \
   _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                   \
     const int64_t ar_ = (M0_) + dr0 + 8 * t;                                        \
@@ -752,11 +772,14 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   _Pragma("unroll") for (int t = 0; t < NBT; ++t) {                                 \
     const int64_t br_ = (N0_) + db0 + (A8 ? 16 : 8) * t;                            \
     bsrc[t] = w_codes + (br_ < k ? br_ : k - 1) * rowb + dbp;                       \
-  }
-  // loads of step S (codes S * KSTEP ..) into buffer BI_
-#define RQ_ISSUE_FROM(BI_, A_, B_, S)                                               \
+  }                                                                                 \
+  gsrc = RQ_GSRC(N0_);
+  // loads of step S (codes S * KSTEP ..) into buffer BI_ (GROUPED: and the
+  // step's two group scales of every B row, from G_)
+#define RQ_ISSUE_FROM(BI_, A_, B_, G_, S)                                           \
   do {                                                                              \
-    const uint32_t buf_ = lds_base + (uint32_t)((BI_) * BUF);                       \
+    const uint32_t buf_ = lds_base + (uint32_t)((BI_) * BUFS);                      \
+    if (GROUPED && wave < 4) RQ_DMA_D(buf_ + (uint32_t)(BUF + 256 * wave), (G_) + 4 * (S)); \
     const int64_t ka_ = (int64_t)(S) * APK, kb_ = (int64_t)(S) * BPK;               \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
       RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * APK), (A_)[t] + ka_);          \
@@ -775,7 +798,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   const int frag_b8 = r16 * BPK + 16 * (g ^ ((r16 >> 1) & 3));
 
   int par = 0;  // buffer of the current step
-  RQ_ISSUE_FROM(0, asrc, bsrc, 0);
+  RQ_ISSUE_FROM(0, asrc, bsrc, gsrc, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -786,14 +809,18 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     const int64_t m0n = (int64_t)(tn % tiles_m) * LM, n0n = (int64_t)(tn / tiles_m) * LN;
 
     v4i acc[4][7];
+    v4f facc[4][7];  // GROUPED: 256 * sum over groups of the group scale times its int32 sum
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 7; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+      for (int j = 0; j < 7; ++j) {
+        acc[i][j] = v4i{0, 0, 0, 0};
+        facc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      }
 
     for (int s = 0; s < steps; ++s) {
       if (s + 1 < steps) {
-        RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, s + 1);
+        RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, gsrc, s + 1);
       } else if (has_next) {
         const uint8_t* an[4];
         const uint8_t* bn[NBT];
@@ -807,9 +834,15 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           const int64_t br = n0n + db0 + (A8 ? 16 : 8) * t;
           bn[t] = w_codes + (br < k ? br : k - 1) * rowb + dbp;
         }
-        RQ_ISSUE_FROM(par ^ 1, an, bn, 0);
+        RQ_ISSUE_FROM(par ^ 1, an, bn, RQ_GSRC(n0n), 0);
       }
-      const unsigned char* cur = lds + par * BUF;
+      const unsigned char* cur = lds + par * BUFS;
+      uint32_t sgw[7];  // GROUPED: the step's two group scales of column j
+      if constexpr (GROUPED) {
+#pragma unroll
+        for (int j = 0; j < 7; ++j)
+          sgw[j] = *reinterpret_cast<const uint32_t*>(cur + BUF + 4 * (wn * 112 + j * 16 + r16));
+      }
 #pragma unroll
       for (int u = 0; u < (A8 ? 1 : 2); ++u) {
         const int fo = u ? frag_off1 : frag_off0;
@@ -836,12 +869,27 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           const uint4 q = *reinterpret_cast<const uint4*>(cur + LM * APK + (wn * 112 + j * 16) * BPK +
                                                           (A8 ? frag_b8 : fo));
           const v4i b0 = widen(q.x, q.y), b1 = widen(q.z, q.w);
+          if constexpr (GROUPED) {
+            const float sg = h2f((uint16_t)(u ? sgw[j] >> 16 : sgw[j]));  // group 2s + u
+            v4i t[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], b0, acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+              t[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+              t[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, t[i], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) facc[i][j][e] = __builtin_fmaf((float)t[i][e], sg, facc[i][j][e]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], b0, acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, acc[i][j], 0, 0, 0);
+          }
         }
       }
       // This wave's loads into buffer par ^ 1 have landed and its reads of
@@ -867,7 +915,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       const int64_t col = n0 + wn * 112 + j * 16 + r16;
-      swv[j] = col < k ? h2f(w_scales[col]) : 0.0f;
+      swv[j] = !GROUPED && col < k ? h2f(w_scales[col]) : 0.0f;
       wsv[j] = AM == kAU4 && col < k ? w_sums[col] : 0;
     }
     const bool full = m0 + LM <= m && n0 + LN <= k;
@@ -876,7 +924,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
       // two halves of 128 rows (464-byte rows) and leaves as coalesced 16-byte
       // stores.  Half h holds row groups 2h and 2h + 1 of every wave: staging
       // row tr is tile row (tr / 32) * 64 + 32 h + tr % 32.
-      unsigned char* stg = lds + (A8 ? STAGE : (par ^ 1) * BUF);
+      unsigned char* stg = lds + (A8 ? STAGE : (par ^ 1) * BUFS);
       // Every activation scale (and zero point) of both halves is loaded up
       // front: loads issued after half 0's stores would wait for them
       // (vector-memory counts drain in issue order).
@@ -906,7 +954,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
               // exact: the MFMA sum is 2^SHIFT * sum qa qw
               const int32_t a = (acc[i][j][e] >> SHIFT) - z * wsv[j];
               *reinterpret_cast<uint16_t*>(stg + tr * OP + 2 * (wn * 112 + j * 16 + r16)) =
-                  f2h_rn(((float)a * sa) * swv[j]);
+                  GROUPED ? f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa)
+                          : f2h_rn(((float)a * sa) * swv[j]);
             }
           }
         }
@@ -934,9 +983,13 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           const int64_t base = row * k + n0 + wn * 112 + r16;
 #pragma unroll
           for (int j = 0; j < 7; ++j) {
-            if (full || n0 + wn * 112 + j * 16 + r16 < k)
-              epilogue_store<SHIFT>(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out,
-                                    z * wsv[j]);
+            if (full || n0 + wn * 112 + j * 16 + r16 < k) {
+              if constexpr (GROUPED)
+                y[base + j * 16] = f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa);
+              else
+                epilogue_store<SHIFT>(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out,
+                                      z * wsv[j]);
+            }
           }
         }
       }
@@ -948,6 +1001,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   }
 #undef RQ_TILE_OK
 #undef RQ_TILE
+#undef RQ_GSRC
 #undef RQ_SET_SRC
 #undef RQ_ISSUE_FROM
 }
@@ -1055,7 +1109,7 @@ hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d,
 // Shapes the persistent prefill kernel takes (d: whole 256-code steps).
 bool large_shape(int64_t m, int64_t k, int64_t d) { return m >= 128 && k >= 224 && d % LK == 0; }
 
-template <int AM>
+template <int AM, bool GROUPED = false>
 hipError_t launch_large(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
                         int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
                         const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
@@ -1066,7 +1120,7 @@ hipError_t launch_large(const uint8_t* a_codes, const uint16_t* a_scales, const 
   const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
   // 16-byte output stores need 16-byte aligned rows and no int32 output
   const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-  hipLaunchKernelGGL(w4a4_large_kernel<AM>, dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
+  hipLaunchKernelGGL((w4a4_large_kernel<AM, GROUPED>), dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
                      a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles, wide_store,
                      y, acc, a_zeros, w_sums);
   return hipGetLastError();
@@ -1131,6 +1185,9 @@ hipError_t launch_gemm_variant(const uint8_t* a, const uint16_t* a_scales, const
 hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                                     const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
                                     int64_t d, uint16_t* y, hipStream_t stream) {
+  if (large_shape(m, k, d))  // the persistent prefill kernel: a half step is one group
+    return launch_large<kA4, true>(a_codes, a_scales, nullptr, m, w_codes, wg_scales, nullptr, k,
+                                   d, y, nullptr, stream);
   if (m <= 16 && d % (2 * DSEG) == 0) {
     if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
       hipLaunchKernelGGL(w4a4_decode_grouped_kernel<2>, dim3((unsigned)((k + 31) / 32)),

@@ -93,8 +93,12 @@ def test_fold_weights_grouped_decode_weights(rq):
         check_groups(w_rot, 128, host(c), host(s), f"fold grouped {k}")
 
 
+# decode kernel, tile kernel, and the persistent prefill kernel (m >= 128,
+# k >= 224, d a multiple of 256): full 256 x 224 tiles (LDS-staged stores),
+# edge tiles in both dimensions, and one tile over 64 groups
 GROUPED_SHAPES = [(1, 1, 256), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
-                  (5, 33, 384), (17, 33, 128), (130, 129, 256), (300, 260, 1024)]
+                  (5, 33, 384), (17, 33, 128), (130, 129, 256), (300, 260, 1024),
+                  (512, 448, 512), (300, 456, 512), (256, 224, 8192)]
 
 
 @pytest.mark.parametrize("m,k,d", GROUPED_SHAPES)
@@ -112,17 +116,18 @@ def test_w4a4_gemm_grouped_random_codes(rq, m, k, d):
     assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
 
 
-def test_grouped_equal_scales_match_per_channel(rq):
+@pytest.mark.parametrize("m,k,d", [(4, 64, 4096), (256, 224, 4096)])
+def test_grouped_equal_scales_match_per_channel(rq, m, k, d):
     # equal group scales in a row: the grouped GEMM is the per-channel GEMM
     # up to fp32 summation order; with power-of-two scales every product and
-    # partial sum is exact, so the two agree bit for bit
-    rng = np.random.default_rng(33)
-    m, k, d = 4, 64, 4096
+    # partial sum is exact, so the two agree bit for bit (decode kernels, and
+    # the persistent prefill kernel)
+    rng = np.random.default_rng(33 + m)
     ac = datagen.random_codes(rng, m, d)
     wc = datagen.random_codes(rng, k, d)
     sa = (2.0 ** rng.integers(-12, -6, m)).astype(np.float16)
     sw1 = (2.0 ** rng.integers(-12, -6, k)).astype(np.float16)
-    say("grouped vs per-channel")
+    say(f"grouped vs per-channel m={m} k={k} d={d}")
     yg = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(np.repeat(sw1[:, None], d // 128, 1)))
     yc, _ = rq.w4a4_gemm(dev(ac), dev(sa), dev(wc), dev(sw1))
     assert np.array_equal(host(yg).view(np.uint16), host(yc).view(np.uint16))
