@@ -363,7 +363,10 @@ int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64
 /*
  * rq_decode_attention_workspace_size -- bytes of device workspace that
  * rq_decode_attention needs for this shape on the current device (one
- * fp32 record of 132 values per query head and split of the cache).
+ * fp32 record of 132 values per query head and split of the cache).  When
+ * batch * kv_heads is a multiple of the device's CU count, the call runs one
+ * workgroup per KV head over the whole sequence and leaves the workspace
+ * untouched; it is still required.
  */
 size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64_t group,
                                           int64_t seq);

@@ -168,23 +168,61 @@ __device__ __forceinline__ int ring_part(int r16, int g) {
   return 16 * (4 * r16 + ((g - (r16 >> 1)) & 3));
 }
 
-template <int GM, bool HAS_SIGNS>
-__global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
+// The normalised output row o~ (lane: dims 2 lane, 2 lane + 1) rotated back,
+// o = (o~ H / sqrt(128)) then the signs, stored as fp16 (and fp32) at
+// out[base ..].
+template <bool HAS_SIGNS>
+__device__ __forceinline__ void finish_row(float o0, float o1, int lane,
+                                           const int8_t* __restrict__ signs, int64_t base,
+                                           uint16_t* __restrict__ out, float* __restrict__ out_f32) {
+  // FWHT over the 128 dims
+  float a = o0 + o1, c = o0 - o1;
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const float pa = __shfl_xor(a, 1 << bit, 64), pc = __shfl_xor(c, 1 << bit, 64);
+    const bool upper = (lane >> bit) & 1;
+    a = upper ? pa - a : a + pa;
+    c = upper ? pc - c : c + pc;
+  }
+  const float sc = 0.08838834764831845f;  // fp32(1 / sqrt(128))
+  float r0 = a * sc, r1 = c * sc;
+  if (HAS_SIGNS) {
+    if (signs[2 * lane] < 0) r0 = -r0;
+    if (signs[2 * lane + 1] < 0) r1 = -r1;
+  }
+  const int64_t at = base + 2 * lane;
+  out[at] = f2h_rn(r0);
+  out[at + 1] = f2h_rn(r1);
+  if (out_f32 != nullptr) {
+    out_f32[at] = r0;
+    out_f32[at + 1] = r1;
+  }
+}
+
+// NW wavefronts per workgroup.  FUSED: the workgroup covers the whole
+// sequence of its KV head (one split) and finishes the job itself: after the
+// merge of its wavefronts it normalises, rotates back and stores the output,
+// so no records and no combine kernel are needed.
+template <int GM, bool HAS_SIGNS, int NW = AW, bool FUSED = false>
+__global__ __launch_bounds__(64 * NW) void decode_attn_split_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const int32_t* __restrict__ lengths, int H, int G, int64_t S, int64_t chunk, float qscale,
-    const int8_t* __restrict__ signs, float* __restrict__ part) {
-  // ring[AW][NSLOT] tile slots, then the f16 value tiles; the queries rotate
+    const int8_t* __restrict__ signs, float* __restrict__ part, uint16_t* __restrict__ out,
+    float* __restrict__ out_f32) {
+  // ring[NW][NSLOT] tile slots, then the f16 value tiles; the queries rotate
   // in the value-tile space before the first tile, and after the tile loop
-  // the per-wavefront records reuse the ring
-  constexpr int RING = AW * NSLOT * SLOT;
-  constexpr int VT = AW * AT * VPITCH * 2;
-  static_assert(AW * GM * PREC * 4 <= RING, "records fit in the ring");
-  static_assert(GM * AD * 4 <= VT, "queries fit in the value tiles");
+  // the per-wavefront records reuse the ring (FUSED: the merged records go to
+  // the value-tile space)
+  constexpr int RING = NW * NSLOT * SLOT;
+  constexpr int VT = NW * AT * VPITCH * 2;
+  static_assert(NW * GM * PREC * 4 <= RING, "records fit in the ring");
+  static_assert(GM * AD * 4 <= VT && GM * PREC * 4 <= VT, "queries fit in the value tiles");
   __shared__ __align__(16) unsigned char smem[RING + VT];
   float(*red)[GM][PREC] = reinterpret_cast<float(*)[GM][PREC]>(smem);
   _Float16(*vt)[AT][VPITCH] = reinterpret_cast<_Float16(*)[AT][VPITCH]>(smem + RING);
   float(*qs)[AD] = reinterpret_cast<float(*)[AD]>(smem + RING);
+  float(*fin)[PREC] = reinterpret_cast<float(*)[PREC]>(smem + RING);
 
   const int tid = threadIdx.x;
   // wave is uniform per wavefront; readfirstlane lets the compiler see that
@@ -203,7 +241,7 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
 
   // ---- the G queries of this KV head to LDS, (q * s) (their loads complete
   // before the tile loads go out: waits count loads in issue order)
-  for (int i = tid; i < GM * AD; i += 64 * AW) {
+  for (int i = tid; i < GM * AD; i += 64 * NW) {
     const int qi = i / AD, d = i % AD;
     float v = 0.0f;
     if (qi < G) {
@@ -221,7 +259,7 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem +
                         (uint32_t)(wave * NSLOT * SLOT);
   const unsigned char* ringp = smem + wave * NSLOT * SLOT;
-  constexpr int64_t kStep = AT * AW;
+  constexpr int64_t kStep = AT * NW;
   const int64_t Pw = p0 + AT * wave;
   issue_tile(ring, kb, vb, ksb, vsb, Pw, last, lane);
   issue_tile(ring + SLOT, kb, vb, ksb, vsb, Pw + kStep, last, lane);
@@ -231,7 +269,7 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
   __syncthreads();
 #pragma unroll
   for (int hs = 1; hs < AD; hs <<= 1) {
-    for (int i = tid; i < GM * AD / 2; i += 64 * AW) {
+    for (int i = tid; i < GM * AD / 2; i += 64 * NW) {
       const int qi = i / (AD / 2), j = i % (AD / 2);
       const int i0 = (j / hs) * 2 * hs + (j % hs);
       const float a = qs[qi][i0], c = qs[qi][i0 + hs];
@@ -379,24 +417,37 @@ __global__ __launch_bounds__(64 * AW) void decode_attn_split_kernel(
   }
   __syncthreads();
 
-  // ---- merge the 4 wavefronts and write the split's record
-  for (int i = tid; i < GM * PREC; i += 64 * AW) {
+  // ---- merge the wavefronts: the split's record (FUSED: into LDS)
+  for (int i = tid; i < GM * PREC; i += 64 * NW) {
     const int qi = i / PREC, c0 = i % PREC;
     if (qi >= G || c0 == 2 || c0 == 3) continue;
     float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < AW; ++w) mx = fmaxf(mx, red[w][qi][0]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w][qi][0]);
     float accv = 0.0f;
     if (c0 == 0) {
       accv = mx;
     } else if (mx != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < AW; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = __builtin_amdgcn_exp2f(red[w][qi][0] - mx);
         accv = __builtin_fmaf(f, red[w][qi][c0], accv);
       }
     }
-    part[((bh * gridDim.x + blockIdx.x) * G + qi) * PREC + c0] = accv;
+    if constexpr (FUSED)
+      fin[qi][c0] = accv;
+    else
+      part[((bh * gridDim.x + blockIdx.x) * G + qi) * PREC + c0] = accv;
+  }
+  if constexpr (FUSED) {
+    __syncthreads();
+    // wavefront qi finishes query qi: lane holds dims 2 lane, 2 lane + 1
+    if (wave < G) {
+      const float den = fin[wave][1];
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      const float o0 = fin[wave][4 + 2 * lane] * inv, o1 = fin[wave][5 + 2 * lane] * inv;
+      finish_row<HAS_SIGNS>(o0, o1, lane, signs, (bh * G + wave) * AD, out, out_f32);
+    }
   }
 }
 #undef RQA_DMA16
@@ -452,30 +503,7 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  o0 *= inv;
-  o1 *= inv;
-  // FWHT over the 128 dims: lane holds dims 2 lane, 2 lane + 1
-  float a = o0 + o1, c = o0 - o1;
-#pragma unroll
-  for (int bit = 0; bit < 6; ++bit) {
-    const float pa = __shfl_xor(a, 1 << bit, 64), pc = __shfl_xor(c, 1 << bit, 64);
-    const bool upper = (lane >> bit) & 1;
-    a = upper ? pa - a : a + pa;
-    c = upper ? pc - c : c + pc;
-  }
-  const float sc = 0.08838834764831845f;  // fp32(1 / sqrt(128))
-  float r0 = a * sc, r1 = c * sc;
-  if (HAS_SIGNS) {
-    if (signs[2 * lane] < 0) r0 = -r0;
-    if (signs[2 * lane + 1] < 0) r1 = -r1;
-  }
-  const int64_t base = row * AD + 2 * lane;
-  out[base] = f2h_rn(r0);
-  out[base + 1] = f2h_rn(r1);
-  if (out_f32 != nullptr) {
-    out_f32[base] = r0;
-    out_f32[base + 1] = r1;
-  }
+  finish_row<HAS_SIGNS>(o0 * inv, o1 * inv, lane, signs, row * AD, out, out_f32);
 }
 
 // Positions per split: about one full round of resident workgroups (3 per CU
@@ -496,14 +524,25 @@ void plan_splits(int64_t bh, int64_t S, int64_t* chunk, int* nsplit) {
   *nsplit = (int)((S + c - 1) / c);
 }
 
+// Wavefronts of the fused workgroup: three per SIMD, as many as the split
+// kernel's three 4-wavefront workgroups per CU (the LDS limit: 12 rings and
+// value tiles take 153 KB).
+constexpr int AW_FUSED = 12;
+
 template <int GM, bool HAS_SIGNS>
 void launch_split(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
                   const uint16_t* vs, const int32_t* lengths, int64_t B, int64_t H, int G,
                   int64_t S, int64_t chunk, int nsplit, float qscale, const int8_t* signs,
-                  float* part, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_split_kernel<GM, HAS_SIGNS>), dim3((unsigned)nsplit, (unsigned)(B * H)),
-                     dim3(64 * AW), 0, stream, reinterpret_cast<const __half*>(q), kc, ks, vc, vs,
-                     lengths, (int)H, G, S, chunk, qscale, signs, part);
+                  float* part, bool fused, uint16_t* out, float* out_f32, hipStream_t stream) {
+  if (fused)
+    hipLaunchKernelGGL((decode_attn_split_kernel<GM, HAS_SIGNS, AW_FUSED, true>),
+                       dim3(1u, (unsigned)(B * H)), dim3(64 * AW_FUSED), 0, stream,
+                       reinterpret_cast<const __half*>(q), kc, ks, vc, vs, lengths, (int)H, G, S, S,
+                       qscale, signs, part, out, out_f32);
+  else
+    hipLaunchKernelGGL((decode_attn_split_kernel<GM, HAS_SIGNS>), dim3((unsigned)nsplit, (unsigned)(B * H)),
+                       dim3(64 * AW), 0, stream, reinterpret_cast<const __half*>(q), kc, ks, vc, vs,
+                       lengths, (int)H, G, S, chunk, qscale, signs, part, out, out_f32);
 }
 
 }  // namespace
@@ -528,14 +567,18 @@ hipError_t launch_decode_attention(const uint16_t* q, const uint8_t* kc, const u
   // scores come out in log2 units: q~ carries 1/sqrt(128), the softmax scale and log2(e)
   const float qscale = 0.08838834764831845f * sm_scale * 1.4426950408889634f;
   const bool sg = signs != nullptr;
+  // One workgroup per KV head over the whole sequence, finishing in place,
+  // when the KV heads fill the CUs in whole rounds (the split kernel then
+  // gains nothing from splitting and needs a combine launch).
+  const bool fused = (B * H) % cu_count() == 0;
   if (G <= 4)
-    sg ? launch_split<4, true>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, stream)
-       : launch_split<4, false>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, stream);
+    sg ? launch_split<4, true>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, fused, out, out_f32, stream)
+       : launch_split<4, false>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, fused, out, out_f32, stream);
   else
-    sg ? launch_split<8, true>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, stream)
-       : launch_split<8, false>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, stream);
+    sg ? launch_split<8, true>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, fused, out, out_f32, stream)
+       : launch_split<8, false>(q, kc, ks, vc, vs, lengths, B, H, (int)G, S, chunk, nsplit, qscale, signs, part, fused, out, out_f32, stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fused) return e;
   const int64_t rows = B * H * G;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (sg)

@@ -165,3 +165,24 @@ def test_attention_full_cache_sampled(rq):
     for b in (0, 17, 31):
         check_attention(q[b:b + 1], host(kc[b:b + 1]), host(ks[b:b + 1]), host(vc[b:b + 1]),
                         host(vs[b:b + 1]), None, None, o16[b:b + 1], o32[b:b + 1], f"full b={b}")
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_attention_one_workgroup_per_kv_head(rq, G):
+    # B * H a multiple of the CU count: one 12-wavefront workgroup per KV head
+    # covers the whole sequence and writes the output itself (no combine);
+    # signs, and lengths 0, 1, S and ragged ones
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = 4
+    if cus % H:
+        pytest.skip(f"{cus} CUs: no whole number of batch entries per round")
+    B, S = cus // H, 200
+    rng = np.random.default_rng(90 + G)
+    kc, ks, vc, vs = random_cache(rng, B, H, S)
+    q = rng.standard_normal((B, H * G, 128)).astype(np.float16)
+    signs = np.where(rng.random(128) < 0.5, -1, 1).astype(np.int8)
+    lens = rng.integers(2, S + 1, B)
+    lens[:3] = [0, 1, S]
+    say(f"attention one workgroup per KV head B={B} H={H} G={G}")
+    o16, o32 = run(rq, q, kc, ks, vc, vs, signs, lens)
+    check_attention(q, kc, ks, vc, vs, signs, lens, o16, o32, f"fused G={G}")
