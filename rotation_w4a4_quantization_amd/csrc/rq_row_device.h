@@ -260,6 +260,26 @@ __device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl
 // widened to contain 0, the step is fp16(fp32(hi - lo) / 15) rounded once,
 // the zero point z = rne(-lo / step) (lane 0 writes it to *zero_out), and the
 // codes are the unsigned nibbles clamp(rne(x / step) + z, 0, 15).
+// Signs and stage e0 of one 16-byte chunk (8 fp16 elements of a lane): the
+// sign flip is an xor on each fp16 pair, then v_fma_mix_f32 gives the pair's
+// sum and difference in fp32, one rounding each.
+template <bool HAS_SIGNS>
+__device__ __forceinline__ void chunk_e0(const uint4& raw, uint2 sg, float* c) {
+  const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t w = w4[p];
+    if constexpr (HAS_SIGNS) {
+      const uint32_t s2 = p < 2 ? sg.x : sg.y;
+      const uint32_t b0 = (2u * p) & 3u;
+      const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
+      w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;  // sign bits of s_2p, s_2p+1
+    }
+    c[2 * p] = mix_add(w);
+    c[2 * p + 1] = mix_sub(w);
+  }
+}
+
 // Sign bytes 512 i + 8 L .. + 7 of each chunk, loaded before the row so that
 // the row's chunks can be waited for one at a time.  The pointer is made
 // opaque per row so that the loads are not hoisted into registers held across
@@ -307,20 +327,8 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
   float u[R];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
     float* c = u + 8 * i;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t w = w4[p];
-      if constexpr (HAS_SIGNS) {
-        const uint32_t s2 = p < 2 ? sg[i].x : sg[i].y;
-        const uint32_t b0 = (2u * p) & 3u;
-        const uint32_t sel = 0x0Cu | (b0 << 8) | (0x0Cu << 16) | ((b0 + 1u) << 24);
-        w ^= __builtin_amdgcn_perm(0u, s2, sel) & 0x80008000u;  // sign bits of s_2p, s_2p+1
-      }
-      c[2 * p] = mix_add(w);
-      c[2 * p + 1] = mix_sub(w);
-    }
+    chunk_e0<HAS_SIGNS>(raw[i], sg[i], c);
     if constexpr (kChunked) {
       chunk512_stages(*reinterpret_cast<float(*)[8]>(c), rl);
       // e9..: chunk j pairs with chunk j + h (h = 1, 2, 4, ...).  Once chunks

@@ -598,7 +598,19 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
 // the weight stream, which the decode GEMM waits for anyway.
 constexpr int LD_FUSED_M = 4;
 
-template <int N, bool HAS_SIGNS, int RG>
+// MW > 0 (8 or 4): every token is rotated by MW wavefronts together (m <= 8 / MW):
+// wavefront w takes token w / MW, chunks (w % MW) * CPW .. + CPW - 1 of its
+// row, runs e0 .. e8 on each and the stages between its own chunks, and
+// writes the values (sign sigma taken out) to an fp32 row in LDS in element
+// order.  After a barrier the token's 64 MW threads take pairs of adjacent
+// positions q = 2a, 2a + 1 of one local chunk lc and finish the stages
+// between wavefronts (chunks lc + CPW j, j = 0 .. MW - 1, in ascending
+// order), then the absmax (wave max, then across the token's wavefronts
+// through LDS), the scale and the codes.  Every butterfly has the same
+// operands as in the one-wavefront rotation, up to the exact sign sigma,
+// and fma(u sigma, c / s, M) = fma(u, (c / s) sigma, M): codes and scales are
+// bit-identical to it.  MW = 0: one wavefront per token (row_rotate_quant).
+template <int N, bool HAS_SIGNS, int RG, int MW = 0>
 __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
     const __half* __restrict__ x, int64_t m, const int8_t* __restrict__ signs, float c32,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int64_t k,
@@ -614,9 +626,111 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
   const DecLane<RG> t = dec_lane<RG>(w_codes, k, rowb, wl);
 
   // The first chunk's weights stream while the tokens are rotated.  A wave
-  // that rotates a token loads it before its weights: loads return in order,
-  // so the token does not wait behind the weight stream.
-  if (t.wave < m) {
+  // that rotates a token loads it (and its sign bytes) before its weights:
+  // loads return in order, so the token does not wait behind the weight
+  // stream.
+  if constexpr (MW > 0) {
+    constexpr int NI = N / 512, CPW = NI / MW, RW = 8 * CPW;
+    static_assert(NI % MW == 0 && DEC_WAVES % MW == 0, "whole chunks and tokens per wavefront");
+    __shared__ __align__(16) float xb[DEC_WAVES / MW][N];  // one fp32 row per token (m <= 8 / MW)
+    __shared__ float wmax[DEC_WAVES];
+    const int L = t.lane;
+    const int tok = t.wave / MW, part = t.wave % MW;
+    const bool rot = tok < m;  // uniform per wavefront
+    uint2 sg[CPW];
+    uint4 raw[CPW];
+    if (rot) {
+      if constexpr (HAS_SIGNS) {
+        const int8_t* sp = signs + 512 * CPW * part + 8 * L;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) sg[i] = *reinterpret_cast<const uint2*>(sp + 512 * i);
+      }
+      load_row(raw, x + (int64_t)tok * N + 512 * CPW * part, L);
+    }
+    dec_issue_w(t, 0);
+    const RowLane rl = make_row_lane(L);
+    if (rot) {
+      float u[RW];
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        chunk_e0<HAS_SIGNS>(raw[i], sg[i], u + 8 * i);
+        chunk512_stages(*reinterpret_cast<float(*)[8]>(u + 8 * i), rl);
+      }
+#pragma unroll
+      for (int h = 8; h < RW; h <<= 1) butterfly_regs(u, h);  // chunk bits inside the wavefront
+      // element 512 chunk + p of register r: p = (r & 1) | (lane_pair << 1) |
+      // (r bit 2) << 7 | (r bit 1) << 8, chunk = part CPW + r / 8
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int e = 512 * (CPW * part + (r >> 3)) + ((r & 1) | (rl.lane_pair << 1) |
+                                                      (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8));
+        xb[tok][e] = u[r] * rl.sigma;
+      }
+    }
+    __syncthreads();
+    constexpr int PG = 256 * CPW;           // position pairs of a token (per local chunk)
+    constexpr int TT = 64 * MW;             // threads per token
+    constexpr int PGT = (PG + TT - 1) / TT; // pairs per thread (MW = 8: half the threads)
+    const int th = 64 * part + L;
+    float v[PGT][2][MW];
+    float amax = 0.0f;
+    if (rot) {
+#pragma unroll
+      for (int gi = 0; gi < PGT; ++gi) {
+        const int G = th + TT * gi;
+        if (G >= PG) continue;
+        const int a = G % 256, lc = G / 256;
+#pragma unroll
+        for (int sd = 0; sd < 2; ++sd) {
+#pragma unroll
+          for (int j = 0; j < MW; ++j) v[gi][sd][j] = xb[tok][512 * (lc + CPW * j) + 2 * a + sd];
+#pragma unroll
+          for (int h = 1; h < MW; h <<= 1) {  // chunk bits across wavefronts, ascending
+#pragma unroll
+            for (int j = 0; j < MW; ++j) {
+              if (!(j & h)) {
+                const float p0 = v[gi][sd][j], p1 = v[gi][sd][j + h];
+                v[gi][sd][j] = p0 + p1;
+                v[gi][sd][j + h] = p0 - p1;
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < MW; ++j) amax = fmaxf(amax, fabsf(v[gi][sd][j]));
+        }
+      }
+    }
+    amax = wave_max(amax);
+    if (L == 0) wmax[t.wave] = amax;
+    __syncthreads();
+    if (rot) {
+      float tmax = 0.0f;
+#pragma unroll
+      for (int w = 0; w < MW; ++w) tmax = fmaxf(tmax, wmax[MW * tok + w]);
+      const uint16_t hb = scale_fp16<7>(tmax * c32);
+      const bool subnormal = hb != 0 && hb < 0x0400u;
+      const float mult = hb == 0 ? 0.0f : c32 / h2f(hb);
+      if (th == 0) ascales[tok] = hb;
+#pragma unroll
+      for (int gi = 0; gi < PGT; ++gi) {
+        const int G = th + TT * gi;
+        if (G >= PG) continue;
+        const int a = G % 256, lc = G / 256;
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+          float t0 = __builtin_fmaf(v[gi][0][j], mult, kMagic);
+          float t1 = __builtin_fmaf(v[gi][1][j], mult, kMagic);
+          if (subnormal) {  // uniform: the scale is shared by the whole row
+            t0 = fminf(fmaxf(t0, kMagicLo), kMagicHi);
+            t1 = fminf(fmaxf(t1, kMagicLo), kMagicHi);
+          }
+          // (q1 + 8) << 4 | (q0 + 8), flipped to two's complement nibbles
+          acodes[tok][256 * (lc + CPW * j) + a] =
+              (unsigned char)(((f2u(t1) << 4) | (f2u(t0) & 0xFu)) ^ 0x88u);
+        }
+      }
+    }
+  } else if (t.wave < m) {
     uint2 sg[N / 512];
     if constexpr (HAS_SIGNS) load_signs(sg, signs, t.lane);
     uint4 raw[N / 512];
@@ -1233,12 +1347,13 @@ size_t linear_decode_workspace_bytes(int64_t m, int64_t d) {
 }
 
 namespace {
-template <int N, bool HAS_SIGNS, int RG>
+template <int N, bool HAS_SIGNS, int RG, int MW = 0>
 hipError_t launch_ld(const uint16_t* x, int64_t m, const int8_t* signs, const uint8_t* w_codes,
                      const uint16_t* w_scales, int64_t k, uint16_t* y, hipStream_t stream) {
   const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
   const int64_t grid = (k + 16 * RG - 1) / (16 * RG);
-  hipLaunchKernelGGL((w4a4_linear_decode_kernel<N, HAS_SIGNS, RG>), dim3((unsigned)grid),
+  if (MW > 0 && m > DEC_WAVES / (MW > 0 ? MW : 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((w4a4_linear_decode_kernel<N, HAS_SIGNS, RG, MW>), dim3((unsigned)grid),
                      dim3(64 * DEC_WAVES), 0, stream, reinterpret_cast<const __half*>(x), m, signs,
                      c32, w_codes, w_scales, k, y);
   return hipGetLastError();
@@ -1251,6 +1366,22 @@ hipError_t launch_ld_n(const uint16_t* x, int64_t m, const int8_t* signs, const 
   // workgroup: the kernel holds a whole row rotation, so fewer of its
   // workgroups fit on a CU than of the plain decode kernel.
   const bool rg2 = (k + 31) / 32 >= (int64_t)cu_count();
+  // n = 4096 with one workgroup per CU at most: one token is rotated by all
+  // 8 wavefronts, two tokens by 4 each (measured: 6.1 -> 5.2 us and 6.05 ->
+  // 5.9 us for k = 4096).  With 3 or 4 tokens, 2 wavefronts a token lost to
+  // one (the exchange and the finishing work outweigh the halved butterflies
+  // once two such wavefronts share a SIMD).  The fp32 rows this takes (16 KB
+  // a token) fit beside one 16-row weight group.
+  if constexpr (N == 4096) {
+    if (!rg2 && m <= 2 && (k + 15) / 16 <= (int64_t)cu_count()) {
+      const bool sg = signs != nullptr;
+      if (m == 1)
+        return sg ? launch_ld<N, true, 1, 8>(x, m, signs, w_codes, w_scales, k, y, stream)
+                  : launch_ld<N, false, 1, 8>(x, m, signs, w_codes, w_scales, k, y, stream);
+      return sg ? launch_ld<N, true, 1, 4>(x, m, signs, w_codes, w_scales, k, y, stream)
+                : launch_ld<N, false, 1, 4>(x, m, signs, w_codes, w_scales, k, y, stream);
+    }
+  }
   if (signs != nullptr)
     return rg2 ? launch_ld<N, true, 2>(x, m, signs, w_codes, w_scales, k, y, stream)
                : launch_ld<N, true, 1>(x, m, signs, w_codes, w_scales, k, y, stream);

@@ -281,12 +281,15 @@ def test_linear_decode_fused_matches_two_launches(rq):
 @pytest.mark.parametrize("m,k,d,with_signs", [(4, 5, 512, True), (3, 40, 8192, True),
                                               (2, 300, 1024, False), (1, 12300, 2048, True),
                                               (4, 14336, 4096, True), (16, 5, 512, True),
-                                              (7, 300, 1024, False)])
+                                              (7, 300, 1024, False), (1, 5, 4096, True),
+                                              (2, 300, 4096, False), (3, 40, 4096, True),
+                                              (4, 1000, 4096, False)])
 def test_linear_decode_fused_shapes(rq, m, k, d, with_signs):
     """One workgroup (k = 5), both weight-group widths (k = 12300, 14336 give
-    two 16-row groups per workgroup), every n class, no signs, and the
-    two-launch route (m > 4); y against the oracle's pipeline and against the
-    two-launch path."""
+    two 16-row groups per workgroup), every n class, no signs, the two-launch
+    route (m > 4), and n = 4096 with one 16-row group per workgroup, where 8
+    or 4 wavefronts rotate each token (m = 1, 2; one wavefront for m = 3, 4);
+    y against the oracle's pipeline and against the two-launch path."""
     rng = np.random.default_rng(m * 7 + k + d)
     x = (rng.standard_normal((m, d)) * np.where(rng.random(d) < 0.01, 50.0, 1.0)).astype(np.float16)
     wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
@@ -386,3 +389,33 @@ def test_kv_full_cache_sampled(rq):
 def test_zz_report():
     for r in REPORT:
         say(str(r))
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_linear_decode_fused_special_tokens(rq, m):
+    """Tokens whose scale is zero, fp16-subnormal (the code clamp) or infinite
+    (zero codes), at n = 4096 where several wavefronts rotate a token (m = 1,
+    2) or one does (m = 4): y is the two-launch path's, bit for bit."""
+    rng = np.random.default_rng(500 + m)
+    d, k = 4096, 64
+    signs = datagen.rademacher(rng, d)
+    sd = dev(signs)
+    # zero; fp16-subnormal values (a subnormal scale); 65504 times the signs
+    # (every signed element 65504: the first rotated value is 65504 * 64, whose
+    # scale overflows fp16); an ordinary token with outlier channels
+    rows = [np.zeros(d), rng.standard_normal(d) * 1e-6, 65504.0 * signs.astype(np.float64),
+            rng.standard_normal(d) * np.where(rng.random(d) < 0.01, 50.0, 1.0)]
+    x = np.stack(rows[1:2] if m == 1 else rows[:m]).astype(np.float16)
+    wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
+    say(f"fused decode linear special tokens m={m}")
+    wc, wsc, _ = rq.fold_weights(dev(wt), sd)
+    y = rq.linear_decode(dev(x), sd, wc, wsc)
+    torch.cuda.synchronize()
+    y_ref = rq.w4a4_linear(dev(x), sd, wc, wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    ac, sa, _ = rq.fwht_quant(dev(x), sd)
+    torch.cuda.synchronize()
+    sa = host(sa).view(np.uint16)
+    if m == 4:
+        assert sa[0] == 0 and 0 < sa[1] < 0x0400 and sa[2] == 0x7C00
