@@ -100,12 +100,13 @@ def test_weight_code_sums(rq):
         assert np.array_equal(sums.astype(np.int64), O.unpack_int4(wc).astype(np.int64).sum(axis=1))
 
 
-# ... (512, 448, 512) and (300, 456, 512): the persistent prefill kernel, full
-# 256 x 224 tiles (the LDS-staged store path on the second, non-debug call)
-# and edge tiles in both dimensions
+# ... (512, 448, 512), (300, 456, 512) and (128, 224, 256): the persistent
+# prefill kernel, full 256 x 224 tiles (the LDS-staged store path on the
+# second, non-debug call), edge tiles in both dimensions, and the smallest
+# shape (one edge tile, one step)
 ASYM_SHAPES = [(1, 1, 64), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
                (5, 33, 192), (17, 33, 64), (130, 129, 256), (300, 260, 1024),
-               (512, 448, 512), (300, 456, 512)]
+               (512, 448, 512), (300, 456, 512), (128, 224, 256)]
 
 
 @pytest.mark.parametrize("m,k,d", ASYM_SHAPES)

@@ -95,10 +95,11 @@ def test_fold_weights_grouped_decode_weights(rq):
 
 # decode kernel, tile kernel, and the persistent prefill kernel (m >= 128,
 # k >= 224, d a multiple of 256): full 256 x 224 tiles (LDS-staged stores),
-# edge tiles in both dimensions, and one tile over 64 groups
+# edge tiles in both dimensions, one tile over 64 groups, and the smallest
+# shape (one edge tile, two groups)
 GROUPED_SHAPES = [(1, 1, 256), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
                   (5, 33, 384), (17, 33, 128), (130, 129, 256), (300, 260, 1024),
-                  (512, 448, 512), (300, 456, 512), (256, 224, 8192)]
+                  (512, 448, 512), (300, 456, 512), (256, 224, 8192), (128, 224, 256)]
 
 
 @pytest.mark.parametrize("m,k,d", GROUPED_SHAPES)

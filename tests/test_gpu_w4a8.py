@@ -116,10 +116,11 @@ def test_fwht_quant8_ties_round_to_even(rq):
 # d not a multiple of 256) with ragged edges; the persistent prefill kernel
 # (m >= 128, k >= 224, d a multiple of 256) with full 256 x 224 tiles (the
 # LDS-staged store path on the second, non-debug call), edge tiles in both
-# dimensions, and one tile over 64 steps of 128 codes
+# dimensions, one tile over 64 steps of 128 codes, and the smallest shape
+# (one edge tile, two steps)
 GEMM8_SHAPES = [(1, 1, 64), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
                 (5, 33, 192), (17, 33, 64), (130, 129, 256), (300, 260, 1024), (129, 257, 4160),
-                (512, 448, 512), (300, 456, 512), (256, 224, 8192)]
+                (512, 448, 512), (300, 456, 512), (256, 224, 8192), (128, 224, 256)]
 
 
 @pytest.mark.parametrize("m,k,d", GEMM8_SHAPES)
