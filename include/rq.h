@@ -352,7 +352,10 @@ int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, u
  *   a_codes         [m][d/2] (rq_fwht_quant), 16-byte aligned; a_scales [m].
  *   w_codes         [k][d/2] (rq_quantize_groups on the folded weights),
  *                   16-byte aligned.
- *   w_group_scales  [k][d / 128] fp16.
+ *   w_group_scales  [k][d / 128] fp16, 2-byte aligned (with 4-byte alignment,
+ *                   shapes with m >= 128, k >= 224 and d a multiple of 256
+ *                   run on the persistent prefill kernel, which reads scale
+ *                   pairs as dwords; otherwise on the tile kernel).
  *   m >= 0; k >= 1 when m > 0; d a multiple of 128 in [128, 16384].
  *   y               [m][k] fp16 output.
  */

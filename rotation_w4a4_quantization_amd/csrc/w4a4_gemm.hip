@@ -1299,7 +1299,9 @@ hipError_t launch_gemm_variant(const uint8_t* a, const uint16_t* a_scales, const
 hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                                     const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
                                     int64_t d, uint16_t* y, hipStream_t stream) {
-  if (large_shape(m, k, d))  // the persistent prefill kernel: a half step is one group
+  // the persistent prefill kernel (a half step is one group) reads each row's
+  // two group scales of a step as one dword: 4-byte aligned scales only
+  if (large_shape(m, k, d) && (reinterpret_cast<uintptr_t>(wg_scales) & 3u) == 0)
     return launch_large<kA4, true>(a_codes, a_scales, nullptr, m, w_codes, wg_scales, nullptr, k,
                                    d, y, nullptr, stream);
   if (m <= 16 && d % (2 * DSEG) == 0) {

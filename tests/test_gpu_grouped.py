@@ -117,6 +117,26 @@ def test_w4a4_gemm_grouped_random_codes(rq, m, k, d):
     assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
 
 
+def test_grouped_prefill_scales_2_byte_aligned(rq):
+    # group scales at an address that is 2 but not 4 modulo 4: the prefill
+    # shape takes the tile kernel (the persistent kernel reads scale pairs
+    # as dwords); the result is the aligned call's up to summation order
+    rng = np.random.default_rng(41)
+    m, k, d = 256, 224, 512
+    ac = datagen.random_codes(rng, m, d)
+    wc = datagen.random_codes(rng, k, d)
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k * (d // 128)).reshape(k, d // 128)
+    buf = torch.empty(k * (d // 128) + 1, dtype=torch.float16, device="cuda")
+    buf[1:] = dev(sw.reshape(-1))
+    sw_mis = buf[1:].view(k, d // 128)
+    assert sw_mis.data_ptr() % 4 == 2
+    say("grouped gemm, 2-byte aligned group scales")
+    y = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), sw_mis)
+    torch.cuda.synchronize()
+    check_gemm_grouped(ac, sa, wc, sw, host(y), "grouped misaligned scales")
+
+
 @pytest.mark.parametrize("m,k,d", [(4, 64, 4096), (256, 224, 4096)])
 def test_grouped_equal_scales_match_per_channel(rq, m, k, d):
     # equal group scales in a row: the grouped GEMM is the per-channel GEMM
