@@ -248,18 +248,6 @@ __device__ __forceinline__ void chunk512_stages(float (&c)[8], const RowLane& rl
   }
 }
 
-// Rotates and quantises the row whose chunks `raw` holds (loaded by
-// load_row, after the sign bytes `sg` were loaded by load_signs; sg is unused
-// without signs): lane 0 writes the fp16 scale to *scale_out, the wavefront writes
-// the code bytes (n/2 packed INT4 codes, or n INT8 codes for BITS == 8) to
-// codes_row through its LDS slice cb (as many bytes), or, with TO_LDS, leaves
-// them in cb (codes_row unused), and the fp32 rotated row goes to xrot_row
-// when it is not null.
-//
-// ASYM (INT4 only): the asymmetric quantiser.  The row range [lo, hi] is
-// widened to contain 0, the step is fp16(fp32(hi - lo) / 15) rounded once,
-// the zero point z = rne(-lo / step) (lane 0 writes it to *zero_out), and the
-// codes are the unsigned nibbles clamp(rne(x / step) + z, 0, 15).
 // Signs and stage e0 of one 16-byte chunk (8 fp16 elements of a lane): the
 // sign flip is an xor on each fp16 pair, then v_fma_mix_f32 gives the pair's
 // sum and difference in fp32, one rounding each.
@@ -296,6 +284,52 @@ __device__ __forceinline__ void load_signs(uint2 (&sg)[NI], const int8_t* __rest
   }
 }
 
+// Stages e0 .. e8 of NI chunks (lane L's 16-byte chunk i at register
+// 8 i .. 8 i + 7) chunk by chunk in load order, so chunk i is worked on while
+// later chunks are in flight.  With PROGRESSIVE the stages between chunks
+// (e9 .., chunk j with chunk j + h for h = 1, 2, 4, ...) also run as soon as
+// their chunks are done: once chunks i + 1 - 2h .. i have had the stages
+// below h, that block's stage for h runs, so little is left once the last
+// chunk is in.
+template <int NI, bool HAS_SIGNS, bool PROGRESSIVE>
+__device__ __forceinline__ void chunk_major_stages(const uint4 (&raw)[NI], const uint2 (&sg)[NI],
+                                                   const RowLane& rl, float* u) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float* c = u + 8 * i;
+    chunk_e0<HAS_SIGNS>(raw[i], sg[i], c);
+    chunk512_stages(*reinterpret_cast<float(*)[8]>(c), rl);
+#pragma unroll
+    for (int h = 1; h < NI; h <<= 1) {
+      if (PROGRESSIVE && (i + 1) % (2 * h) == 0) {
+#pragma unroll
+        for (int j = i + 1 - 2 * h; j < i + 1 - h; ++j) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const float a = u[8 * j + r], b = u[8 * (j + h) + r];
+            u[8 * j + r] = a + b;
+            u[8 * (j + h) + r] = a - b;
+          }
+        }
+      }
+    }
+    // keeps the next chunk's first use (and so its wait) after this chunk
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Rotates and quantises the row whose chunks `raw` holds (loaded by
+// load_row, after the sign bytes `sg` were loaded by load_signs; sg is unused
+// without signs): lane 0 writes the fp16 scale to *scale_out, the wavefront writes
+// the code bytes (n/2 packed INT4 codes, or n INT8 codes for BITS == 8) to
+// codes_row through its LDS slice cb (as many bytes), or, with TO_LDS, leaves
+// them in cb (codes_row unused), and the fp32 rotated row goes to xrot_row
+// when it is not null.
+//
+// ASYM (INT4 only): the asymmetric quantiser.  The row range [lo, hi] is
+// widened to contain 0, the step is fp16(fp32(hi - lo) / 15) rounded once,
+// the zero point z = rne(-lo / step) (lane 0 writes it to *zero_out), and the
+// codes are the unsigned nibbles clamp(rne(x / step) + z, 0, 15).
 template <int N, bool HAS_SIGNS, bool TO_LDS = false, int BITS = 4, bool ASYM = false>
 __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
                                                  const uint2 (&sg)[N / 512], int L,
@@ -325,34 +359,11 @@ __device__ __forceinline__ void row_rotate_quant(const uint4 (&raw)[N / 512],
   // the compiler spills with it), else after the last chunk.
   constexpr bool kProgressive = kChunked && NI <= 8;
   float u[R];
+  if constexpr (kChunked) {
+    chunk_major_stages<NI, HAS_SIGNS, kProgressive>(raw, sg, rl, u);
+  } else {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    float* c = u + 8 * i;
-    chunk_e0<HAS_SIGNS>(raw[i], sg[i], c);
-    if constexpr (kChunked) {
-      chunk512_stages(*reinterpret_cast<float(*)[8]>(c), rl);
-      // e9..: chunk j pairs with chunk j + h (h = 1, 2, 4, ...).  Once chunks
-      // i + 1 - 2h .. i have all had the stages below h, that block's stage
-      // for h runs, so little is left once the last chunk is in.
-#pragma unroll
-      for (int h = 1; h < NI; h <<= 1) {
-        if (kProgressive && (i + 1) % (2 * h) == 0) {
-#pragma unroll
-          for (int j = i + 1 - 2 * h; j < i + 1 - h; ++j) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const float a = u[8 * j + r], b = u[8 * (j + h) + r];
-              u[8 * j + r] = a + b;
-              u[8 * (j + h) + r] = a - b;
-            }
-          }
-        }
-      }
-      // keeps the next chunk's first use (and so its wait) after this chunk
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  if constexpr (!kChunked) {
+    for (int i = 0; i < NI; ++i) chunk_e0<HAS_SIGNS>(raw[i], sg[i], u + 8 * i);
     const float(&g)[4] = rl.g;
     butterfly_regs(u, 2);  // e1
     butterfly_regs(u, 4);  // e2

@@ -111,8 +111,8 @@ def test_linear_28x512(rq, m, k):
     check_gemm(host(ac), host(sa), host(wc), host(ws), host(y), host(acc), what="gemm d=28x512")
 
 
-def test_fwht_quant_special_rows(rq):
-    n = 4096
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_fwht_quant_special_rows(rq, n):
     rng = np.random.default_rng(5)
     signs = datagen.rademacher(rng, n)
     x = np.zeros((8, n), np.float32)
@@ -123,9 +123,9 @@ def test_fwht_quant_special_rows(rq):
     x[5] = -x[5 - 4]
     x[6] = rng.standard_normal(n)
     x[7, :] = 2.0                         # constant row: all energy in element 0
-    say("fwht_quant special rows")
+    say(f"fwht_quant special rows n={n}")
     c, s, r = run_fq(rq, x, signs)
-    check_rotation_result(x, signs, c, s, r, what="special rows")
+    check_rotation_result(x, signs, c, s, r, what=f"special rows n={n}")
     q = O.unpack_int4(c)
     assert set(np.abs(q[1]).tolist()) == {7}
     assert not q[0].any() and not q[2].any()
