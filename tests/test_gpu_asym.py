@@ -164,3 +164,28 @@ def test_asym_empty(rq):
     c, s, z, _ = rq.fwht_quant_asym(torch.zeros((0, 512), dtype=torch.float16, device="cuda"))
     assert c.shape == (0, 256) and z.shape == (0,)
     torch.cuda.synchronize()
+
+
+def test_asym_prefill_full_size_sampled(rq):
+    # the prefill configuration with asymmetric activations, launched as the
+    # benchmark does (the persistent kernel with the zero-point epilogue):
+    # exact accumulators and y on every row x sampled columns and sampled
+    # rows x every column
+    w = datagen.prefill_linear(0)
+    s = dev(w["signs"])
+    say("asym prefill: fold 28672x8192, asymmetric rotation of 2048x8192")
+    wc, ws, _ = rq.fold_weights(dev(w["wt"]), s)
+    wsum = rq.weight_code_sums(wc)
+    ac, sa, za, _ = rq.fwht_quant_asym(dev(w["x"]), s)
+    say("asym prefill: gemm 2048x8192 -> 28672")
+    y, acc = rq.w4a4_gemm_asym(ac, sa, za, wc, ws, wsum, debug=True)
+    y2, _ = rq.w4a4_gemm_asym(ac, sa, za, wc, ws, wsum)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    del y2, wsum
+    ac, sa, za, wc, ws, y, acc = map(host, (ac, sa, za, wc, ws, y, acc))
+    rng = np.random.default_rng(79)
+    rows = np.sort(rng.choice(2048, 128, replace=False))
+    cols = np.sort(rng.choice(28672, 256, replace=False))
+    check_gemm_asym(ac, sa, za, wc[cols], ws[cols], y[:, cols], acc[:, cols], "asym prefill cols")
+    check_gemm_asym(ac[rows], sa[rows], za[rows], wc, ws, y[rows], acc[rows], "asym prefill rows")

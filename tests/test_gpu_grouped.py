@@ -166,3 +166,24 @@ def test_grouped_decode_linear_end_to_end(rq):
             torch.cuda.synchronize()
             check_gemm_grouped(host(ac[:m]), host(sa[:m]), host(wc), host(ws), host(y),
                                f"grouped decode m={m} k={k}")
+
+
+def test_grouped_prefill_full_size_sampled(rq):
+    # the prefill configuration with per-group (128) weight scales, launched
+    # as the benchmark does (the persistent kernel): y on every row x sampled
+    # columns and sampled rows x every column (the oracle keeps one int64 sum
+    # per group, so the samples are smaller than for the other GEMMs)
+    w = datagen.prefill_linear(0)
+    s = dev(w["signs"])
+    say("grouped prefill: fold 28672x8192 with group scales, rotation of 2048x8192")
+    wc, wsg = rq.fold_weights_grouped(dev(w["wt"]), s, 128)
+    ac, sa, _ = rq.fwht_quant(dev(w["x"]), s)
+    say("grouped prefill: gemm 2048x8192 -> 28672")
+    y = rq.w4a4_gemm_grouped(ac, sa, wc, wsg)
+    torch.cuda.synchronize()
+    ac, sa, wc, wsg, y = map(host, (ac, sa, wc, wsg, y))
+    rng = np.random.default_rng(80)
+    rows = np.sort(rng.choice(2048, 16, replace=False))
+    cols = np.sort(rng.choice(28672, 64, replace=False))
+    check_gemm_grouped(ac, sa, wc[cols], wsg[cols], y[:, cols], "grouped prefill cols")
+    check_gemm_grouped(ac[rows], sa[rows], wc, wsg, y[rows], "grouped prefill rows")

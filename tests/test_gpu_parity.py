@@ -386,11 +386,6 @@ def test_kv_full_cache_sampled(rq):
                               what=f"kv {name} sampled", rows=rows, report=REPORT)
 
 
-def test_zz_report():
-    for r in REPORT:
-        say(str(r))
-
-
 @pytest.mark.parametrize("m", [1, 2, 4])
 def test_linear_decode_fused_special_tokens(rq, m):
     """Tokens whose scale is zero, fp16-subnormal (the code clamp) or infinite
@@ -419,3 +414,8 @@ def test_linear_decode_fused_special_tokens(rq, m):
     sa = host(sa).view(np.uint16)
     if m == 4:
         assert sa[0] == 0 and 0 < sa[1] < 0x0400 and sa[2] == 0x7C00
+
+
+def test_zz_report():
+    for r in REPORT:
+        say(str(r))

@@ -197,3 +197,26 @@ def test_w4a8_empty(rq):
                         torch.ones((5,), dtype=torch.float16, device="cuda"))
     assert y.shape == (0, 5)
     torch.cuda.synchronize()
+
+
+def test_w4a8_prefill_full_size_sampled(rq):
+    # the prefill configuration, launched as the benchmark does (the
+    # persistent kernel with LDS-staged stores, 128-code steps): the oracle on
+    # every row x sampled columns and sampled rows x every column
+    w = datagen.prefill_linear(0)
+    s = dev(w["signs"])
+    say("w4a8 prefill: fold 28672x8192, INT8 rotation of 2048x8192")
+    wc, ws, _ = rq.fold_weights(dev(w["wt"]), s)
+    a8, sa, _ = rq.fwht_quant8(dev(w["x"]), s)
+    say("w4a8 prefill: gemm 2048x8192 -> 28672")
+    y, acc = rq.w4a8_gemm(a8, sa, wc, ws, debug=True)
+    y2, _ = rq.w4a8_gemm(a8, sa, wc, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    del y2
+    a8, sa, wc, ws, y, acc = map(host, (a8, sa, wc, ws, y, acc))
+    rng = np.random.default_rng(78)
+    rows = np.sort(rng.choice(2048, 128, replace=False))
+    cols = np.sort(rng.choice(28672, 256, replace=False))
+    check_gemm(a8, sa, wc, ws, y, acc, what="w4a8 prefill cols", cols=cols, a8=True)
+    check_gemm(a8, sa, wc, ws, y, acc, what="w4a8 prefill rows", rows=rows, a8=True)
