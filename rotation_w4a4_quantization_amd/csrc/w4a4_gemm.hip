@@ -497,30 +497,44 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
 template <int RG>
 __device__ __forceinline__ void dec_mma_chunk_grouped(const DecLane<RG>& t,
                                                       const unsigned char* wl,
-                                                      const uint8_t* a_src, bool a_ok,
-                                                      int64_t c0,
+                                                      const uint8_t* a_src, int64_t c0,
                                                       const uint16_t* __restrict__ wg_scales,
                                                       int64_t ngroups, int64_t k,
                                                       v4f (&facc)[RG]) {
   constexpr int SEGB = 16 * RG * DSEG;
+  // Every load is unconditional, from a clamped address that is always
+  // valid: rows past m re-read row 0 (a_src) and feed only outputs that are
+  // not stored, and parts past the end are skipped below.  A zeroed register
+  // refilled by a load under a branch would get a wait for every load in
+  // flight (the weight stream included, which the compiler cannot see).
   uint4 av[2][2];
   uint16_t sc[2][2][RG];
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     const int64_t seg = c0 + 2 * t.wave + sl;
+    const int64_t segc = seg < t.nseg ? seg : t.nseg - 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      av[sl][h] = make_uint4(0, 0, 0, 0);
-      if (a_ok && seg < t.nseg)
-        av[sl][h] = *reinterpret_cast<const uint4*>(a_src + seg * DSEG + 64 * h);
+      av[sl][h] = *reinterpret_cast<const uint4*>(a_src + segc * DSEG + 64 * h);
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         const int64_t col = t.n0 + 16 * q + t.r16;
-        sc[sl][h][q] = 0;
-        if (seg < t.nseg) sc[sl][h][q] = wg_scales[(col < k ? col : k - 1) * ngroups + 2 * seg + h];
+        sc[sl][h][q] = wg_scales[(col < k ? col : k - 1) * ngroups + 2 * segc + h];
       }
     }
   }
+  // The loads read kernel arguments the compiler treats as invariant, so it
+  // may sink them past the wait below into their uses (each then pays a
+  // memory latency of its own): an empty asm that takes every loaded value
+  // keeps them issued before the wait.
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      asm volatile("" ::"v"(av[sl][h].x), "v"(av[sl][h].y), "v"(av[sl][h].z), "v"(av[sl][h].w));
+#pragma unroll
+      for (int q = 0; q < RG; ++q) asm volatile("" ::"v"(sc[sl][h][q]));
+    }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
@@ -562,7 +576,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
   for (int q = 0; q < RG; ++q) facc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
     dec_issue_w(t, c0);
-    dec_mma_chunk_grouped<RG>(t, wl, a_src, a_ok, c0, wg_scales, ngroups, k, facc);
+    dec_mma_chunk_grouped<RG>(t, wl, a_src, c0, wg_scales, ngroups, k, facc);
   }
 #pragma unroll
   for (int q = 0; q < RG; ++q) partial[t.wave][q][t.lane] = facc[q];
