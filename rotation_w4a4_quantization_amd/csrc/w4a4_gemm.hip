@@ -1038,13 +1038,34 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     int tid_o = tid;
     asm volatile("" : "+v"(tid_o));
     const int g = (tid_o & 63) >> 4, r16 = tid_o & 15;
+    // Every scale, zero point and code sum the epilogue needs is loaded here,
+    // unconditionally, from a clamped row or column that is always valid (past
+    // m or k the value is dropped): a load under a branch gets a wait of its
+    // own, and loads issued after the first stores would wait for those
+    // (vector-memory counts drain in issue order), so one batch means one
+    // memory round trip per tile instead of one per load.
+    float sav[4][4];
+    int32_t zv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t arow = m0 + wm * 64 + i * 16 + 4 * g + e;
+        const int64_t arowc = arow < m ? arow : m - 1;
+        sav[i][e] = h2f(a_scales[arowc]);
+        zv[i][e] = AM == kAU4 ? (int32_t)a_zeros[arowc] : 0;
+      }
+    }
     float swv[7];
     int32_t wsv[7];  // weight code sums (asymmetric activations only)
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       const int64_t col = n0 + wn * 112 + j * 16 + r16;
-      swv[j] = !GROUPED && col < k ? h2f(w_scales[col]) : 0.0f;
-      wsv[j] = AM == kAU4 && col < k ? w_sums[col] : 0;
+      const int64_t colc = col < k ? col : k - 1;
+      const float sw = GROUPED ? 0.0f : h2f(w_scales[colc]);
+      const int32_t ws = AM == kAU4 ? w_sums[colc] : 0;
+      swv[j] = col < k ? sw : 0.0f;
+      wsv[j] = col < k ? ws : 0;
     }
     const bool full = m0 + LM <= m && n0 + LN <= k;
     if (full && wide_store) {
@@ -1053,20 +1074,6 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
       // stores.  Half h holds row groups 2h and 2h + 1 of every wave: staging
       // row tr is tile row (tr / 32) * 64 + 32 h + tr % 32.
       unsigned char* stg = lds + (A8 ? STAGE : (par ^ 1) * BUFS);
-      // Every activation scale (and zero point) of both halves is loaded up
-      // front: loads issued after half 0's stores would wait for them
-      // (vector-memory counts drain in issue order).
-      float sav[4][4];
-      int32_t zv[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t arow = m0 + wm * 64 + i * 16 + 4 * g + e;
-          sav[i][e] = h2f(a_scales[arow]);
-          zv[i][e] = AM == kAU4 ? (int32_t)a_zeros[arow] : 0;
-        }
-      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -1106,8 +1113,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
         for (int e = 0; e < 4; ++e) {
           const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
           if (!full && row >= m) continue;
-          const float sa = h2f(a_scales[row]);
-          const int32_t z = AM == kAU4 ? (int32_t)a_zeros[row] : 0;
+          const float sa = sav[i][e];
+          const int32_t z = zv[i][e];
           const int64_t base = row * k + n0 + wn * 112 + r16;
 #pragma unroll
           for (int j = 0; j < 7; ++j) {
