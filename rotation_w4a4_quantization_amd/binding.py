@@ -138,7 +138,46 @@ def _signs(signs, n, device):
     return signs
 
 
-def _rotate_quant(cfunc: str, x: torch.Tensor, signs, debug: bool):
+def _out(name: str, t, shape, dtype, device) -> torch.Tensor:
+    """A caller-supplied output tensor, checked before anything is launched
+    (dtype, exact shape, device, contiguity), or a new one when t is None."""
+    shape = tuple(int(v) for v in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if not t.is_cuda or t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _outs(names, shapes, dtypes, device, out):
+    """Unpack an `out=` tuple (or None) into checked output tensors."""
+    if out is None:
+        out = (None,) * len(names)
+    if not isinstance(out, (tuple, list)) or len(out) != len(names):
+        raise ValueError(f"out must be a tuple ({', '.join(names)})")
+    return tuple(_out(n, t, sh, dt, device) for n, t, sh, dt in zip(names, out, shapes, dtypes))
+
+
+def _workspace(t, nbytes: int, device) -> torch.Tensor:
+    """A caller-supplied device workspace (uint8, contiguous, at least nbytes)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if not t.is_cuda or t.device != torch.device(device) or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if t.numel() < nbytes:
+        raise ValueError(f"workspace holds {t.numel()} bytes, {nbytes} are needed")
+    return t
+
+
+def _rotate_quant(cfunc: str, x: torch.Tensor, signs, debug: bool, out=None):
     _need_cuda("x", x)
     if x.dtype not in (torch.float16, torch.float32):
         raise ValueError("x must be float16 or float32")
@@ -146,9 +185,12 @@ def _rotate_quant(cfunc: str, x: torch.Tensor, signs, debug: bool):
         raise ValueError("x must be 2-D [rows, n]")
     rows, n = x.shape
     s = _signs(signs, n, x.device)
-    codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows,), dtype=torch.float16, device=x.device)
-    rot = torch.empty((rows, n), dtype=torch.float32, device=x.device) if debug else None
+    names = ("codes", "scales") + (("x_rot",) if debug else ())
+    shapes = ((rows, n // 2), (rows,), (rows, n))
+    dtypes = (torch.uint8, torch.float16, torch.float32)
+    outs = _outs(names, shapes[:len(names)], dtypes[:len(names)], x.device, out)
+    codes, scales = outs[0], outs[1]
+    rot = outs[2] if debug else None
     dtype = RQ_F16 if x.dtype == torch.float16 else RQ_F32
     st = getattr(load_library(), cfunc)(_ptr(x), dtype, rows, n, _ptr(s), _ptr(codes),
                                         _ptr(scales), _ptr(rot), _stream())
@@ -156,19 +198,24 @@ def _rotate_quant(cfunc: str, x: torch.Tensor, signs, debug: bool):
     return codes, scales, rot
 
 
-def fwht_quant(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
-    """rq_fwht_quant: returns (codes uint8 [m, n/2], scales fp16 [m], x_rot fp32 or None)."""
-    return _rotate_quant("rq_fwht_quant", x, signs, debug)
+def fwht_quant(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False,
+               out=None):
+    """rq_fwht_quant: returns (codes uint8 [m, n/2], scales fp16 [m], x_rot fp32 or None).
+    `out` optionally gives the output tensors (codes, scales[, x_rot])."""
+    return _rotate_quant("rq_fwht_quant", x, signs, debug, out)
 
 
-def fold_weights(wt: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+def fold_weights(wt: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False,
+                 out=None):
     """rq_fold_weights on W^T [k][d]: returns (codes [k, d/2], scales [k], w_rot or None)."""
-    return _rotate_quant("rq_fold_weights", wt, signs, debug)
+    return _rotate_quant("rq_fold_weights", wt, signs, debug, out)
 
 
 def w4a4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
-              w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
-    """rq_w4a4_gemm: returns (y fp16 [m, k], acc int32 [m, k] or None)."""
+              w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None,
+              acc_out: torch.Tensor | None = None):
+    """rq_w4a4_gemm: returns (y fp16 [m, k], acc int32 [m, k] or None).
+    `out` / `acc_out` optionally give y and (with debug) the accumulators."""
     for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes),
                     ("w_scales", w_scales)):
         _need_cuda(name, t)
@@ -186,18 +233,20 @@ def w4a4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
     lib = load_library()
     ws_bytes = int(lib.rq_w4a4_gemm_workspace_size(m, k, d))
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=a_codes.device) if ws_bytes else None
-    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
-    acc = torch.empty((m, k), dtype=torch.int32, device=a_codes.device) if debug else None
+    y = _out("out", out, (m, k), torch.float16, a_codes.device)
+    acc = _out("acc_out", acc_out, (m, k), torch.int32, a_codes.device) if debug else None
     st = lib.rq_w4a4_gemm(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes), _ptr(w_scales), k, d,
                           _ptr(y), _ptr(acc), _ptr(ws), ws_bytes, _stream())
     _check("rq_w4a4_gemm", st)
     return y, acc
 
 
-def kv_rotate_quant(k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor | None = None):
+def kv_rotate_quant(k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor | None = None,
+                    out=None):
     """rq_kv_rotate_quant on fp16 [..., 128] K and V.
 
-    Returns (k_codes [..., 64], k_scales [...], v_codes, v_scales)."""
+    Returns (k_codes [..., 64], k_scales [...], v_codes, v_scales); `out`
+    optionally gives those four tensors."""
     _need_cuda("k", k)
     _need_cuda("v", v)
     if k.dtype != torch.float16 or v.dtype != torch.float16 or k.shape != v.shape:
@@ -206,10 +255,9 @@ def kv_rotate_quant(k: torch.Tensor, v: torch.Tensor, signs: torch.Tensor | None
     rows = k.numel() // head_dim
     s = _signs(signs, head_dim, k.device)
     lead = tuple(k.shape[:-1])
-    kc = torch.empty(lead + (head_dim // 2,), dtype=torch.uint8, device=k.device)
-    vc = torch.empty_like(kc)
-    ks = torch.empty(lead, dtype=torch.float16, device=k.device)
-    vs = torch.empty_like(ks)
+    kc, ks, vc, vs = _outs(("k_codes", "k_scales", "v_codes", "v_scales"),
+                           (lead + (head_dim // 2,), lead, lead + (head_dim // 2,), lead),
+                           (torch.uint8, torch.float16, torch.uint8, torch.float16), k.device, out)
     st = load_library().rq_kv_rotate_quant(_ptr(k), _ptr(v), rows, head_dim, _ptr(s), _ptr(kc),
                                            _ptr(ks), _ptr(vc), _ptr(vs), _stream())
     _check("rq_kv_rotate_quant", st)
@@ -250,15 +298,18 @@ def linear_decode(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Te
     if half_d * 2 != d or w_scales.numel() != k:
         raise ValueError("weight codes do not match x")
     s = _signs(signs, d, x.device)
-    ws = workspace if workspace is not None else linear_decode_workspace(m, d, x.device)
-    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=x.device)
+    need = int(load_library().rq_linear_decode_workspace_size(m, d))
+    ws = _workspace(workspace, need, x.device) if workspace is not None else \
+        linear_decode_workspace(m, d, x.device)
+    y = _out("out", out, (m, k), torch.float16, x.device)
     st = load_library().rq_linear_decode(_ptr(x), m, d, _ptr(s), _ptr(w_codes), _ptr(w_scales), k,
                                          _ptr(y), _ptr(ws), ws.numel(), _stream())
     _check("rq_linear_decode", st)
     return y
 
 
-def fwht_quant8(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+def fwht_quant8(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False,
+                out=None):
     """rq_fwht_quant8 (W4A8 activations): returns (codes int8 [m, n],
     scales fp16 [m], x_rot fp32 or None)."""
     _need_cuda("x", x)
@@ -266,9 +317,11 @@ def fwht_quant8(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool 
         raise ValueError("x must be a float16 [rows, n] tensor")
     rows, n = x.shape
     s = _signs(signs, n, x.device)
-    codes = torch.empty((rows, n), dtype=torch.int8, device=x.device)
-    scales = torch.empty((rows,), dtype=torch.float16, device=x.device)
-    rot = torch.empty((rows, n), dtype=torch.float32, device=x.device) if debug else None
+    names = ("codes", "scales") + (("x_rot",) if debug else ())
+    outs = _outs(names, ((rows, n), (rows,), (rows, n))[:len(names)],
+                 (torch.int8, torch.float16, torch.float32)[:len(names)], x.device, out)
+    codes, scales = outs[0], outs[1]
+    rot = outs[2] if debug else None
     st = load_library().rq_fwht_quant8(_ptr(x), rows, n, _ptr(s), _ptr(codes), _ptr(scales),
                                        _ptr(rot), _stream())
     _check("rq_fwht_quant8", st)
@@ -276,7 +329,8 @@ def fwht_quant8(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool 
 
 
 def w4a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
-              w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None):
+              w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None,
+              acc_out: torch.Tensor | None = None):
     """rq_w4a8_gemm: INT8 activation codes [m, d] times packed INT4 weight
     codes [k, d/2]; returns (y fp16 [m, k], acc int32 [m, k] or None)."""
     for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes),
@@ -292,8 +346,8 @@ def w4a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
         raise ValueError("activation and weight codes differ in d")
     if a_scales.numel() != m or w_scales.numel() != k:
         raise ValueError("scale counts do not match the code rows")
-    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
-    acc = torch.empty((m, k), dtype=torch.int32, device=a_codes.device) if debug else None
+    y = _out("out", out, (m, k), torch.float16, a_codes.device)
+    acc = _out("acc_out", acc_out, (m, k), torch.int32, a_codes.device) if debug else None
     st = load_library().rq_w4a8_gemm(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes),
                                      _ptr(w_scales), k, d, _ptr(y), _ptr(acc), _stream())
     _check("rq_w4a8_gemm", st)
@@ -309,7 +363,8 @@ def w4a8_linear(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tens
     return y
 
 
-def fwht_quant_asym(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False):
+def fwht_quant_asym(x: torch.Tensor, signs: torch.Tensor | None = None, debug: bool = False,
+                    out=None):
     """rq_fwht_quant_asym: returns (codes uint8 [m, n/2] unsigned nibbles,
     scales fp16 [m], zeros uint8 [m], x_rot fp32 or None)."""
     _need_cuda("x", x)
@@ -317,23 +372,25 @@ def fwht_quant_asym(x: torch.Tensor, signs: torch.Tensor | None = None, debug: b
         raise ValueError("x must be a float16 [rows, n] tensor")
     rows, n = x.shape
     s = _signs(signs, n, x.device)
-    codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows,), dtype=torch.float16, device=x.device)
-    zeros = torch.empty((rows,), dtype=torch.uint8, device=x.device)
-    rot = torch.empty((rows, n), dtype=torch.float32, device=x.device) if debug else None
+    names = ("codes", "scales", "zeros") + (("x_rot",) if debug else ())
+    outs = _outs(names, ((rows, n // 2), (rows,), (rows,), (rows, n))[:len(names)],
+                 (torch.uint8, torch.float16, torch.uint8, torch.float32)[:len(names)], x.device,
+                 out)
+    codes, scales, zeros = outs[:3]
+    rot = outs[3] if debug else None
     st = load_library().rq_fwht_quant_asym(_ptr(x), rows, n, _ptr(s), _ptr(codes), _ptr(scales),
                                            _ptr(zeros), _ptr(rot), _stream())
     _check("rq_fwht_quant_asym", st)
     return codes, scales, zeros, rot
 
 
-def weight_code_sums(w_codes: torch.Tensor) -> torch.Tensor:
+def weight_code_sums(w_codes: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """rq_weight_code_sums: int32 [k] sums of the signed INT4 codes per row."""
     _need_cuda("w_codes", w_codes)
     if w_codes.dtype != torch.uint8 or w_codes.dim() != 2:
         raise ValueError("w_codes must be a uint8 [k, d/2] tensor")
     k, half_d = w_codes.shape
-    sums = torch.empty((k,), dtype=torch.int32, device=w_codes.device)
+    sums = _out("out", out, (k,), torch.int32, w_codes.device)
     st = load_library().rq_weight_code_sums(_ptr(w_codes), k, 2 * half_d, _ptr(sums), _stream())
     _check("rq_weight_code_sums", st)
     return sums
@@ -341,7 +398,8 @@ def weight_code_sums(w_codes: torch.Tensor) -> torch.Tensor:
 
 def w4a4_gemm_asym(a_codes: torch.Tensor, a_scales: torch.Tensor, a_zeros: torch.Tensor,
                    w_codes: torch.Tensor, w_scales: torch.Tensor, w_sums: torch.Tensor,
-                   debug: bool = False, out: torch.Tensor | None = None):
+                   debug: bool = False, out: torch.Tensor | None = None,
+                   acc_out: torch.Tensor | None = None):
     """rq_w4a4_gemm_asym: returns (y fp16 [m, k], acc int32 [m, k] or None)."""
     for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("a_zeros", a_zeros),
                     ("w_codes", w_codes), ("w_scales", w_scales), ("w_sums", w_sums)):
@@ -355,8 +413,8 @@ def w4a4_gemm_asym(a_codes: torch.Tensor, a_scales: torch.Tensor, a_zeros: torch
     if half_d != half_d2 or a_scales.numel() != m or a_zeros.numel() != m or \
             w_scales.numel() != k or w_sums.numel() != k:
         raise ValueError("shapes do not match")
-    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
-    acc = torch.empty((m, k), dtype=torch.int32, device=a_codes.device) if debug else None
+    y = _out("out", out, (m, k), torch.float16, a_codes.device)
+    acc = _out("acc_out", acc_out, (m, k), torch.int32, a_codes.device) if debug else None
     st = load_library().rq_w4a4_gemm_asym(_ptr(a_codes), _ptr(a_scales), _ptr(a_zeros), m,
                                           _ptr(w_codes), _ptr(w_scales), _ptr(w_sums), k,
                                           2 * half_d, _ptr(y), _ptr(acc), _stream())
@@ -372,15 +430,15 @@ def w4a4_linear_asym(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch
     return y
 
 
-def quantize_groups(x: torch.Tensor, group: int = 128):
+def quantize_groups(x: torch.Tensor, group: int = 128, out=None):
     """rq_quantize_groups on fp32 rows: returns (codes uint8 [rows, n/2],
     scales fp16 [rows, n / group])."""
     _need_cuda("x", x)
     if x.dtype != torch.float32 or x.dim() != 2:
         raise ValueError("x must be a float32 [rows, n] tensor")
     rows, n = x.shape
-    codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((rows, max(1, n // group)), dtype=torch.float16, device=x.device)
+    codes, scales = _outs(("codes", "scales"), ((rows, n // 2), (rows, max(1, n // group))),
+                          (torch.uint8, torch.float16), x.device, out)
     st = load_library().rq_quantize_groups(_ptr(x), rows, n, group, _ptr(codes), _ptr(scales),
                                            _stream())
     _check("rq_quantize_groups", st)
@@ -410,7 +468,7 @@ def w4a4_gemm_grouped(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: to
     d = 2 * half_d
     if half_d != half_d2 or a_scales.numel() != m or w_group_scales.numel() != k * (d // 128):
         raise ValueError("shapes do not match")
-    y = out if out is not None else torch.empty((m, k), dtype=torch.float16, device=a_codes.device)
+    y = _out("out", out, (m, k), torch.float16, a_codes.device)
     st = load_library().rq_w4a4_gemm_grouped(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes),
                                              _ptr(w_group_scales), k, d, _ptr(y), _stream())
     _check("rq_w4a4_gemm_grouped", st)
@@ -429,7 +487,8 @@ def decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
                      v_codes: torch.Tensor, v_scales: torch.Tensor,
                      signs: torch.Tensor | None = None, lengths: torch.Tensor | None = None,
                      sm_scale: float | None = None, debug: bool = False,
-                     workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+                     workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     out_f32: torch.Tensor | None = None):
     """rq_decode_attention: q fp16 [B, H * G, 128] against the 4-bit rotated
     cache (codes [B, H, S, 64], scales [B, H, S] from kv_rotate_quant).
     Returns (out fp16 [B, H * G, 128], out fp32 or None)."""
@@ -452,9 +511,11 @@ def decode_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
         _need_cuda("lengths", lengths)
         if lengths.dtype != torch.int32 or lengths.numel() != B:
             raise ValueError("lengths must be int32 [batch]")
-    ws = workspace if workspace is not None else decode_attention_workspace(B, H, G, S, q.device)
-    y = out if out is not None else torch.empty_like(q)
-    y32 = torch.empty(q.shape, dtype=torch.float32, device=q.device) if debug else None
+    need = int(load_library().rq_decode_attention_workspace_size(B, H, G, S))
+    ws = _workspace(workspace, need, q.device) if workspace is not None else \
+        decode_attention_workspace(B, H, G, S, q.device)
+    y = _out("out", out, tuple(q.shape), torch.float16, q.device)
+    y32 = _out("out_f32", out_f32, tuple(q.shape), torch.float32, q.device) if debug else None
     scale = (1.0 / 128 ** 0.5) if sm_scale is None else float(sm_scale)
     st = load_library().rq_decode_attention(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                             _ptr(v_scales), _ptr(lengths), B, H, G, S, 128, _ptr(s),

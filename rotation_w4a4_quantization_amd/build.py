@@ -16,7 +16,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "librq.so")
-SOURCES = ["rq_api.hip", "fwht_quant.hip", "w4a4_gemm.hip", "decode_attn.hip"]
+# every HIP source of the library (csrc/*.hip), in a fixed order
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -58,11 +58,13 @@ def check_codes(q_gpu: np.ndarray, ref: dict, what: str, band_rel: float = 0.0) 
 
 
 def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant",
-                          rows=None, report=None, bits=4):
+                          rows=None, report=None, bits=4, ref=None):
     """Full check of one rq_fwht_quant / rq_fold_weights result (bits=4) or
     rq_fwht_quant8 result (bits=8, codes int8 [m, n]).
 
     ``rows`` optionally selects the rows (of x and of the outputs) to check.
+    ``ref`` optionally passes the oracle's (fp32 mirror, fp64) results for
+    the same x and signs, computed once by the caller (not with ``rows``).
     """
     quant = O.fwht_quant if bits == 4 else O.fwht_quant8
     unpack = O.unpack_int4 if bits == 4 else (lambda c: np.asarray(c).astype(np.int8))
@@ -73,7 +75,7 @@ def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant"
         scales = scales[rows]
         if x_rot is not None:
             x_rot = x_rot[rows]
-    mirror = quant(x, signs, "f32")
+    mirror = quant(x, signs, "f32") if ref is None else ref[0]
     if x_rot is not None:
         diff = x_rot.view(np.uint32) != mirror["x_rot"].view(np.uint32)
         # +0 and -0 are the same value
@@ -89,7 +91,7 @@ def check_rotation_result(x, signs, codes, scales, x_rot=None, what="fwht_quant"
     band_rel = 0.0 if bits == 4 else BAND8_REL
     n_band = check_codes(q_gpu, mirror, what, band_rel)
     # against the fp64 oracle: report, and require each difference to be explained
-    truth = quant(x, signs, "f64")
+    truth = quant(x, signs, "f64") if ref is None else ref[1]
     same_scale = scales.view(np.uint16) == truth["scales"].view(np.uint16)
     d = (q_gpu != truth["q"]) & same_scale[..., None]
     n_truth = int(d.sum())

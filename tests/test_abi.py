@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol
-include/rq.h declares, and rejects bad arguments on the host before any HIP
-call (null pointers, shapes, alignment, dtype)."""
+include/*.h declares, and rejects bad arguments on the host before any HIP
+call (null pointers, shapes, alignment, dtype); the binding rejects output
+and workspace tensors that do not fit the call before anything runs."""
 
 import ctypes
 import os
@@ -20,10 +21,14 @@ def lib():
     return binding.load_library()
 
 
-def declared_functions():
-    text = open(os.path.join(ROOT, "include", "rq.h")).read()
+def declared_functions(header="rq.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def all_headers():
+    return sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 
 def test_header_declares_the_bound_entry_points():
@@ -31,8 +36,28 @@ def test_header_declares_the_bound_entry_points():
 
 
 def test_every_declared_symbol_is_exported(lib):
-    for name in declared_functions():
-        assert hasattr(lib, name), name
+    for h in all_headers():
+        for name in declared_functions(h):
+            assert hasattr(lib, name), (h, name)
+
+
+def test_ceiling_probe_argument_errors(lib):
+    lib.rq_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rq_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.rq_ceiling_mfma_i8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    lib.rq_ceiling_mfma_i8.restype = ctypes.c_int64
+    lib.rq_ceiling_mfma_out_words.argtypes = [ctypes.c_int64]
+    lib.rq_ceiling_mfma_out_words.restype = ctypes.c_size_t
+    assert lib.rq_ceiling_read(None, 16, A16, None) == 1
+    assert lib.rq_ceiling_read(A16, 17, A16b, None) == 3
+    assert lib.rq_ceiling_read(MIS, 16, A16b, None) == 3
+    assert lib.rq_ceiling_read(A16, 0, A16b, None) == 0
+    assert lib.rq_ceiling_copy(A16, None, 16, None) == 1
+    assert lib.rq_ceiling_copy(A16, MIS, 16, None) == 3
+    assert lib.rq_ceiling_mfma_i8(None, 2, 10, None) == -1
+    assert lib.rq_ceiling_mfma_i8(A16, 9, 10, None) == -2
+    assert lib.rq_ceiling_mfma_i8(A16, 2, 0, None) == -2
+    assert lib.rq_ceiling_mfma_out_words(0) == 0
 
 
 def test_version_and_status_strings(lib):
@@ -245,3 +270,29 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         binding.fwht_quant(torch.zeros(4, 16, dtype=torch.float16))
+
+
+def test_binding_rejects_unfit_outputs_before_launch():
+    """Caller-supplied outputs and workspaces are checked on the host: the
+    wrong dtype, shape or layout, or a host tensor, raise ValueError (an
+    undersized or strided output would otherwise be written past its end)."""
+    import torch
+    dev = "cuda"
+    ok = torch.empty((4, 8), dtype=torch.float16)
+    with pytest.raises(ValueError, match="float16"):
+        binding._out("out", ok.float(), (4, 8), torch.float16, dev)
+    with pytest.raises(ValueError, match="shape"):
+        binding._out("out", torch.empty((4, 7), dtype=torch.float16), (4, 8), torch.float16, dev)
+    with pytest.raises(ValueError, match="shape"):
+        binding._out("out", torch.empty((32,), dtype=torch.float16), (4, 8), torch.float16, dev)
+    with pytest.raises(ValueError):
+        binding._out("out", ok, (4, 8), torch.float16, dev)  # a host tensor
+    with pytest.raises(ValueError, match="torch.Tensor"):
+        binding._out("out", [0] * 32, (4, 8), torch.float16, dev)
+    with pytest.raises(ValueError, match="tuple"):
+        binding._outs(("codes", "scales"), ((4, 8), (4,)), (torch.uint8, torch.float16), dev,
+                      (None,))
+    with pytest.raises(ValueError, match="uint8"):
+        binding._workspace(torch.empty((64,), dtype=torch.int32), 16, dev)
+    with pytest.raises(ValueError):
+        binding._workspace(torch.empty((64,), dtype=torch.uint8), 16, dev)  # a host tensor

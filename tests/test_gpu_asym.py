@@ -11,6 +11,7 @@ import pytest
 
 from oracle import rq_oracle as O
 from rotation_w4a4_quantization_amd import datagen
+from tests.guard import SENTINELS, Out, check_all
 from tests.parity import Y_TOL, check_asym_result
 
 torch = pytest.importorskip("torch")
@@ -40,16 +41,24 @@ def host(t):
     return None if t is None else t.cpu().numpy()
 
 
-def run_asym(rq, x, signs, debug=True):
-    c, s, z, r = rq.fwht_quant_asym(dev(x), None if signs is None else dev(signs), debug=debug)
-    torch.cuda.synchronize()
-    return host(c), host(s), host(z), host(r)
+def run_asym(rq, x, signs, debug=True, sentinel=0xFF):
+    """One rq_fwht_quant_asym call into guarded, sentinel-filled outputs."""
+    m, n = x.shape
+    specs = [((m, n // 2), torch.uint8), ((m,), torch.float16), ((m,), torch.uint8)]
+    if debug:
+        specs.append(((m, n), torch.float32))
+    o = [Out(sh, dt, sentinel) for sh, dt in specs]
+    rq.fwht_quant_asym(dev(x), None if signs is None else dev(signs), debug=debug,
+                       out=tuple(t.t for t in o))
+    check_all(o, f"fwht_quant_asym n={n}")
+    return o[0].host(), o[1].host(), o[2].host(), (o[3].host() if debug else None)
 
 
 def check_gemm_asym(ac, sa, za, wc, sw, y, acc, what):
     y_ref, acc_ref = O.w4a4_gemm_asym(ac, sa, za, wc, sw)
-    assert np.array_equal(acc.astype(np.int64), acc_ref), \
-        f"{what}: accumulators differ in {int((acc != acc_ref).sum())} places"
+    if acc is not None:
+        assert np.array_equal(acc.astype(np.int64), acc_ref), \
+            f"{what}: accumulators differ in {int((acc != acc_ref).sum())} places"
     yr, yg = y_ref.astype(np.float64), y.astype(np.float64)
     both_inf = np.isinf(yr) & np.isinf(yg) & (np.sign(yr) == np.sign(yg))
     ok = (np.abs(yg - yr) <= Y_TOL * np.maximum(np.abs(yr), 2.0 ** -14)) | both_inf
@@ -67,8 +76,11 @@ def test_fwht_quant_asym_sizes_ragged(rq, n):
     for signs in (datagen.rademacher(rng, n), None):
         c, s, z, r = run_asym(rq, x, signs)
         check_asym_result(x, signs, c, s, z, r, what=f"asym n={n}")
-        c2, s2, z2, _ = run_asym(rq, x, signs, debug=False)
-        assert np.array_equal(c, c2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+        for sentinel in SENTINELS:  # the launch the benchmark times, against the oracle
+            c2, s2, z2, _ = run_asym(rq, x, signs, debug=False, sentinel=sentinel)
+            check_asym_result(x, signs, c2, s2, z2, None, what=f"asym n={n} timed")
+            assert np.array_equal(c, c2) and np.array_equal(s.view(np.uint16), s2.view(np.uint16)) \
+                and np.array_equal(z, z2)
 
 
 def test_fwht_quant_asym_special_rows(rq):
@@ -118,12 +130,20 @@ def test_w4a4_gemm_asym_random_codes(rq, m, k, d):
     sa = datagen.random_scales(rng, m)
     sw = datagen.random_scales(rng, k)
     say(f"w4a4 asym gemm m={m} k={k} d={d}")
-    wsum = rq.weight_code_sums(dev(wc))
-    y, acc = rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum, debug=True)
-    torch.cuda.synchronize()
-    check_gemm_asym(ac, sa, za, wc, sw, host(y), host(acc), f"asym {m}x{k}x{d}")
-    y2, _ = rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum)
-    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
+    so = Out((k,), torch.int32)
+    wsum = rq.weight_code_sums(dev(wc), out=so.t)
+    check_all([so], "weight sums")
+    yo, ao = Out((m, k), torch.float16), Out((m, k), torch.int32)
+    rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum, debug=True, out=yo.t,
+                      acc_out=ao.t)
+    check_all([yo, ao], "asym gemm debug")
+    check_gemm_asym(ac, sa, za, wc, sw, yo.host(), ao.host(), f"asym {m}x{k}x{d}")
+    for sentinel in SENTINELS:  # the launch the benchmark times, against the oracle
+        y2 = Out((m, k), torch.float16, sentinel)
+        rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum, out=y2.t)
+        check_all([y2], "asym gemm timed")
+        check_gemm_asym(ac, sa, za, wc, sw, y2.host(), None, f"asym {m}x{k}x{d} timed")
+        assert np.array_equal(y2.host().view(np.uint16), yo.host().view(np.uint16))
 
 
 def test_w4a4_gemm_asym_closed_form(rq):
@@ -178,14 +198,20 @@ def test_asym_prefill_full_size_sampled(rq):
     wsum = rq.weight_code_sums(wc)
     ac, sa, za, _ = rq.fwht_quant_asym(dev(w["x"]), s)
     say("asym prefill: gemm 2048x8192 -> 28672")
-    y, acc = rq.w4a4_gemm_asym(ac, sa, za, wc, ws, wsum, debug=True)
-    y2, _ = rq.w4a4_gemm_asym(ac, sa, za, wc, ws, wsum)
-    torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    del y2, wsum
-    ac, sa, za, wc, ws, y, acc = map(host, (ac, sa, za, wc, ws, y, acc))
+    m, k = ac.shape[0], wc.shape[0]
+    yo, ao = Out((m, k), torch.float16), Out((m, k), torch.int32)
+    rq.w4a4_gemm_asym(ac, sa, za, wc, ws, wsum, debug=True, out=yo.t, acc_out=ao.t)
+    check_all([yo, ao], "asym prefill debug")
+    y2 = Out((m, k), torch.float16, SENTINELS[1])
+    rq.w4a4_gemm_asym(ac, sa, za, wc, ws, wsum, out=y2.t)  # the launch the benchmark times
+    check_all([y2], "asym prefill timed")
+    assert torch.equal(yo.t.view(torch.int16), y2.t.view(torch.int16))
+    del wsum
+    ac, sa, za, wc, ws, y, acc, yt = map(host, (ac, sa, za, wc, ws, yo.t, ao.t, y2.t))
+    del yo, ao, y2
     rng = np.random.default_rng(79)
     rows = np.sort(rng.choice(2048, 128, replace=False))
     cols = np.sort(rng.choice(28672, 256, replace=False))
     check_gemm_asym(ac, sa, za, wc[cols], ws[cols], y[:, cols], acc[:, cols], "asym prefill cols")
     check_gemm_asym(ac[rows], sa[rows], za[rows], wc, ws, y[rows], acc[rows], "asym prefill rows")
+    check_gemm_asym(ac, sa, za, wc[cols], ws[cols], yt[:, cols], None, "asym prefill timed cols")

@@ -19,6 +19,7 @@ import pytest
 
 from oracle import rq_oracle as O
 from rotation_w4a4_quantization_amd import datagen
+from tests.guard import SENTINELS, Out, check_all
 
 torch = pytest.importorskip("torch")
 
@@ -72,13 +73,24 @@ def random_cache(rng, B, H, S):
     return kc, ks, vc, vs
 
 
-def run(rq, q, kc, ks, vc, vs, signs=None, lengths=None, sm_scale=None):
-    o16, o32 = rq.decode_attention(dev(q), dev(kc), dev(ks), dev(vc), dev(vs),
-                                   None if signs is None else dev(signs),
-                                   None if lengths is None else dev(np.asarray(lengths, np.int32)),
-                                   sm_scale=sm_scale, debug=True)
-    torch.cuda.synchronize()
-    return host(o16), host(o32)
+def run(rq, q, kc, ks, vc, vs, signs=None, lengths=None, sm_scale=None, sentinel=0xFF):
+    """One rq_decode_attention call into guarded, sentinel-filled outputs and
+    workspace; the fp16 output of the launch without the fp32 copy (the one
+    the benchmark times) must equal the debug launch's."""
+    B, H, S, _ = kc.shape
+    o = [Out(q.shape, torch.float16, sentinel), Out(q.shape, torch.float32, sentinel),
+         Out((max(16, int(rq.load_library().rq_decode_attention_workspace_size(
+             B, H, q.shape[1] // H, S))),), torch.uint8, sentinel)]
+    args = (dev(q), dev(kc), dev(ks), dev(vc), dev(vs), None if signs is None else dev(signs),
+            None if lengths is None else dev(np.asarray(lengths, np.int32)))
+    rq.decode_attention(*args, sm_scale=sm_scale, debug=True, workspace=o[2].t, out=o[0].t,
+                        out_f32=o[1].t)
+    check_all(o, "attention")
+    t = Out(q.shape, torch.float16, SENTINELS[1])
+    rq.decode_attention(*args, sm_scale=sm_scale, workspace=o[2].t, out=t.t)
+    check_all([t], "attention timed")
+    assert np.array_equal(t.host().view(np.uint16), o[0].host().view(np.uint16))
+    return o[0].host(), o[1].host()
 
 
 @pytest.mark.parametrize("G", [1, 3, 4, 5, 8])
@@ -159,9 +171,14 @@ def test_attention_full_cache_sampled(rq):
     rng = np.random.default_rng(74)
     q = rng.standard_normal((32, 32, 128)).astype(np.float16)
     say("attention 32 x 8 x 4096, G = 4")
-    o16, o32 = rq.decode_attention(dev(q), kc, ks, vc, vs, None, debug=True)
-    torch.cuda.synchronize()
-    o16, o32 = host(o16), host(o32)
+    oo = [Out(q.shape, torch.float16), Out(q.shape, torch.float32)]
+    rq.decode_attention(dev(q), kc, ks, vc, vs, None, debug=True, out=oo[0].t, out_f32=oo[1].t)
+    check_all(oo, "attention full")
+    ot = Out(q.shape, torch.float16, SENTINELS[1])
+    rq.decode_attention(dev(q), kc, ks, vc, vs, None, out=ot.t)  # the launch the benchmark times
+    check_all([ot], "attention full timed")
+    o16, o32 = oo[0].host(), oo[1].host()
+    assert np.array_equal(ot.host().view(np.uint16), o16.view(np.uint16))
     for b in (0, 17, 31):
         check_attention(q[b:b + 1], host(kc[b:b + 1]), host(ks[b:b + 1]), host(vc[b:b + 1]),
                         host(vs[b:b + 1]), None, None, o16[b:b + 1], o32[b:b + 1], f"full b={b}")

@@ -16,6 +16,7 @@ import pytest
 
 from oracle import rq_oracle as O
 from rotation_w4a4_quantization_amd import datagen
+from tests.guard import SENTINELS, Out, check_all
 from tests.parity import BAND, Y_TOL, dist_to_half_integer
 
 torch = pytest.importorskip("torch")
@@ -78,9 +79,11 @@ def test_quantize_groups_random_rows(rq, group):
     x[2, :4] = [3e-5, -3e-5, 1e-5, 0.0]   # an fp16-subnormal scale in group 0
     x[2, 4:group] = 0.0
     say(f"quantize_groups group={group}")
-    c, s = rq.quantize_groups(dev(x), group)
-    torch.cuda.synchronize()
-    check_groups(x, group, host(c), host(s), f"groups {group}")
+    for sentinel in SENTINELS:
+        o = [Out((rows, n // 2), torch.uint8, sentinel), Out((rows, n // group), torch.float16, sentinel)]
+        rq.quantize_groups(dev(x), group, out=(o[0].t, o[1].t))
+        check_all(o, "quantize_groups")
+        check_groups(x, group, o[0].host(), o[1].host(), f"groups {group}")
 
 
 def test_fold_weights_grouped_decode_weights(rq):
@@ -110,11 +113,14 @@ def test_w4a4_gemm_grouped_random_codes(rq, m, k, d):
     sa = datagen.random_scales(rng, m)
     sw = datagen.random_scales(rng, k * (d // 128)).reshape(k, d // 128)
     say(f"grouped gemm m={m} k={k} d={d}")
-    y = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw))
-    torch.cuda.synchronize()
-    check_gemm_grouped(ac, sa, wc, sw, host(y), f"grouped {m}x{k}x{d}")
-    y2 = rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw))
-    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
+    first = None
+    for sentinel in SENTINELS:
+        yo = Out((m, k), torch.float16, sentinel)
+        rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw), out=yo.t)
+        check_all([yo], "grouped gemm")
+        check_gemm_grouped(ac, sa, wc, sw, yo.host(), f"grouped {m}x{k}x{d}")
+        first = yo.host() if first is None else first
+        assert np.array_equal(yo.host().view(np.uint16), first.view(np.uint16))
 
 
 def test_grouped_prefill_scales_2_byte_aligned(rq):
@@ -179,9 +185,11 @@ def test_grouped_prefill_full_size_sampled(rq):
     wc, wsg = rq.fold_weights_grouped(dev(w["wt"]), s, 128)
     ac, sa, _ = rq.fwht_quant(dev(w["x"]), s)
     say("grouped prefill: gemm 2048x8192 -> 28672")
-    y = rq.w4a4_gemm_grouped(ac, sa, wc, wsg)
-    torch.cuda.synchronize()
-    ac, sa, wc, wsg, y = map(host, (ac, sa, wc, wsg, y))
+    yo = Out((ac.shape[0], wc.shape[0]), torch.float16)
+    rq.w4a4_gemm_grouped(ac, sa, wc, wsg, out=yo.t)
+    check_all([yo], "grouped prefill")
+    ac, sa, wc, wsg, y = map(host, (ac, sa, wc, wsg, yo.t))
+    del yo
     rng = np.random.default_rng(80)
     rows = np.sort(rng.choice(2048, 16, replace=False))
     cols = np.sort(rng.choice(28672, 64, replace=False))

@@ -13,6 +13,7 @@ import pytest
 
 from oracle import rq_oracle as O
 from rotation_w4a4_quantization_amd import datagen
+from tests.guard import SENTINELS, Out, check_all
 from tests.parity import check_gemm, check_rotation_result
 
 torch = pytest.importorskip("torch")
@@ -42,10 +43,15 @@ def host(t):
     return None if t is None else t.cpu().numpy()
 
 
-def run_fq8(rq, x, signs, debug=True):
-    c, s, r = rq.fwht_quant8(dev(x), None if signs is None else dev(signs), debug=debug)
-    torch.cuda.synchronize()
-    return host(c), host(s), host(r)
+def run_fq8(rq, x, signs, debug=True, sentinel=0xFF):
+    """One rq_fwht_quant8 call into guarded, sentinel-filled outputs."""
+    m, n = x.shape
+    specs = [((m, n), torch.int8), ((m,), torch.float16)] + ([((m, n), torch.float32)] if debug else [])
+    o = [Out(sh, dt, sentinel) for sh, dt in specs]
+    rq.fwht_quant8(dev(x), None if signs is None else dev(signs), debug=debug,
+                   out=tuple(t.t for t in o))
+    check_all(o, f"fwht_quant8 n={n}")
+    return o[0].host(), o[1].host(), (o[2].host() if debug else None)
 
 
 @pytest.mark.parametrize("n", [512, 1024, 2048, 4096, 8192])
@@ -58,8 +64,10 @@ def test_fwht_quant8_sizes_ragged(rq, n):
     for signs in (datagen.rademacher(rng, n), None):
         c, s, r = run_fq8(rq, x, signs)
         check_rotation_result(x, signs, c, s, r, what=f"int8 n={n}", bits=8)
-        c2, s2, _ = run_fq8(rq, x, signs, debug=False)
-        assert np.array_equal(c, c2) and np.array_equal(s, s2)
+        for sentinel in SENTINELS:  # the launch the benchmark times, against the oracle
+            c2, s2, _ = run_fq8(rq, x, signs, debug=False, sentinel=sentinel)
+            check_rotation_result(x, signs, c2, s2, None, what=f"int8 n={n} timed", bits=8)
+            assert np.array_equal(c, c2) and np.array_equal(s.view(np.uint16), s2.view(np.uint16))
 
 
 def test_fwht_quant8_special_rows(rq):
@@ -131,11 +139,16 @@ def test_w4a8_gemm_random_codes(rq, m, k, d):
     sa = datagen.random_scales(rng, m)
     sw = datagen.random_scales(rng, k)
     say(f"w4a8 gemm m={m} k={k} d={d}")
-    y, acc = rq.w4a8_gemm(dev(ac), dev(sa), dev(wc), dev(sw), debug=True)
-    torch.cuda.synchronize()
-    check_gemm(ac, sa, wc, sw, host(y), host(acc), what=f"w4a8 {m}x{k}x{d}", a8=True)
-    y2, _ = rq.w4a8_gemm(dev(ac), dev(sa), dev(wc), dev(sw))
-    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
+    yo, ao = Out((m, k), torch.float16), Out((m, k), torch.int32)
+    rq.w4a8_gemm(dev(ac), dev(sa), dev(wc), dev(sw), debug=True, out=yo.t, acc_out=ao.t)
+    check_all([yo, ao], "w4a8 debug")
+    check_gemm(ac, sa, wc, sw, yo.host(), ao.host(), what=f"w4a8 {m}x{k}x{d}", a8=True)
+    for sentinel in SENTINELS:  # the launch the benchmark times, against the oracle
+        y2 = Out((m, k), torch.float16, sentinel)
+        rq.w4a8_gemm(dev(ac), dev(sa), dev(wc), dev(sw), out=y2.t)
+        check_all([y2], "w4a8 timed")
+        check_gemm(ac, sa, wc, sw, y2.host(), None, what=f"w4a8 {m}x{k}x{d} timed", a8=True)
+        assert np.array_equal(y2.host().view(np.uint16), yo.host().view(np.uint16))
 
 
 @pytest.mark.parametrize("m,k", [(3, 40), (64, 40), (256, 224)])
@@ -209,14 +222,19 @@ def test_w4a8_prefill_full_size_sampled(rq):
     wc, ws, _ = rq.fold_weights(dev(w["wt"]), s)
     a8, sa, _ = rq.fwht_quant8(dev(w["x"]), s)
     say("w4a8 prefill: gemm 2048x8192 -> 28672")
-    y, acc = rq.w4a8_gemm(a8, sa, wc, ws, debug=True)
-    y2, _ = rq.w4a8_gemm(a8, sa, wc, ws)
-    torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    del y2
-    a8, sa, wc, ws, y, acc = map(host, (a8, sa, wc, ws, y, acc))
+    m, k = a8.shape[0], wc.shape[0]
+    yo, ao = Out((m, k), torch.float16), Out((m, k), torch.int32)
+    rq.w4a8_gemm(a8, sa, wc, ws, debug=True, out=yo.t, acc_out=ao.t)
+    check_all([yo, ao], "w4a8 prefill debug")
+    y2 = Out((m, k), torch.float16, SENTINELS[1])
+    rq.w4a8_gemm(a8, sa, wc, ws, out=y2.t)  # the launch the benchmark times
+    check_all([y2], "w4a8 prefill timed")
+    assert torch.equal(yo.t.view(torch.int16), y2.t.view(torch.int16))
+    a8, sa, wc, ws, y, acc, yt = map(host, (a8, sa, wc, ws, yo.t, ao.t, y2.t))
+    del yo, ao, y2
     rng = np.random.default_rng(78)
     rows = np.sort(rng.choice(2048, 128, replace=False))
     cols = np.sort(rng.choice(28672, 256, replace=False))
     check_gemm(a8, sa, wc, ws, y, acc, what="w4a8 prefill cols", cols=cols, a8=True)
     check_gemm(a8, sa, wc, ws, y, acc, what="w4a8 prefill rows", rows=rows, a8=True)
+    check_gemm(a8, sa, wc, ws, yt, None, what="w4a8 prefill timed cols", cols=cols, a8=True)
