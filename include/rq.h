@@ -214,6 +214,30 @@ int rq_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* sign
                      const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device array rq_linear_decode_noalloc works in:
+ * 16 tokens x 8192 / 2 code bytes + 64 (codes, then fp16 scales). */
+#define RQ_NOALLOC_SCRATCH_BYTES (16 * 8192 / 2 + 64)
+
+/*
+ * rq_linear_decode_noalloc -- rq_linear_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.  Same arguments, kernels and result
+ * as rq_linear_decode (y bit-identical), without the workspace: when m > 4
+ * the activation codes and scales go to a file-scope device array of
+ * RQ_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it has
+ * run on until the process ends.  Nothing is allocated by the call (the
+ * array's device address is looked up once per device, with that device
+ * current).  Calls that overlap in time on one GPU share the array and race;
+ * serialise them (one stream, or events).  Shapes beyond the array's size
+ * cannot occur within the limits below and would return RQ_ERR_SHAPE.
+ *
+ *   x, m, d, signs, w_codes, w_scales, k, y, stream: as rq_linear_decode
+ *   (0 <= m <= 16, d a power of two in [512, 8192]).
+ */
+int rq_linear_decode_noalloc(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k,
+                             uint16_t* y, void* stream);
+
 /*
  * rq_fwht_quant8 -- online rotation fused with per-token INT8 quantisation,
  * the activation side of the W4A8 variant.

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     fwht_quant_asym,
     kv_rotate_quant,
     linear_decode,
+    linear_decode_noalloc,
     linear_decode_workspace,
     quantize_groups,
     load_library,

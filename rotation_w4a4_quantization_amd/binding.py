@@ -27,6 +27,7 @@ EXPORTED = (
     "rq_kv_rotate_quant",
     "rq_linear_decode_workspace_size",
     "rq_linear_decode",
+    "rq_linear_decode_noalloc",
     "rq_fwht_quant8",
     "rq_w4a8_gemm",
     "rq_fwht_quant_asym",
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_linear_decode_workspace_size.restype = sz
     lib.rq_linear_decode.argtypes = [p, i64, i64, p, p, p, i64, p, p, sz, p]
     lib.rq_linear_decode.restype = i32
+    lib.rq_linear_decode_noalloc.argtypes = [p, i64, i64, p, p, p, i64, p, p]
+    lib.rq_linear_decode_noalloc.restype = i32
     lib.rq_fwht_quant8.argtypes = [p, i64, i64, p, p, p, p, p]
     lib.rq_fwht_quant8.restype = i32
     lib.rq_w4a8_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, p, p]
@@ -305,6 +308,29 @@ def linear_decode(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Te
     st = load_library().rq_linear_decode(_ptr(x), m, d, _ptr(s), _ptr(w_codes), _ptr(w_scales), k,
                                          _ptr(y), _ptr(ws), ws.numel(), _stream())
     _check("rq_linear_decode", st)
+    return y
+
+
+def linear_decode_noalloc(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tensor,
+                          w_scales: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """rq_linear_decode_noalloc: rq_linear_decode without a workspace (the
+    library's own device array holds the codes; calls that overlap in time on
+    one GPU race).  Nothing is allocated when `out` is given."""
+    for name, t in (("x", x), ("w_codes", w_codes), ("w_scales", w_scales)):
+        _need_cuda(name, t)
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a float16 [m, d] tensor")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.float16:
+        raise ValueError("weight codes must be uint8 and scales float16")
+    m, d = x.shape
+    k, half_d = w_codes.shape
+    if half_d * 2 != d or w_scales.numel() != k:
+        raise ValueError("weight codes do not match x")
+    s = _signs(signs, d, x.device)
+    y = _out("out", out, (m, k), torch.float16, x.device)
+    st = load_library().rq_linear_decode_noalloc(_ptr(x), m, d, _ptr(s), _ptr(w_codes),
+                                                 _ptr(w_scales), k, _ptr(y), _stream())
+    _check("rq_linear_decode_noalloc", st)
     return y
 
 
