@@ -427,29 +427,51 @@ def main():
 
         if want("downproj"):
             # the online rotation in front of a down projection: 2048 tokens x
-            # 14336 = 28 * 512 (H_28 (x) H_512), same input statistics as the
-            # prefill activations
-            mm, d = 2048, 14336
-            rng = np.random.default_rng(4)
-            x28 = datagen.activations(rng, mm, d, datagen.outlier_channels(rng, d), 100.0)
-            x28 = torch.from_numpy(x28).to(dev)
-            s28 = torch.from_numpy(datagen.rademacher(rng, d)).to(dev)
-            ac28 = torch.empty((mm, d // 2), dtype=torch.uint8, device=dev)
-            sa28 = torch.empty((mm,), dtype=torch.float16, device=dev)
-            fsets = -(-2 * MALL_BYTES // (x28.numel() * 2)) + 1
-            x28s = [x28] + [x28.clone() for _ in range(fsets - 1)]
+            # 14336 = 28 * 512 (H_28 (x) H_512) and x 28672 = 28 * 1024
+            # (H_28 (x) H_1024), same input statistics as the prefill
+            # activations; then the 28672 -> 8192 down projection GEMM
+            for mm, d, seed in ((2048, 14336, 4), (2048, 28672, 6)):
+                key = f"fwht_quant_{mm}x{d}"
+                rng = np.random.default_rng(seed)
+                x28 = datagen.activations(rng, mm, d, datagen.outlier_channels(rng, d), 100.0)
+                x28 = torch.from_numpy(x28).to(dev)
+                s28 = torch.from_numpy(datagen.rademacher(rng, d)).to(dev)
+                ac28 = torch.empty((mm, d // 2), dtype=torch.uint8, device=dev)
+                sa28 = torch.empty((mm,), dtype=torch.float16, device=dev)
+                fsets = -(-2 * MALL_BYTES // (x28.numel() * 2)) + 1
+                x28s = [x28] + [x28.clone() for _ in range(fsets - 1)]
 
-            def f28(i):
-                st = lib.rq_fwht_quant(_ptr(x28s[i]), RQ_F16, mm, d, _ptr(s28), _ptr(ac28),
-                                       _ptr(sa28), None, _stream())
-                assert st == 0
+                def f28(i, x28s=x28s, s28=s28, ac28=ac28, sa28=sa28, mm=mm, d=d):
+                    st = lib.rq_fwht_quant(_ptr(x28s[i]), RQ_F16, mm, d, _ptr(s28), _ptr(ac28),
+                                           _ptr(sa28), None, _stream())
+                    assert st == 0
 
-            ms28 = time_launches(torch, f28, fsets, steps2, warm2)
-            b = fwht_bytes(mm, d)
-            sec["fwht_quant_2048x14336"] = line(ms28, **{"GB/s": round(b / (ms28 * 1e-3) / 1e9, 1),
-                                            "hbm_frac": round(b / (ms28 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-            log(f"[bench] fwht_quant 2048x14336: {sec['fwht_quant_2048x14336']}")
-            del x28s, x28
+                if want_line(key):
+                    ms28 = time_launches(torch, f28, fsets, steps2, warm2)
+                    b = fwht_bytes(mm, d)
+                    sec[key] = line(ms28, **{"GB/s": round(b / (ms28 * 1e-3) / 1e9, 1),
+                                             "hbm_frac": round(b / (ms28 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                    log(f"[bench] {key}: {sec[key]}")
+                del x28s
+                if d == 28672 and want_line("gemm_downproj_2048x28672x8192"):
+                    f28(0)
+                    k = 8192
+                    wt = torch.from_numpy(datagen.gaussian(rng, (k, d), std=0.02)).to(dev)
+                    wc, ws, _ = rq.fold_weights(wt, s28)
+                    del wt
+                    y = torch.empty((mm, k), dtype=torch.float16, device=dev)
+                    wcs = [wc, wc.clone()]
+
+                    def gd(i, wcs=wcs, ws=ws, y=y, ac28=ac28, sa28=sa28):
+                        rq.w4a4_gemm(ac28, sa28, wcs[i], ws, out=y)
+
+                    msd = time_launches(torch, gd, 2, max(5, steps2 // 2), warm2)
+                    tops = 2 * mm * d * k / (msd * 1e-3) / 1e12
+                    sec["gemm_downproj_2048x28672x8192"] = line(
+                        msd, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
+                    log(f"[bench] down projection gemm: {sec['gemm_downproj_2048x28672x8192']}")
+                    del wcs, wc, y
+                del x28
 
         if want("w4a8"):
             # the W4A8 variant: INT8 per-token activations against the same

@@ -70,6 +70,19 @@ typedef enum { RQ_F16 = 0, RQ_F32 = 1 } rq_dtype;
  * matrix of order 14.
  */
 #define RQ_N_28X512 14336
+/*
+ * 28 * 1024 = 28672, the down-projection input width of the 8192 -> 28672
+ * model: H_28 (x) H_1024 (element e = 1024 b + p), the 1024-point factor first
+ * (ascending strides), then H_28 in the same Paley order as for RQ_N_28X512.
+ */
+#define RQ_N_28X1024 28672
+/*
+ * Largest reduction length d of the GEMMs: a multiple of 64 up to 32768
+ * covers a down projection of width 28672.  Every int32 sum stays exact:
+ * the W4A4 MFMA sum is 256 * acc with |acc| <= 64 d (2^29 at d = 32768), the
+ * W4A8 sum 16 * acc with |acc| <= 1024 d.
+ */
+#define RQ_MAX_D 32768
 
 /*
  * rq_fwht_quant -- online rotation fused with per-token INT4 quantisation.
@@ -84,8 +97,8 @@ typedef enum { RQ_F16 = 0, RQ_F32 = 1 } rq_dtype;
  *   x       [m][n] activations, dtype x_dtype (RQ_F16 or RQ_F32), row major,
  *           16-byte aligned.
  *   m       number of rows (tokens), >= 0.
- *   n       rotation length, a power of two in [RQ_MIN_N, RQ_MAX_N] or
- *           RQ_N_28X512.
+ *   n       rotation length, a power of two in [RQ_MIN_N, RQ_MAX_N],
+ *           RQ_N_28X512 or RQ_N_28X1024.
  *   signs   [n] int8, each +1 or -1; NULL means all +1 (plain H_n/sqrt(n)).
  *   codes   [m][n/2] uint8 output, 16-byte aligned.
  *   scales  [m] fp16 output (one per row).
@@ -112,8 +125,8 @@ int rq_fwht_quant(const void* x, int x_dtype, int64_t m, int64_t n, const int8_t
  *            W~^T is w_j R = (w_j * s) H_d / sqrt(d): the same row transform
  *            as rq_fwht_quant, with the same signs as the activations.
  *   k        output channels (rows of W^T), >= 0.
- *   d        input width, a power of two in [RQ_MIN_N, RQ_MAX_N] or
- *            RQ_N_28X512.
+ *   d        input width, a power of two in [RQ_MIN_N, RQ_MAX_N],
+ *            RQ_N_28X512 or RQ_N_28X1024.
  *   signs    [d] int8 +-1 or NULL.
  *   w_codes  [k][d/2] uint8 output; w_scales [k] fp16 output.
  *   w_rot    optional [k][d] float32 output of W~^T (debug), or NULL.
@@ -135,7 +148,7 @@ size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d);
  * layers run integer GEMMs end to end); [QuaRot] "End-to-end flow" (the INT4
  * rotated activation multiplies the INT4 folded weight in a low-bit kernel).
  * INT4 codes are widened to int8 in registers and multiplied with int8 MFMA
- * into int32 accumulators (exact: |acc| <= 64 * d); the epilogue is
+ * into int32 accumulators (exact: |acc| <= 64 * d, see RQ_MAX_D); the epilogue is
  * fp32(acc) * sa, then * sw, rounded to fp16 half to even.
  *
  *   a_codes  [m][d/2] uint8 activation codes (rq_fwht_quant output), 16-byte
@@ -144,7 +157,7 @@ size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d);
  *   w_codes  [k][d/2] uint8 weight codes (rq_fold_weights output), 16-byte
  *            aligned; w_scales [k] fp16.
  *   k        output channels, >= 1 when m > 0.
- *   d        reduction length, a multiple of 64 in [64, 16384].
+ *   d        reduction length, a multiple of 64 in [64, RQ_MAX_D].
  *   y        [m][k] fp16 output.
  *   acc      optional [m][k] int32 output of the accumulators (debug), or NULL.
  *   workspace, workspace_bytes  device scratch of at least
@@ -270,7 +283,7 @@ int rq_fwht_quant8(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs,
  * [SpinQuant] "The architecture: every piece explained" (INT4 weights, INT8
  * activations, integer matmul).  The weight codes are widened to 16 * q in
  * int8 lanes and multiplied with the activation bytes by int8 MFMA; the
- * int32 sum is exactly 16 * acc (|16 * acc| <= 2^14 * d).  The epilogue is
+ * int32 sum is exactly 16 * acc (|16 * acc| <= 2^14 * d < 2^31).  The epilogue is
  * the one of rq_w4a4_gemm.
  *
  *   a_codes  [m][d] int8 activation codes (rq_fwht_quant8), 16-byte aligned;
@@ -279,7 +292,7 @@ int rq_fwht_quant8(const uint16_t* x, int64_t m, int64_t n, const int8_t* signs,
  *   w_codes  [k][d/2] uint8 weight codes (rq_fold_weights), 16-byte aligned;
  *            w_scales [k] fp16.
  *   k        output channels, >= 1 when m > 0.
- *   d        reduction length, a multiple of 64 in [64, 16384].
+ *   d        reduction length, a multiple of 64 in [64, RQ_MAX_D].
  *   y        [m][k] fp16 output; acc optional [m][k] int32 accumulators.
  */
 int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
@@ -315,7 +328,7 @@ int rq_fwht_quant_asym(const uint16_t* x, int64_t m, int64_t n, const int8_t* si
  * asymmetric GEMM needs: sum_i (qa_i - z) qw_i = sum_i qa_i qw_i - z sums[j]).
  *
  *   w_codes  [k][d/2] uint8 (rq_fold_weights output), 16-byte aligned.
- *   k        rows, >= 0;  d  a multiple of 64 in [64, 16384].
+ *   k        rows, >= 0;  d  a multiple of 64 in [64, RQ_MAX_D].
  *   sums     [k] int32 output.
  */
 int rq_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
@@ -335,7 +348,7 @@ int rq_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* s
  *            a_scales [m] fp16; a_zeros [m] uint8.
  *   w_codes  [k][d/2] signed codes (rq_fold_weights), 16-byte aligned;
  *            w_scales [k] fp16; w_sums [k] int32 (rq_weight_code_sums).
- *   m >= 0, k >= 1 when m > 0, d a multiple of 64 in [64, 16384].
+ *   m >= 0, k >= 1 when m > 0, d a multiple of 64 in [64, RQ_MAX_D].
  *   y        [m][k] fp16 output; acc optional [m][k] int32 accumulators.
  */
 int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
@@ -380,7 +393,7 @@ int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, u
  *                   shapes with m >= 128, k >= 224 and d a multiple of 256
  *                   run on the persistent prefill kernel, which reads scale
  *                   pairs as dwords; otherwise on the tile kernel).
- *   m >= 0; k >= 1 when m > 0; d a multiple of 128 in [128, 16384].
+ *   m >= 0; k >= 1 when m > 0; d a multiple of 128 in [128, RQ_MAX_D].
  *   y               [m][k] fp16 output.
  */
 int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,

@@ -366,18 +366,21 @@ __global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_ke
 }
 
 // ------------------------------------------------------------------------
-// n = 28 * 512 = 14336 (the width of a Llama-class down projection input):
-// H_14336 = H_28 (x) H_512, H_28 by Paley's second construction with q = 13
-// ([RQ] "Learned Orthogonal Rotations: SpinQuant": fixed Hadamard rotations
-// need power-of-two sizes or products of small Hadamard-compatible sizes;
-// [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms", part 2:
-// the down projection's input needs an online rotation).  Element
-// e = 512 b + p: block b of 28, position p of 512.
+// n = 28 * P with P = 512 (14336, the width of a Llama-class down projection
+// input, 4096 -> 14336) or P = 1024 (28672, the same for the 8192 -> 28672
+// model): H_n = H_28 (x) H_P, H_28 by Paley's second construction with
+// q = 13 ([RQ] "Learned Orthogonal Rotations: SpinQuant": fixed Hadamard
+// rotations need power-of-two sizes or products of small Hadamard-compatible
+// sizes; [RQ] "Weight Absorption and Online Fast Walsh-Hadamard Transforms",
+// part 2: the down projection's input needs an online rotation).  Element
+// e = P b + p: block b of 28, position p of P.
 //
-// One row per 512-thread workgroup at a time.  Wave w rotates blocks w, w + 8,
-// w + 16 (and w + 24) with the 512-point stages of the row kernel (one
-// 16-byte chunk per lane and block) and writes them, sign-corrected, to LDS in
-// fp32; the next row's chunks are loaded while the rest of the row runs.
+// One row per P-thread workgroup at a time (P / 64 wavefronts).  Wave w
+// rotates blocks w, w + P/64, ... with the P-point FWHT: each 512-element
+// sub-block is one 16-byte chunk per lane through the 512-point stages of the
+// row kernel, and for P = 1024 the last stage (stride 512) combines the two
+// sub-blocks in registers.  The block goes, sign-corrected, to an fp32 LDS
+// row; the next row's chunks are loaded while the rest of the row runs.
 // After a barrier, thread t takes position t and applies H_28 across the 28
 // blocks in the order the Paley structure H_28 = C (x) H_2 + I (x) J_2 gives
 // (C the order-14 conference matrix, J_2 = [[1, -1], [-1, -1]]):
@@ -400,10 +403,8 @@ constexpr int paley_conf14(int j, int i) {
 }
 
 constexpr int kN28 = 28 * 512;
-constexpr int k28Waves = 8;  // wavefronts per workgroup
+constexpr int kN28x1024 = 28 * 1024;
 
-// The 16-byte (fp16) or 32-byte (fp32) chunk of elements 8L .. 8L + 7 of one
-// block, as raw words.
 template <typename T>
 struct Chunk28 {
   v4u w[sizeof(T) / 2];
@@ -456,40 +457,58 @@ __device__ __forceinline__ void chunk28_e0(const Chunk28<T>& raw, const int8_t* 
   }
 }
 
-template <typename T, bool HAS_SIGNS>
-__global__ __launch_bounds__(64 * k28Waves) void fwht28x512_kernel(FQOut o, int64_t rows,
-                                                                  const int8_t* __restrict__ signs,
-                                                                  float c32) {
-  constexpr int P = 512, NB = 28, BPW = (NB + k28Waves - 1) / k28Waves;  // blocks per wave (4 or 3)
-  __shared__ __align__(16) float xb[NB][P];  // 56 KB; then the code bytes of the row
-  __shared__ float amx[k28Waves];
+template <typename T, bool HAS_SIGNS, int P>
+__global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
+                                                   const int8_t* __restrict__ signs, float c32) {
+  constexpr int NB = 28, W = P / 64, N = NB * P;
+  constexpr int BPW = (NB + W - 1) / W;  // blocks per wave
+  constexpr int SUB = P / 512;           // 512-element sub-blocks (chunks) per block
+  static_assert(P == 512 || P == 1024, "blocks of 512 or 1024 elements");
+  __shared__ __align__(16) float xb[NB][P];  // the row in fp32; then its code bytes
+  __shared__ float amx[W];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const RowLane rl = make_row_lane(L);
   unsigned char* cbuf = reinterpret_cast<unsigned char*>(&xb[0][0]);
 
   int64_t row = blockIdx.x;
   if (row >= rows) return;  // uniform per workgroup
-  // wave w owns blocks w, w + 8, w + 16 (and w + 24 for w < 4)
-  Chunk28<T> raw[BPW];
+  // wave w owns blocks w, w + W, ...; sub-block j of block b starts at P b + 512 j
+  Chunk28<T> raw[BPW][SUB];
 #pragma unroll
   for (int i = 0; i < BPW; ++i)
-    if (wave + k28Waves * i < NB)
-      raw[i] = load_chunk28(static_cast<const T*>(o.x) + row * kN28, P * (wave + k28Waves * i) + 8 * L);
+#pragma unroll
+    for (int j = 0; j < SUB; ++j)
+      if (wave + W * i < NB)
+        raw[i][j] = load_chunk28(static_cast<const T*>(o.x) + row * N,
+                                 P * (wave + W * i) + 512 * j + 8 * L);
 
   for (;;) {
-    // 1. the 512-point stages of this wave's blocks, sign-corrected into LDS
+    // 1. the P-point stages of this wave's blocks, sign-corrected into LDS
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const int b = wave + k28Waves * i;
+      const int b = wave + W * i;
       if (b >= NB) continue;  // uniform per wave
-      float c[8];
-      chunk28_e0<T, HAS_SIGNS>(raw[i], signs, P * b + 8 * L, c);
-      chunk512_stages(c, rl);
+      float c[SUB][8];
 #pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        const int p = (rl.lane_pair << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8);
-        *reinterpret_cast<float2*>(&xb[b][p]) = make_float2(c[r] * rl.sigma, c[r + 1] * rl.sigma);
+      for (int j = 0; j < SUB; ++j) {
+        chunk28_e0<T, HAS_SIGNS>(raw[i][j], signs, P * b + 512 * j + 8 * L, c[j]);
+        chunk512_stages(c[j], rl);
       }
+      if constexpr (SUB == 2) {  // stride 512: sub-block 0 with sub-block 1
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float x0 = c[0][r], x1 = c[1][r];
+          c[0][r] = x0 + x1;
+          c[1][r] = x0 - x1;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < SUB; ++j)
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+          const int p = 512 * j + ((rl.lane_pair << 1) | (((r >> 2) & 1) << 7) | (((r >> 1) & 1) << 8));
+          *reinterpret_cast<float2*>(&xb[b][p]) = make_float2(c[j][r] * rl.sigma, c[j][r + 1] * rl.sigma);
+        }
     }
     // the next row's chunks are in flight during the rest of this row
     const int64_t next = row + gridDim.x;
@@ -497,9 +516,11 @@ __global__ __launch_bounds__(64 * k28Waves) void fwht28x512_kernel(FQOut o, int6
     if (more) {
 #pragma unroll
       for (int i = 0; i < BPW; ++i)
-        if (wave + k28Waves * i < NB)
-          raw[i] = load_chunk28(static_cast<const T*>(o.x) + next * kN28,
-                                P * (wave + k28Waves * i) + 8 * L);
+#pragma unroll
+        for (int j = 0; j < SUB; ++j)
+          if (wave + W * i < NB)
+            raw[i][j] = load_chunk28(static_cast<const T*>(o.x) + next * N,
+                                     P * (wave + W * i) + 512 * j + 8 * L);
     }
     __syncthreads();
 
@@ -546,18 +567,18 @@ __global__ __launch_bounds__(64 * k28Waves) void fwht28x512_kernel(FQOut o, int6
     if (L == 0) amx[wave] = amax;
     __syncthreads();  // also: every thread has read xb
 #pragma unroll
-    for (int w = 0; w < k28Waves; ++w) amax = fmaxf(amax, amx[w]);
+    for (int w = 0; w < W; ++w) amax = fmaxf(amax, amx[w]);
     const uint16_t hb = scale_fp16(amax * c32);
     const bool subnormal = hb != 0 && hb < 0x0400u;
     const float mult = hb == 0 ? 0.0f : c32 / h2f(hb);
     if (tid == 0) o.scales[row] = hb;
     if (o.xrot != nullptr) {
-      float* xo = o.xrot + row * kN28;
+      float* xo = o.xrot + row * N;
 #pragma unroll
       for (int b = 0; b < NB; ++b) xo[P * b + tid] = y[b] * c32;
     }
 
-    // 4. codes: element 512 b + tid is nibble (tid & 1) of byte 256 b + tid / 2;
+    // 4. codes: element P b + tid is nibble (tid & 1) of byte (P / 2) b + tid / 2;
     // the odd lane's code reaches its even neighbour by DPP
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -565,11 +586,11 @@ __global__ __launch_bounds__(64 * k28Waves) void fwht28x512_kernel(FQOut o, int6
       if (subnormal) q = fminf(fmaxf(q, kMagicLo), kMagicHi);
       const uint32_t code = f2u(q) & 0xFu;
       const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, 0xB1, 0xF, 0xF, false);
-      if (!(tid & 1)) cbuf[256 * b + (tid >> 1)] = (unsigned char)((code | (other << 4)) ^ 0x88u);
+      if (!(tid & 1)) cbuf[(P / 2) * b + (tid >> 1)] = (unsigned char)((code | (other << 4)) ^ 0x88u);
     }
     __syncthreads();
-    uint8_t* dst = o.codes + row * (kN28 / 2);
-    for (int c = tid; c < kN28 / 32; c += 64 * k28Waves)
+    uint8_t* dst = o.codes + row * (N / 2);
+    for (int c = tid; c < N / 32; c += P)
       __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(cbuf + 16 * c),
                                   reinterpret_cast<v4u*>(dst + 16 * c));
     if (!more) break;
@@ -578,13 +599,14 @@ __global__ __launch_bounds__(64 * k28Waves) void fwht28x512_kernel(FQOut o, int6
   }
 }
 
-template <typename T, bool HAS_SIGNS>
+template <typename T, bool HAS_SIGNS, int P>
 hipError_t launch_28(FQOut o, int64_t rows, const int8_t* signs, hipStream_t stream) {
-  const float c32 = (float)(1.0 / __builtin_sqrt((double)kN28));
-  const int64_t cap = (int64_t)cu_count() * 2;  // two 56 KB workgroups per CU
+  const float c32 = (float)(1.0 / __builtin_sqrt((double)(28 * P)));
+  // workgroups resident per CU: two of 56 KB (P = 512) or one of 112 KB
+  const int64_t cap = (int64_t)cu_count() * (P == 512 ? 2 : 1);
   const int64_t blocks = rows < cap ? rows : cap;
-  hipLaunchKernelGGL((fwht28x512_kernel<T, HAS_SIGNS>), dim3((unsigned)blocks), dim3(64 * k28Waves), 0,
-                     stream, o, rows, signs, c32);
+  hipLaunchKernelGGL((fwht28_kernel<T, HAS_SIGNS, P>), dim3((unsigned)blocks), dim3(P), 0, stream,
+                     o, rows, signs, c32);
   return hipGetLastError();
 }
 
@@ -796,10 +818,17 @@ hipError_t launch_fwht_quant(const void* x, bool is_f32, int64_t rows, int n, co
   const FQOut o{x, codes, scales, x_rot};
   if (n == kN28) {
     if (is_f32)
-      return signs ? launch_28<float, true>(o, rows, signs, stream)
-                   : launch_28<float, false>(o, rows, signs, stream);
-    return signs ? launch_28<__half, true>(o, rows, signs, stream)
-                 : launch_28<__half, false>(o, rows, signs, stream);
+      return signs ? launch_28<float, true, 512>(o, rows, signs, stream)
+                   : launch_28<float, false, 512>(o, rows, signs, stream);
+    return signs ? launch_28<__half, true, 512>(o, rows, signs, stream)
+                 : launch_28<__half, false, 512>(o, rows, signs, stream);
+  }
+  if (n == kN28x1024) {
+    if (is_f32)
+      return signs ? launch_28<float, true, 1024>(o, rows, signs, stream)
+                   : launch_28<float, false, 1024>(o, rows, signs, stream);
+    return signs ? launch_28<__half, true, 1024>(o, rows, signs, stream)
+                 : launch_28<__half, false, 1024>(o, rows, signs, stream);
   }
   if (is_f32) {
     return signs ? dispatch_n<float, true>(o, o, 1, rows, n, signs, stream)

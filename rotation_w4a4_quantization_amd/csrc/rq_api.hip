@@ -22,7 +22,8 @@ int check_rotation_args(const void* x, int dtype, int64_t m, int64_t n, const in
                         const void* codes, const void* scales, const void* rot) {
   if (dtype != RQ_F16 && dtype != RQ_F32) return RQ_ERR_DTYPE;
   if (m < 0 || m >= kMaxRows) return RQ_ERR_SHAPE;
-  if (n != RQ_N_28X512 && (!is_pow2(n) || n < RQ_MIN_N || n > RQ_MAX_N)) return RQ_ERR_SHAPE;
+  if (n != RQ_N_28X512 && n != RQ_N_28X1024 && (!is_pow2(n) || n < RQ_MIN_N || n > RQ_MAX_N))
+    return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return RQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return RQ_ERR_ALIGN;
@@ -75,7 +76,7 @@ int rq_fwht_quant_asym(const uint16_t* x, int64_t m, int64_t n, const int8_t* si
 
 int rq_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d, int32_t* sums,
                         void* stream) {
-  if (k < 0 || k >= kMaxRows || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if (k < 0 || k >= kMaxRows || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
   if (k == 0) return RQ_OK;
   if (w_codes == nullptr || sums == nullptr) return RQ_ERR_NULL;
   if (!aligned16(w_codes)) return RQ_ERR_ALIGN;
@@ -96,7 +97,7 @@ int rq_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                  void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  if (m < 0 || k < 0 || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if (m < 0 || k < 0 || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
   if (m > 16 && (m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
@@ -128,7 +129,7 @@ int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
 int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
                  const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                  uint16_t* y, int32_t* acc, void* stream) {
-  if (m < 0 || k < 0 || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if (m < 0 || k < 0 || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
   if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
@@ -145,7 +146,7 @@ int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const ui
                       int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
                       const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
                       void* stream) {
-  if (m < 0 || k < 0 || d < 64 || d > 16384 || d % 64 != 0) return RQ_ERR_SHAPE;
+  if (m < 0 || k < 0 || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
   if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
@@ -174,7 +175,7 @@ int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, u
 int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                          const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
                          int64_t d, uint16_t* y, void* stream) {
-  if (m < 0 || k < 0 || d < 128 || d > 16384 || d % 128 != 0) return RQ_ERR_SHAPE;
+  if (m < 0 || k < 0 || d < 128 || d > RQ_MAX_D || d % 128 != 0) return RQ_ERR_SHAPE;
   if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;

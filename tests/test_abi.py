@@ -85,6 +85,9 @@ def test_fwht_quant_argument_errors(lib):
     assert fq(lib, n=3) == binding.RQ_ERR_SHAPE
     assert fq(lib, n=1) == binding.RQ_ERR_SHAPE
     assert fq(lib, n=16384) == binding.RQ_ERR_SHAPE
+    assert fq(lib, n=28 * 2048) == binding.RQ_ERR_SHAPE   # 28 x 2^k beyond 28 x 1024
+    assert fq(lib, n=28 * 256) == binding.RQ_ERR_SHAPE
+    assert fq(lib, n=28672, x=None) == binding.RQ_ERR_NULL  # 28 x 1024 is a valid length
     assert fq(lib, n=0) == binding.RQ_ERR_SHAPE
     assert fq(lib, m=-1) == binding.RQ_ERR_SHAPE
     assert fq(lib, m=1 << 31) == binding.RQ_ERR_SHAPE
@@ -115,7 +118,8 @@ def test_gemm_argument_errors(lib):
     assert gemm(lib, sw=None) == binding.RQ_ERR_NULL
     assert gemm(lib, d=96) == binding.RQ_ERR_SHAPE
     assert gemm(lib, d=32) == binding.RQ_ERR_SHAPE
-    assert gemm(lib, d=32768) == binding.RQ_ERR_SHAPE
+    assert gemm(lib, d=32768 + 64) == binding.RQ_ERR_SHAPE  # above RQ_MAX_D
+    assert gemm(lib, d=28672, a=None) == binding.RQ_ERR_NULL  # the down-projection width is valid
     assert gemm(lib, k=0) == binding.RQ_ERR_SHAPE
     assert gemm(lib, m=-3) == binding.RQ_ERR_SHAPE
     assert gemm(lib, m=128 * 65536) == binding.RQ_ERR_SHAPE
@@ -165,7 +169,7 @@ def test_w4a8_gemm_argument_errors(lib):
     assert call(sa=None) == binding.RQ_ERR_NULL
     assert call(y=None) == binding.RQ_ERR_NULL
     assert call(d=96) == binding.RQ_ERR_SHAPE
-    assert call(d=32768) == binding.RQ_ERR_SHAPE
+    assert call(d=32768 + 64) == binding.RQ_ERR_SHAPE
     assert call(k=0) == binding.RQ_ERR_SHAPE
     assert call(m=-1) == binding.RQ_ERR_SHAPE
     assert call(m=128 * 65536) == binding.RQ_ERR_SHAPE

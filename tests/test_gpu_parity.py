@@ -110,25 +110,61 @@ def test_fwht_quant_28x512(rq, m, dtype):
         timed_fq_matches_oracle(rq, x, signs, c, s, f"n=28x512 m={m}", fold=dtype == np.float32)
 
 
-@pytest.mark.parametrize("m,k", [(4, 40), (300, 256)])
-def test_linear_28x512(rq, m, k):
-    """A W4A4 linear with d = 14336 (the down projection width): the fold and
-    the online rotation with H_28 (x) H_512, then the decode (m = 4) or the
-    large (m = 300) GEMM, against the oracle."""
-    d = 14336
-    rng = np.random.default_rng(m + k)
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("m", [1, 7, 300])
+def test_fwht_quant_28x1024(rq, m, dtype):
+    """n = 28 * 1024 (H_28 (x) H_1024, the 8192 -> 28672 model's down-projection
+    input): rotated rows bit-identical to the oracle's fp32 mirror, codes
+    within the rounding band; 300 rows exceed the grid (one workgroup per CU),
+    so workgroups take several rows."""
+    n = 28672
+    rng = np.random.default_rng(100 + m)
+    say(f"fwht_quant n=28x1024 m={m} dtype={np.dtype(dtype).name}")
+    x = (rng.standard_normal((m, n)) * rng.uniform(0.1, 10, (m, 1))).astype(dtype)
+    x[:, rng.choice(n, 28, replace=False)] *= 100  # outlier channels
+    for signs in (datagen.rademacher(rng, n), None):
+        c, s, r = run_fq(rq, x, signs, fold=dtype == np.float32)
+        check_rotation_result(x, signs, c, s, r, what=f"n=28x1024 m={m}", report=REPORT)
+        timed_fq_matches_oracle(rq, x, signs, c, s, f"n=28x1024 m={m}", fold=dtype == np.float32)
+
+
+def test_fwht_quant_28x1024_special_rows(rq):
+    n = 28672
+    rng = np.random.default_rng(55)
+    signs = datagen.rademacher(rng, n)
+    x = np.zeros((5, n), np.float32)
+    x[1, 12345] = 3.0                     # one-hot: every code +-7
+    x[2] = 1e-30                          # underflows the fp16 scale -> zero codes
+    x[3] = rng.standard_normal(n) * 1e6   # fp16 scale overflows -> +inf, zero codes
+    x[4, :4] = [4e-4, -4e-4, 1e-4, 0.0]   # fp16-subnormal scale (clamped path)
+    say("fwht_quant n=28x1024 special rows")
+    c, s, r = run_fq(rq, x, signs)
+    check_rotation_result(x, signs, c, s, r, what="28x1024 special rows")
+    q = O.unpack_int4(c)
+    assert not q[0].any() and not q[2].any() and not q[3].any()
+    assert set(np.abs(q[1]).tolist()) == {7}
+    assert s.view(np.uint16)[3] == 0x7C00 and 0 < s.view(np.uint16)[4] < 0x0400
+
+
+@pytest.mark.parametrize("m,k,d", [(4, 40, 14336), (300, 256, 14336), (4, 40, 28672),
+                                   (300, 256, 28672)])
+def test_linear_28x512(rq, m, k, d):
+    """A W4A4 linear with d = 14336 or 28672 (the down projection widths): the
+    fold and the online rotation with H_28 (x) H_512 or H_28 (x) H_1024, then
+    the decode (m = 4) or the large (m = 300) GEMM, against the oracle."""
+    rng = np.random.default_rng(m + k + d)
     x = (rng.standard_normal((m, d)) * np.where(rng.random(d) < 0.001, 100.0, 1.0)).astype(np.float16)
     wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
     signs = datagen.rademacher(rng, d)
-    say(f"linear d=28x512 m={m} k={k}")
+    say(f"linear d={d} m={m} k={k}")
     s = dev(signs)
     wc, ws, wr = rq.fold_weights(dev(wt), s, debug=True)
     ac, sa, xr = rq.fwht_quant(dev(x), s, debug=True)
     y, acc = rq.w4a4_gemm(ac, sa, wc, ws, debug=True)
     torch.cuda.synchronize()
-    check_rotation_result(wt, signs, host(wc), host(ws), host(wr), what="fold d=28x512")
-    check_rotation_result(x, signs, host(ac), host(sa), host(xr), what="activations d=28x512")
-    check_gemm(host(ac), host(sa), host(wc), host(ws), host(y), host(acc), what="gemm d=28x512")
+    check_rotation_result(wt, signs, host(wc), host(ws), host(wr), what=f"fold d={d}")
+    check_rotation_result(x, signs, host(ac), host(sa), host(xr), what=f"activations d={d}")
+    check_gemm(host(ac), host(sa), host(wc), host(ws), host(y), host(acc), what=f"gemm d={d}")
 
 
 @pytest.mark.parametrize("n", [4096, 8192])
@@ -421,6 +457,40 @@ def test_prefill_gemm_full_size_sampled(rq):
     c_rows = wc_h[wrows]
     s_rows = ws_h[wrows]
     check_rotation_result(w["wt"][wrows], w["signs"], c_rows, s_rows, None, what="fold 28672 sampled")
+
+
+def test_downproj_28672_full_size_sampled(rq):
+    """The down projection of the prefill-shaped model as the benchmark runs
+    it: 2048 tokens x 28672 fp16 (0.1% of channels x100) rotated with
+    H_28 (x) H_1024, W^T 8192 x 28672 ~ N(0, 0.02^2) folded with the same
+    signs, then the persistent prefill GEMM (d = 28672 -> k = 8192); the
+    rotation on sampled rows, the GEMM on every row x sampled columns and
+    sampled rows x every column, exact accumulators."""
+    m, d, k = 2048, 28672, 8192
+    rng = np.random.default_rng(7)
+    x = datagen.activations(rng, m, d, datagen.outlier_channels(rng, d), 100.0)
+    signs = datagen.rademacher(rng, d)
+    say("down projection: fold 8192 x 28672 fp32")
+    s = dev(signs)
+    wt = datagen.gaussian(rng, (k, d), std=0.02)
+    wc, ws, _ = rq.fold_weights(dev(wt), s)
+    say("down projection: rotate 2048 x 28672, gemm 2048 x 28672 -> 8192")
+    co, so = Out((m, d // 2), torch.uint8), Out((m,), torch.float16)
+    rq.fwht_quant(dev(x), s, out=(co.t, so.t))
+    yo, ao = Out((m, k), torch.float16), Out((m, k), torch.int32)
+    rq.w4a4_gemm(co.t, so.t, wc, ws, debug=True, out=yo.t, acc_out=ao.t)
+    y2 = Out((m, k), torch.float16, SENTINELS[1])
+    rq.w4a4_gemm(co.t, so.t, wc, ws, out=y2.t)  # the launch the benchmark times
+    check_all([co, so, yo, ao, y2], "down projection")
+    assert torch.equal(yo.t.view(torch.int16), y2.t.view(torch.int16))
+    ac, sa, wc_h, ws_h, y, acc = co.host(), so.host(), host(wc), host(ws), yo.host(), ao.host()
+    rows = np.sort(rng.choice(m, 64, replace=False))
+    cols = np.sort(rng.choice(k, 128, replace=False))
+    check_rotation_result(x, signs, ac, sa, None, what="down projection rows", rows=rows)
+    check_gemm(ac, sa, wc_h, ws_h, y, acc, what="down projection cols", cols=cols)
+    check_gemm(ac, sa, wc_h, ws_h, y, acc, what="down projection rows", rows=rows)
+    wrows = np.sort(rng.choice(k, 128, replace=False))
+    check_rotation_result(wt[wrows], signs, wc_h[wrows], ws_h[wrows], None, what="fold 28672 sampled")
 
 
 def test_kv_small_and_ragged(rq):
