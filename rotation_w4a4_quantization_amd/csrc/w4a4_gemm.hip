@@ -366,32 +366,52 @@ __device__ __forceinline__ void dec_issue_w(const DecLane<RG>& t, int64_t c0) {
   }
 }
 
-// Activation fragments of the chunk, wait for them and for the chunk's
-// weights, then the MFMAs; this wave's LDS reads are back on return (before
-// its next loads may overwrite them).  A8: the activations are INT8 codes
-// (one byte per code, a_src advancing 2 bytes per weight byte), so a lane's
-// 32 codes of a part take two 16-byte loads.
-template <int RG, int AM = kA4>
-__device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsigned char* wl,
-                                              const uint8_t* a_src, bool a_ok, int64_t c0,
-                                              v4i (&acc0)[RG], v4i (&acc1)[RG]) {
-  constexpr int SEGB = 16 * RG * DSEG;
-  constexpr bool A8 = AM == kA8;
-  constexpr int AW = A8 ? 2 : 1;  // 16-byte activation loads per part
-  uint4 av[2][2][AW];
+// Activation fragments of this wave's two parts of the chunk that starts at
+// segment c0 (16 bytes per lane and half: a 32-code part; A8: two loads, the
+// INT8 codes of the same 32 positions).  Every load is unconditional, from a
+// clamped address that is always valid: rows past m re-read row 0 (a_src)
+// and feed only outputs that are not stored, segments past the end re-read
+// the last one and are skipped by the MFMAs.  A register refilled by a load
+// under a branch would get a wait for every load in flight (the weight DMA
+// included, which the compiler cannot see).
+template <int AM = kA4>
+__device__ __forceinline__ void dec_load_act(int wave, int64_t nseg, const uint8_t* a_src,
+                                             int64_t c0, uint4 (&av)[2][2][AM == kA8 ? 2 : 1]) {
+  constexpr int AW = AM == kA8 ? 2 : 1;
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
-    const int64_t seg = c0 + 2 * t.wave + sl;
+    const int64_t seg = c0 + 2 * wave + sl;
+    const int64_t segc = seg < nseg ? seg : nseg - 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int u = 0; u < AW; ++u) {
-        av[sl][h][u] = make_uint4(0, 0, 0, 0);
-        if (a_ok && seg < t.nseg)
-          av[sl][h][u] =
-              *reinterpret_cast<const uint4*>(a_src + AW * (seg * DSEG + 64 * h) + 16 * u);
-      }
+      for (int u = 0; u < AW; ++u)
+        av[sl][h][u] = *reinterpret_cast<const uint4*>(a_src + AW * (segc * DSEG + 64 * h) + 16 * u);
   }
+}
+
+// Wait for the chunk's activation fragments (av) and weights, then the
+// MFMAs; this wave's LDS reads are back on return (before its next loads may
+// overwrite them).  A8: the activations are INT8 codes, two 16-byte loads per
+// 32-code part, put in widen's k order.
+template <int RG, int AM = kA4>
+__device__ __forceinline__ void dec_mma_loaded(const DecLane<RG>& t, const unsigned char* wl,
+                                               uint4 (&av)[2][2][AM == kA8 ? 2 : 1], int64_t c0,
+                                               v4i (&acc0)[RG], v4i (&acc1)[RG]) {
+  constexpr int SEGB = 16 * RG * DSEG;
+  constexpr bool A8 = AM == kA8;
+  constexpr int AW = A8 ? 2 : 1;
+  // The loads read kernel arguments the compiler treats as invariant, so it
+  // may sink them past the wait below into their uses: an empty asm that
+  // takes every loaded value keeps them issued before the wait.
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < AW; ++u)
+        asm volatile("" ::"v"(av[sl][h][u].x), "v"(av[sl][h][u].y), "v"(av[sl][h][u].z),
+                     "v"(av[sl][h][u].w));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
@@ -422,6 +442,75 @@ __device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsign
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// The same with the activation fragments read here from a_src (the fused
+// decode linear: its token codes are in LDS), after the chunk's weight loads.
+template <int RG, int AM = kA4>
+__device__ __forceinline__ void dec_mma_chunk(const DecLane<RG>& t, const unsigned char* wl,
+                                              const uint8_t* a_src, bool a_ok, int64_t c0,
+                                              v4i (&acc0)[RG], v4i (&acc1)[RG]) {
+  constexpr int AW = AM == kA8 ? 2 : 1;
+  uint4 av[2][2][AW];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    const int64_t seg = c0 + 2 * t.wave + sl;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < AW; ++u) {
+        av[sl][h][u] = make_uint4(0, 0, 0, 0);
+        if (a_ok && seg < t.nseg)
+          av[sl][h][u] =
+              *reinterpret_cast<const uint4*>(a_src + AW * (seg * DSEG + 64 * h) + 16 * u);
+      }
+  }
+  dec_mma_loaded<RG, AM>(t, wl, av, c0, acc0, acc1);
+}
+
+// Epilogue operands of the waves that finish a 16-row group (waves < RG):
+// the column's weight scale (and code sum) and the activation scales (and
+// zero points) of the lane's four rows, loaded with the first chunk, before
+// its wait, from clamped (always valid) addresses.
+struct DecEpi {
+  float sw = 0.0f, sa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int32_t ws = 0, za[4] = {0, 0, 0, 0};
+};
+
+template <int RG>
+__device__ __forceinline__ DecEpi dec_load_epi(const DecLane<RG>& t, int64_t m, int64_t k,
+                                               const uint16_t* __restrict__ a_scales,
+                                               const uint16_t* __restrict__ w_scales,
+                                               const uint8_t* __restrict__ a_zeros,
+                                               const int32_t* __restrict__ w_sums) {
+  DecEpi e;
+  if (t.wave < RG) {  // uniform per wave
+    const int64_t col = t.n0 + 16 * t.wave + t.r16;
+    const int64_t colc = col < k ? col : k - 1;
+    const uint32_t swb = w_scales[colc];
+    const int32_t wsv = w_sums != nullptr ? w_sums[colc] : 0;
+    uint32_t sab[4], zab[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = 4 * t.g + i;
+      const int64_t rowc = row < m ? row : m - 1;
+      sab[i] = a_scales[rowc];
+      zab[i] = a_zeros != nullptr ? a_zeros[rowc] : 0u;
+    }
+    // (the loads all issue here; taking their values waits for them, and
+    // everything issued before them, at once)
+    asm volatile("" ::"v"(swb), "v"(wsv));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(sab[i]), "v"(zab[i]));
+    e.sw = h2f((uint16_t)swb);
+    e.ws = wsv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e.sa[i] = h2f((uint16_t)sab[i]);
+      e.za[i] = (int32_t)zab[i];
+    }
+  }
+  return e;
+}
+
 // Partial sums of the 8 waves meet in LDS (wave w's RG x 64 sums start at
 // partial + w * pitch); waves 0..RG-1 finish one 16-row group each.
 template <int RG, int SHIFT = 8>
@@ -433,7 +522,8 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
                                                  uint16_t* __restrict__ y,
                                                  int32_t* __restrict__ acc_out,
                                                  const uint8_t* __restrict__ a_zeros = nullptr,
-                                                 const int32_t* __restrict__ w_sums = nullptr) {
+                                                 const int32_t* __restrict__ w_sums = nullptr,
+                                                 const DecEpi* epi = nullptr) {
 #pragma unroll
   for (int q = 0; q < RG; ++q) partial[t.wave * pitch + q * 64 + t.lane] = acc0[q] + acc1[q];
   __syncthreads();
@@ -443,14 +533,16 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
     for (int w = 1; w < DEC_WAVES; ++w) s += partial[w * pitch + t.wave * 64 + t.lane];
     const int64_t col = t.n0 + 16 * t.wave + t.r16;
     if (col < k) {
-      const float sw = h2f(w_scales[col]);
-      const int32_t ws = w_sums != nullptr ? w_sums[col] : 0;
+      const float sw = epi != nullptr ? epi->sw : h2f(w_scales[col]);
+      const int32_t ws = epi != nullptr ? epi->ws : (w_sums != nullptr ? w_sums[col] : 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 4 * t.g + e;
-        if (row < m)
-          epilogue_store<SHIFT>(s[e], h2f(a_scales[row]), sw, row * k + col, y, acc_out,
-                                a_zeros != nullptr ? (int32_t)a_zeros[row] * ws : 0);
+        if (row < m) {
+          const float sa = epi != nullptr ? epi->sa[e] : h2f(a_scales[row]);
+          const int32_t z = epi != nullptr ? epi->za[e] : (a_zeros != nullptr ? (int32_t)a_zeros[row] : 0);
+          epilogue_store<SHIFT>(s[e], sa, sw, row * k + col, y, acc_out, z * ws);
+        }
       }
     }
   }
@@ -478,14 +570,23 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
   v4i acc0[RG], acc1[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
+  DecEpi epi;
   for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
+    // the activation fragments (L2-resident, read by every workgroup) go out
+    // ahead of the chunk's weights, and the epilogue's scales with the first
+    // chunk, so neither adds a memory round trip after the weights are in
+    uint4 av[2][2][AW];
+    dec_load_act<AM>(t.wave, t.nseg, a_src, c0, av);
     dec_issue_w(t, c0);
-    dec_mma_chunk<RG, AM>(t, wl, a_src, a_ok, c0, acc0, acc1);
+    if (c0 == 0)
+      epi = dec_load_epi(t, m, k, a_scales, w_scales, AM == kAU4 ? a_zeros : nullptr,
+                         AM == kAU4 ? w_sums : nullptr);
+    dec_mma_loaded<RG, AM>(t, wl, av, c0, acc0, acc1);
   }
   dec_reduce_store<RG, AM == kA4 ? 8 : 4>(t, &partial[0][0][0], RG * 64, acc0, acc1, m, k,
                                           a_scales, w_scales, y, acc_out,
                                           AM == kAU4 ? a_zeros : nullptr,
-                                          AM == kAU4 ? w_sums : nullptr);
+                                          AM == kAU4 ? w_sums : nullptr, &epi);
 }
 
 // ------------------------------------------- decode GEMM, per-group scales
@@ -495,34 +596,41 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_lds_kernel(
 // turns into fp32 with the group's scale.  The scales load with the
 // activation fragments, before the chunk's wait.
 template <int RG>
-__device__ __forceinline__ void dec_mma_chunk_grouped(const DecLane<RG>& t,
-                                                      const unsigned char* wl,
-                                                      const uint8_t* a_src, int64_t c0,
-                                                      const uint16_t* __restrict__ wg_scales,
-                                                      int64_t ngroups, int64_t k,
-                                                      v4f (&facc)[RG]) {
-  constexpr int SEGB = 16 * RG * DSEG;
+struct DecGroupedLoads {
+  uint4 av[2][2];
+  uint16_t sc[2][2][RG];
+};
+
+template <int RG>
+__device__ __forceinline__ void dec_load_grouped(const DecLane<RG>& t, const uint8_t* a_src,
+                                                 int64_t c0, const uint16_t* __restrict__ wg_scales,
+                                                 int64_t ngroups, int64_t k, DecGroupedLoads<RG>& l) {
   // Every load is unconditional, from a clamped address that is always
   // valid: rows past m re-read row 0 (a_src) and feed only outputs that are
   // not stored, and parts past the end are skipped below.  A zeroed register
   // refilled by a load under a branch would get a wait for every load in
   // flight (the weight stream included, which the compiler cannot see).
-  uint4 av[2][2];
-  uint16_t sc[2][2][RG];
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     const int64_t seg = c0 + 2 * t.wave + sl;
     const int64_t segc = seg < t.nseg ? seg : t.nseg - 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      av[sl][h] = *reinterpret_cast<const uint4*>(a_src + segc * DSEG + 64 * h);
+      l.av[sl][h] = *reinterpret_cast<const uint4*>(a_src + segc * DSEG + 64 * h);
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         const int64_t col = t.n0 + 16 * q + t.r16;
-        sc[sl][h][q] = wg_scales[(col < k ? col : k - 1) * ngroups + 2 * segc + h];
+        l.sc[sl][h][q] = wg_scales[(col < k ? col : k - 1) * ngroups + 2 * segc + h];
       }
     }
   }
+}
+
+template <int RG>
+__device__ __forceinline__ void dec_mma_grouped(const DecLane<RG>& t, const unsigned char* wl,
+                                                DecGroupedLoads<RG>& l, int64_t c0,
+                                                v4f (&facc)[RG]) {
+  constexpr int SEGB = 16 * RG * DSEG;
   // The loads read kernel arguments the compiler treats as invariant, so it
   // may sink them past the wait below into their uses (each then pays a
   // memory latency of its own): an empty asm that takes every loaded value
@@ -531,9 +639,9 @@ __device__ __forceinline__ void dec_mma_chunk_grouped(const DecLane<RG>& t,
   for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      asm volatile("" ::"v"(av[sl][h].x), "v"(av[sl][h].y), "v"(av[sl][h].z), "v"(av[sl][h].w));
+      asm volatile("" ::"v"(l.av[sl][h].x), "v"(l.av[sl][h].y), "v"(l.av[sl][h].z), "v"(l.av[sl][h].w));
 #pragma unroll
-      for (int q = 0; q < RG; ++q) asm volatile("" ::"v"(sc[sl][h][q]));
+      for (int q = 0; q < RG; ++q) asm volatile("" ::"v"(l.sc[sl][h][q]));
     }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
@@ -541,7 +649,7 @@ __device__ __forceinline__ void dec_mma_chunk_grouped(const DecLane<RG>& t,
     if (c0 + 2 * t.wave + sl >= t.nseg) continue;  // uniform per wave
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const v4i a0 = widen(av[sl][h].x, av[sl][h].y), a1 = widen(av[sl][h].z, av[sl][h].w);
+      const v4i a0 = widen(l.av[sl][h].x, l.av[sl][h].y), a1 = widen(l.av[sl][h].z, l.av[sl][h].w);
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         const uint4 w = *reinterpret_cast<const uint4*>(
@@ -549,7 +657,7 @@ __device__ __forceinline__ void dec_mma_chunk_grouped(const DecLane<RG>& t,
             16 * ((4 * h + t.g) ^ (t.r16 & 7)));
         v4i pg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, widen(w.x, w.y), v4i{0, 0, 0, 0}, 0, 0, 0);
         pg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, widen(w.z, w.w), pg, 0, 0, 0);
-        const float sg = h2f(sc[sl][h][q]);
+        const float sg = h2f(l.sc[sl][h][q]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) facc[q][e] = __builtin_fmaf((float)pg[e], sg, facc[q][e]);
       }
@@ -574,9 +682,15 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
   v4f facc[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) facc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  DecEpi epi;
   for (int64_t c0 = 0; c0 < t.nseg; c0 += DCHUNK) {
+    // activation fragments and group scales ahead of the chunk's weights,
+    // the epilogue's activation scales with the first chunk
+    DecGroupedLoads<RG> l;
+    dec_load_grouped<RG>(t, a_src, c0, wg_scales, ngroups, k, l);
     dec_issue_w(t, c0);
-    dec_mma_chunk_grouped<RG>(t, wl, a_src, c0, wg_scales, ngroups, k, facc);
+    if (c0 == 0) epi = dec_load_epi(t, m, k, a_scales, wg_scales, nullptr, nullptr);
+    dec_mma_grouped<RG>(t, wl, l, c0, facc);
   }
 #pragma unroll
   for (int q = 0; q < RG; ++q) partial[t.wave][q][t.lane] = facc[q];
@@ -590,7 +704,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 4 * t.g + e;
-        if (row < m) y[row * k + col] = f2h_rn((sum[e] * (1.0f / 256.0f)) * h2f(a_scales[row]));
+        if (row < m) y[row * k + col] = f2h_rn((sum[e] * (1.0f / 256.0f)) * epi.sa[e]);
       }
     }
   }
