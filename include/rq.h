@@ -395,10 +395,14 @@ int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, u
  *                   pairs as dwords; otherwise on the tile kernel).
  *   m >= 0; k >= 1 when m > 0; d a multiple of 128 in [128, RQ_MAX_D].
  *   y               [m][k] fp16 output.
+ *   acc             optional [m][k][d / 128] int32 output (debug) of every
+ *                   group's exact integer sum acc[m][j][g], or NULL; it
+ *                   selects an instantiation of the same kernels that also
+ *                   stores them.
  */
 int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                          const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
-                         int64_t d, uint16_t* y, void* stream);
+                         int64_t d, uint16_t* y, int32_t* acc, void* stream);
 
 /*
  * rq_decode_attention_workspace_size -- bytes of device workspace that

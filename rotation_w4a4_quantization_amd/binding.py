@@ -89,7 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_w4a4_gemm_asym.restype = i32
     lib.rq_quantize_groups.argtypes = [p, i64, i64, i64, p, p, p]
     lib.rq_quantize_groups.restype = i32
-    lib.rq_w4a4_gemm_grouped.argtypes = [p, p, i64, p, p, i64, i64, p, p]
+    lib.rq_w4a4_gemm_grouped.argtypes = [p, p, i64, p, p, i64, i64, p, p, p]
     lib.rq_w4a4_gemm_grouped.restype = i32
     lib.rq_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64]
     lib.rq_decode_attention_workspace_size.restype = sz
@@ -480,8 +480,10 @@ def fold_weights_grouped(wt: torch.Tensor, signs: torch.Tensor | None = None, gr
 
 
 def w4a4_gemm_grouped(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
-                      w_group_scales: torch.Tensor, out: torch.Tensor | None = None):
-    """rq_w4a4_gemm_grouped (group 128): returns y fp16 [m, k]."""
+                      w_group_scales: torch.Tensor, out: torch.Tensor | None = None,
+                      debug: bool = False, acc_out: torch.Tensor | None = None):
+    """rq_w4a4_gemm_grouped (group 128): returns y fp16 [m, k], or with
+    debug=True (y, acc int32 [m, k, d / 128]: every group's integer sum)."""
     for name, t in (("a_codes", a_codes), ("a_scales", a_scales), ("w_codes", w_codes),
                     ("w_group_scales", w_group_scales)):
         _need_cuda(name, t)
@@ -495,10 +497,12 @@ def w4a4_gemm_grouped(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: to
     if half_d != half_d2 or a_scales.numel() != m or w_group_scales.numel() != k * (d // 128):
         raise ValueError("shapes do not match")
     y = _out("out", out, (m, k), torch.float16, a_codes.device)
+    acc = _out("acc_out", acc_out, (m, k, d // 128), torch.int32, a_codes.device) if debug else None
     st = load_library().rq_w4a4_gemm_grouped(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes),
-                                             _ptr(w_group_scales), k, d, _ptr(y), _stream())
+                                             _ptr(w_group_scales), k, d, _ptr(y), _ptr(acc),
+                                             _stream())
     _check("rq_w4a4_gemm_grouped", st)
-    return y
+    return (y, acc) if debug else y
 
 
 def decode_attention_workspace(batch: int, kv_heads: int, group: int, seq: int,

@@ -174,7 +174,7 @@ int rq_quantize_groups(const float* x, int64_t rows, int64_t n, int64_t group, u
 
 int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                          const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
-                         int64_t d, uint16_t* y, void* stream) {
+                         int64_t d, uint16_t* y, int32_t* acc, void* stream) {
   if (m < 0 || k < 0 || d < 128 || d > RQ_MAX_D || d % 128 != 0) return RQ_ERR_SHAPE;
   if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
@@ -185,7 +185,7 @@ int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64
     return RQ_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
   return from_hip(rq::launch_w4a4_gemm_grouped(a_codes, a_scales, m, w_codes, w_group_scales, k,
-                                               d, y, static_cast<hipStream_t>(stream)));
+                                               d, y, acc, static_cast<hipStream_t>(stream)));
 }
 
 size_t rq_linear_decode_workspace_size(int64_t m, int64_t d) {

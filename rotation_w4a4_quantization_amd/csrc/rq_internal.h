@@ -54,12 +54,13 @@ hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d,
 
 // Per-group INT4 weights: symmetric INT4 with one scale per `group`
 // elements of fp32 rows (group 32, 64, 128 or 256), and the W4A4 GEMM with
-// per-group weight scales (group 128, wg_scales [k][d / 128]).
+// per-group weight scales (group 128, wg_scales [k][d / 128]; gacc, when
+// not null, receives the int32 sum of every group, [m][k][d / 128]).
 hipError_t launch_quantize_groups(const float* x, int64_t rows, int64_t n, int group,
                                   uint8_t* codes, uint16_t* scales, hipStream_t stream);
 hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                                     const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
-                                    int64_t d, uint16_t* y, hipStream_t stream);
+                                    int64_t d, uint16_t* y, int32_t* gacc, hipStream_t stream);
 
 // Decode attention over the 4-bit rotated KV cache (head_dim 128, G <= 8
 // query heads per KV head); the workspace holds one (max, sum, output)

@@ -97,7 +97,7 @@ constexpr int PITCH8 = TK + 16;   // INT8 activation rows (64 bytes per step), 1
 // unsigned INT4 with zero points a_zeros and weight code sums w_sums).
 // GROUPED (with kA4): w_scales holds per-group scales [k][d / WG]; every
 // two 64-code steps (one group) the int32 tile turns into fp32 with its
-// group scale.
+// group scale, and (debug) acc_out [m][k][d / WG] receives the group sums.
 template <int AM = kA4, bool GROUPED = false>
 __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restrict__ a_codes,
                                                         const uint16_t* __restrict__ a_scales,
@@ -186,6 +186,13 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
           const float sg = h2f(w_scales[(col < k ? col : k - 1) * ngroups + grp]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            if (acc_out != nullptr) {  // debug: the exact int32 group sums
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
+                if (row < m && col < k) acc_out[(row * k + col) * ngroups + grp] = acc[i][j][e] >> 8;
+              }
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) facc[i][j][e] = __builtin_fmaf((float)acc[i][j][e], sg, facc[i][j][e]);
             acc[i][j] = v4i{0, 0, 0, 0};
@@ -626,10 +633,11 @@ __device__ __forceinline__ void dec_load_grouped(const DecLane<RG>& t, const uin
   }
 }
 
-template <int RG>
+template <int RG, bool GACC = false>
 __device__ __forceinline__ void dec_mma_grouped(const DecLane<RG>& t, const unsigned char* wl,
                                                 DecGroupedLoads<RG>& l, int64_t c0,
-                                                v4f (&facc)[RG]) {
+                                                v4f (&facc)[RG], int64_t m = 0, int64_t k = 0,
+                                                int64_t ngroups = 0, int32_t* gacc = nullptr) {
   constexpr int SEGB = 16 * RG * DSEG;
   // The loads read kernel arguments the compiler treats as invariant, so it
   // may sink them past the wait below into their uses (each then pays a
@@ -657,6 +665,15 @@ __device__ __forceinline__ void dec_mma_grouped(const DecLane<RG>& t, const unsi
             16 * ((4 * h + t.g) ^ (t.r16 & 7)));
         v4i pg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, widen(w.x, w.y), v4i{0, 0, 0, 0}, 0, 0, 0);
         pg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, widen(w.z, w.w), pg, 0, 0, 0);
+        if constexpr (GACC) {  // debug: the exact int32 sum of group 2 seg + h
+          const int64_t col = t.n0 + 16 * q + t.r16;
+          const int64_t grp = 2 * (c0 + 2 * t.wave + sl) + h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t row = 4 * t.g + e;
+            if (row < m && col < k) gacc[(row * k + col) * ngroups + grp] = pg[e] >> 8;
+          }
+        }
         const float sg = h2f(l.sc[sl][h][q]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) facc[q][e] = __builtin_fmaf((float)pg[e], sg, facc[q][e]);
@@ -666,11 +683,11 @@ __device__ __forceinline__ void dec_mma_grouped(const DecLane<RG>& t, const unsi
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <int RG>
+template <int RG, bool GACC = false>
 __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
     const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ wg_scales, int64_t m,
-    int64_t k, int64_t d, uint16_t* __restrict__ y) {
+    int64_t k, int64_t d, uint16_t* __restrict__ y, int32_t* __restrict__ gacc) {
   __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];
   __shared__ v4f partial[DEC_WAVES][RG][64];
   const int64_t rowb = d / 2;
@@ -690,7 +707,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
     dec_load_grouped<RG>(t, a_src, c0, wg_scales, ngroups, k, l);
     dec_issue_w(t, c0);
     if (c0 == 0) epi = dec_load_epi(t, m, k, a_scales, wg_scales, nullptr, nullptr);
-    dec_mma_grouped<RG>(t, wl, l, c0, facc);
+    dec_mma_grouped<RG, GACC>(t, wl, l, c0, facc, m, k, ngroups, gacc);
   }
 #pragma unroll
   for (int q = 0; q < RG; ++q) partial[t.wave][q][t.lane] = facc[q];
@@ -938,7 +955,7 @@ __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); 
 // group scales of its B rows (4 bytes a row, dword DMA by waves 0..3); per
 // half step every (i, j) tile's int32 sum over the group is two MFMAs from
 // zero, and it turns into fp32 with its column's group scale.
-template <int AM = kA4, bool GROUPED = false>
+template <int AM = kA4, bool GROUPED = false, bool GACC = false>
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
                                                               const uint8_t* __restrict__ w_codes,
@@ -951,6 +968,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
                                                               const int32_t* __restrict__ w_sums) {
   static_assert(AM == kA4 || AM == kAU4 || AM == kA8, "activation format");
   static_assert(!GROUPED || AM == kA4, "group scales with symmetric INT4 activations");
+  static_assert(!GACC || GROUPED, "group sums are an output of the grouped GEMM");
   constexpr bool A8 = AM == kA8;
   constexpr int SHIFT = AM == kA4 ? 8 : 4;
   constexpr int KSTEP = A8 ? LK / 2 : LK;       // codes per step
@@ -1120,6 +1138,17 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               t[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, t[i], 0, 0, 0);
+            if constexpr (GACC) {  // debug: the exact int32 sum of group 2 s + u
+              const int64_t col = n0 + wn * 112 + j * 16 + r16;
+              const int64_t ng = d / WG, grp = 2 * (int64_t)s + u;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + e;
+                  if (row < m && col < k) acc_out[(row * k + col) * ng + grp] = t[i][e] >> 8;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1358,7 +1387,7 @@ hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d,
 // Shapes the persistent prefill kernel takes (d: whole 256-code steps).
 bool large_shape(int64_t m, int64_t k, int64_t d) { return m >= 128 && k >= 224 && d % LK == 0; }
 
-template <int AM, bool GROUPED = false>
+template <int AM, bool GROUPED = false, bool GACC = false>
 hipError_t launch_large(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
                         int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
                         const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
@@ -1369,7 +1398,7 @@ hipError_t launch_large(const uint8_t* a_codes, const uint16_t* a_scales, const 
   const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
   // 16-byte output stores need 16-byte aligned rows and no int32 output
   const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-  hipLaunchKernelGGL((w4a4_large_kernel<AM, GROUPED>), dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
+  hipLaunchKernelGGL((w4a4_large_kernel<AM, GROUPED, GACC>), dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
                      a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles, wide_store,
                      y, acc, a_zeros, w_sums);
   return hipGetLastError();
@@ -1433,25 +1462,34 @@ hipError_t launch_gemm_variant(const uint8_t* a, const uint16_t* a_scales, const
 
 hipError_t launch_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                                     const uint8_t* w_codes, const uint16_t* wg_scales, int64_t k,
-                                    int64_t d, uint16_t* y, hipStream_t stream) {
+                                    int64_t d, uint16_t* y, int32_t* gacc, hipStream_t stream) {
   // the persistent prefill kernel (a half step is one group) reads each row's
   // two group scales of a step as one dword: 4-byte aligned scales only
   if (large_shape(m, k, d) && (reinterpret_cast<uintptr_t>(wg_scales) & 3u) == 0)
-    return launch_large<kA4, true>(a_codes, a_scales, nullptr, m, w_codes, wg_scales, nullptr, k,
-                                   d, y, nullptr, stream);
+    return gacc != nullptr
+               ? launch_large<kA4, true, true>(a_codes, a_scales, nullptr, m, w_codes, wg_scales,
+                                               nullptr, k, d, y, gacc, stream)
+               : launch_large<kA4, true>(a_codes, a_scales, nullptr, m, w_codes, wg_scales,
+                                         nullptr, k, d, y, nullptr, stream);
   if (m <= 16 && d % (2 * DSEG) == 0) {
-    if (m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2)
-      hipLaunchKernelGGL(w4a4_decode_grouped_kernel<2>, dim3((unsigned)((k + 31) / 32)),
-                         dim3(64 * DEC_WAVES), 0, stream, a_codes, a_scales, w_codes, wg_scales, m,
-                         k, d, y);
+    const bool rg2 = m > 4 && (k + 31) / 32 >= (int64_t)cu_count() * 3 / 2;
+    const dim3 grid((unsigned)(rg2 ? (k + 31) / 32 : (k + 15) / 16));
+    if (rg2 && gacc != nullptr)
+      hipLaunchKernelGGL((w4a4_decode_grouped_kernel<2, true>), grid, dim3(64 * DEC_WAVES), 0,
+                         stream, a_codes, a_scales, w_codes, wg_scales, m, k, d, y, gacc);
+    else if (rg2)
+      hipLaunchKernelGGL((w4a4_decode_grouped_kernel<2>), grid, dim3(64 * DEC_WAVES), 0, stream,
+                         a_codes, a_scales, w_codes, wg_scales, m, k, d, y, nullptr);
+    else if (gacc != nullptr)
+      hipLaunchKernelGGL((w4a4_decode_grouped_kernel<1, true>), grid, dim3(64 * DEC_WAVES), 0,
+                         stream, a_codes, a_scales, w_codes, wg_scales, m, k, d, y, gacc);
     else
-      hipLaunchKernelGGL(w4a4_decode_grouped_kernel<1>, dim3((unsigned)((k + 15) / 16)),
-                         dim3(64 * DEC_WAVES), 0, stream, a_codes, a_scales, w_codes, wg_scales, m,
-                         k, d, y);
+      hipLaunchKernelGGL((w4a4_decode_grouped_kernel<1>), grid, dim3(64 * DEC_WAVES), 0, stream,
+                         a_codes, a_scales, w_codes, wg_scales, m, k, d, y, nullptr);
   } else {
     const dim3 grid((unsigned)((k + TN - 1) / TN), (unsigned)((m + TM - 1) / TM));
     hipLaunchKernelGGL((w4a4_tile_kernel<kA4, true>), grid, dim3(256), 0, stream, a_codes,
-                       a_scales, w_codes, wg_scales, m, k, d, y, nullptr, nullptr, nullptr);
+                       a_scales, w_codes, wg_scales, m, k, d, y, gacc, nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -237,11 +237,11 @@ def test_grouped_argument_errors(lib):
     assert q(A16, 4, 64, 128, A16b, A16b, None) == binding.RQ_ERR_SHAPE
     assert q(MIS, 4, 4096, 128, A16b, A16b, None) == binding.RQ_ERR_ALIGN
     g = lib.rq_w4a4_gemm_grouped
-    assert g(A16, A16b, 0, A16, A16b, 64, 4096, A16b, None) == binding.RQ_OK
-    assert g(A16, A16b, 4, A16, None, 64, 4096, A16b, None) == binding.RQ_ERR_NULL
-    assert g(A16, A16b, 4, A16, A16b, 64, 192, A16b, None) == binding.RQ_ERR_SHAPE
-    assert g(A16, A16b, 4, A16, A16b, 0, 4096, A16b, None) == binding.RQ_ERR_SHAPE
-    assert g(MIS, A16b, 4, A16, A16b, 64, 4096, A16b, None) == binding.RQ_ERR_ALIGN
+    assert g(A16, A16b, 0, A16, A16b, 64, 4096, A16b, None, None) == binding.RQ_OK
+    assert g(A16, A16b, 4, A16, None, 64, 4096, A16b, None, None) == binding.RQ_ERR_NULL
+    assert g(A16, A16b, 4, A16, A16b, 64, 192, A16b, None, None) == binding.RQ_ERR_SHAPE
+    assert g(A16, A16b, 4, A16, A16b, 0, 4096, A16b, None, None) == binding.RQ_ERR_SHAPE
+    assert g(MIS, A16b, 4, A16, A16b, 64, 4096, A16b, None, None) == binding.RQ_ERR_ALIGN
 
 
 def test_decode_attention_argument_errors(lib):

@@ -57,8 +57,13 @@ def check_groups(x, group, codes, scales, what):
     return int(bad.sum())
 
 
-def check_gemm_grouped(ac, sa, wc, sw, y, what):
+def check_gemm_grouped(ac, sa, wc, sw, y, what, gacc=None):
+    """y within the tolerance; gacc (the kernel's int32 group sums
+    [m][k][d / 128], when given) exactly equal to the oracle's."""
     y_ref, acc = O.w4a4_gemm_grouped(ac, sa, wc, sw)
+    if gacc is not None:
+        assert np.array_equal(gacc.astype(np.int64), acc), \
+            f"{what}: int32 group sums differ in {int((gacc != acc).sum())} places"
     k = wc.shape[0]
     ng = acc.shape[-1]
     absum = np.abs(acc.astype(np.float64) * sw.astype(np.float64).reshape(k, ng)[None]).sum(-1)
@@ -113,14 +118,17 @@ def test_w4a4_gemm_grouped_random_codes(rq, m, k, d):
     sa = datagen.random_scales(rng, m)
     sw = datagen.random_scales(rng, k * (d // 128)).reshape(k, d // 128)
     say(f"grouped gemm m={m} k={k} d={d}")
-    first = None
-    for sentinel in SENTINELS:
+    # debug launch: the exact int32 sum of every group against the oracle's
+    yd, gd = Out((m, k), torch.float16), Out((m, k, d // 128), torch.int32)
+    rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw), out=yd.t, debug=True, acc_out=gd.t)
+    check_all([yd, gd], "grouped gemm debug")
+    check_gemm_grouped(ac, sa, wc, sw, yd.host(), f"grouped {m}x{k}x{d} debug", gacc=gd.host())
+    for sentinel in SENTINELS:  # the launch the benchmark times
         yo = Out((m, k), torch.float16, sentinel)
         rq.w4a4_gemm_grouped(dev(ac), dev(sa), dev(wc), dev(sw), out=yo.t)
         check_all([yo], "grouped gemm")
         check_gemm_grouped(ac, sa, wc, sw, yo.host(), f"grouped {m}x{k}x{d}")
-        first = yo.host() if first is None else first
-        assert np.array_equal(yo.host().view(np.uint16), first.view(np.uint16))
+        assert np.array_equal(yo.host().view(np.uint16), yd.host().view(np.uint16))
 
 
 def test_grouped_prefill_scales_2_byte_aligned(rq):
@@ -185,13 +193,22 @@ def test_grouped_prefill_full_size_sampled(rq):
     wc, wsg = rq.fold_weights_grouped(dev(w["wt"]), s, 128)
     ac, sa, _ = rq.fwht_quant(dev(w["x"]), s)
     say("grouped prefill: gemm 2048x8192 -> 28672")
-    yo = Out((ac.shape[0], wc.shape[0]), torch.float16)
-    rq.w4a4_gemm_grouped(ac, sa, wc, wsg, out=yo.t)
+    m, k = ac.shape[0], wc.shape[0]
+    yo = Out((m, k), torch.float16)
+    rq.w4a4_gemm_grouped(ac, sa, wc, wsg, out=yo.t)  # the launch the benchmark times
     check_all([yo], "grouped prefill")
-    ac, sa, wc, wsg, y = map(host, (ac, sa, wc, wsg, yo.t))
-    del yo
+    # the debug launch writes every group's int32 sum (2048 x 28672 x 64 words)
+    yd, gd = Out((m, k), torch.float16), Out((m, k, 64), torch.int32)
+    rq.w4a4_gemm_grouped(ac, sa, wc, wsg, out=yd.t, debug=True, acc_out=gd.t)
+    check_all([yd, gd], "grouped prefill debug")
+    assert torch.equal(yo.t.view(torch.int16), yd.t.view(torch.int16))
     rng = np.random.default_rng(80)
     rows = np.sort(rng.choice(2048, 16, replace=False))
     cols = np.sort(rng.choice(28672, 64, replace=False))
-    check_gemm_grouped(ac, sa, wc[cols], wsg[cols], y[:, cols], "grouped prefill cols")
-    check_gemm_grouped(ac[rows], sa[rows], wc, wsg, y[rows], "grouped prefill rows")
+    rows_t, cols_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    g_rows, g_cols = host(gd.t[rows_t]), host(gd.t[:, cols_t])
+    del gd, yd
+    ac, sa, wc, wsg, y = map(host, (ac, sa, wc, wsg, yo.t))
+    del yo
+    check_gemm_grouped(ac, sa, wc[cols], wsg[cols], y[:, cols], "grouped prefill cols", gacc=g_cols)
+    check_gemm_grouped(ac[rows], sa[rows], wc, wsg, y[rows], "grouped prefill rows", gacc=g_rows)
