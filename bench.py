@@ -498,7 +498,8 @@ def main():
             del x8s, o8, x8
             dec = datagen.decode_linear(0)
             s = torch.from_numpy(dec["signs"]).to(dev)
-            ac8, sa8, _ = rq.fwht_quant8(torch.from_numpy(dec["x"]).to(dev), s)
+            xd = torch.from_numpy(dec["x"]).to(dev)
+            ac8, sa8, _ = rq.fwht_quant8(xd, s)
             for k, wt in dec["wts"].items():
                 wc, ws, _ = rq.fold_weights(torch.from_numpy(wt).to(dev), s)
                 nsets = max(2, -(-2 * MALL_BYTES // wc.numel()) + 1)
@@ -510,12 +511,36 @@ def main():
                     def g8(i, a_m=a_m, s_m=s_m, y=y):
                         rq.w4a8_gemm(a_m, s_m, wcs[i], ws, out=y)
 
-                    msg = time_launches(torch, g8, nsets, steps2, warm2)
-                    bb = gemm8_bytes(mm, k, 4096)
                     key = f"gemm_w4a8_decode_m{mm}_k{k}"
-                    sec[key] = line(msg, **{"GB/s": round(bb / (msg * 1e-3) / 1e9, 1),
-                                "hbm_frac": round(bb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-                    log(f"[bench] {key}: {sec[key]}")
+                    if want_line(key):
+                        msg = time_launches(torch, g8, nsets, steps2, warm2)
+                        bb = gemm8_bytes(mm, k, 4096)
+                        sec[key] = line(msg, **{"GB/s": round(bb / (msg * 1e-3) / 1e9, 1),
+                                    "hbm_frac": round(bb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                        log(f"[bench] {key}: {sec[key]}")
+                    if mm > 4:
+                        continue
+                    # the whole W4A8 decode linear from fp16 tokens: two launches
+                    # (rotate + INT8 quantise, then the GEMM), and one (the rotation
+                    # as the GEMM's prologue)
+                    x_m = xd[:mm].contiguous()
+                    a_q = torch.empty((mm, 4096), dtype=torch.int8, device=dev)
+                    s_q = torch.empty((mm,), dtype=torch.float16, device=dev)
+
+                    def lin8_d(i, x_m=x_m, a_q=a_q, s_q=s_q, y=y, mm=mm):
+                        st = lib.rq_fwht_quant8(_ptr(x_m), mm, 4096, _ptr(s), _ptr(a_q), _ptr(s_q),
+                                                None, _stream())
+                        assert st == 0
+                        rq.w4a8_gemm(a_q, s_q, wcs[i], ws, out=y)
+
+                    def lin8_f(i, x_m=x_m, y=y):
+                        rq.linear_decode_w4a8(x_m, s, wcs[i], ws, out=y)
+
+                    for key, fn in ((f"linear_w4a8_decode_m{mm}_k{k}_rotate_plus_gemm", lin8_d),
+                                    (f"linear_w4a8_decode_m{mm}_k{k}_fused", lin8_f)):
+                        if want_line(key):
+                            sec[key] = line(time_launches(torch, fn, nsets, steps2, warm2))
+                            log(f"[bench] {key}: {sec[key]}")
                 del wcs, wc
             pf = datagen.prefill_linear(0)
             sp = torch.from_numpy(pf["signs"]).to(dev)

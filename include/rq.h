@@ -300,6 +300,34 @@ int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
                  uint16_t* y, int32_t* acc, void* stream);
 
 /*
+ * rq_linear_decode_w4a8 -- the decode-shaped W4A8 linear in one launch:
+ * rq_fwht_quant8 of the fp16 tokens, then rq_w4a8_gemm with the folded
+ * weights.
+ *
+ * [SpinQuant] "The architecture: every piece explained" (INT4 weights with
+ * 8-bit activations, the online rotation fused into the low-bit matmul).
+ * Every workgroup of the INT8-activation decode GEMM rotates and quantises
+ * the tokens into LDS as its prologue, with the device code of
+ * rq_fwht_quant8, while its weights stream in; y is bit-identical to
+ * rq_fwht_quant8 followed by rq_w4a8_gemm on the same arguments.  No
+ * workspace: the activation codes never leave the workgroup.
+ *
+ *   x          [m][d] fp16 tokens, 16-byte aligned.
+ *   m          tokens, 0 <= m <= 4 (m == 0 returns RQ_OK without launching;
+ *              more tokens: rq_fwht_quant8 then rq_w4a8_gemm).
+ *   d          input width, a power of two in [512, 8192].
+ *   signs      [d] int8 +-1 (the ones the weights were folded with), or NULL;
+ *              16-byte aligned when given.
+ *   w_codes    [k][d/2] folded weight codes (rq_fold_weights), 16-byte
+ *              aligned; w_scales [k] fp16.
+ *   k          output channels, >= 1.
+ *   y          [m][k] fp16 output.
+ */
+int rq_linear_decode_w4a8(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                          const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
+                          void* stream);
+
+/*
  * rq_fwht_quant_asym -- online rotation fused with asymmetric per-token INT4.
  *
  * [RQ] "The Activation Outlier Bottleneck in Low-Bit Serving" (a uniform

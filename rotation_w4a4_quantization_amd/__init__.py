@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     kv_rotate_quant,
     linear_decode,
     linear_decode_noalloc,
+    linear_decode_w4a8,
     linear_decode_workspace,
     quantize_groups,
     load_library,

@@ -28,6 +28,7 @@ EXPORTED = (
     "rq_linear_decode_workspace_size",
     "rq_linear_decode",
     "rq_linear_decode_noalloc",
+    "rq_linear_decode_w4a8",
     "rq_fwht_quant8",
     "rq_w4a8_gemm",
     "rq_fwht_quant_asym",
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_linear_decode.restype = i32
     lib.rq_linear_decode_noalloc.argtypes = [p, i64, i64, p, p, p, i64, p, p]
     lib.rq_linear_decode_noalloc.restype = i32
+    lib.rq_linear_decode_w4a8.argtypes = [p, i64, i64, p, p, p, i64, p, p]
+    lib.rq_linear_decode_w4a8.restype = i32
     lib.rq_fwht_quant8.argtypes = [p, i64, i64, p, p, p, p, p]
     lib.rq_fwht_quant8.restype = i32
     lib.rq_w4a8_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, p, p]
@@ -331,6 +334,29 @@ def linear_decode_noalloc(x: torch.Tensor, signs: torch.Tensor | None, w_codes: 
     st = load_library().rq_linear_decode_noalloc(_ptr(x), m, d, _ptr(s), _ptr(w_codes),
                                                  _ptr(w_scales), k, _ptr(y), _stream())
     _check("rq_linear_decode_noalloc", st)
+    return y
+
+
+def linear_decode_w4a8(x: torch.Tensor, signs: torch.Tensor | None, w_codes: torch.Tensor,
+                       w_scales: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """rq_linear_decode_w4a8: rotation + per-token INT8 quantisation of m <= 4
+    fp16 tokens and the W4A8 decode GEMM in one launch (y bit-identical to
+    fwht_quant8 then w4a8_gemm)."""
+    for name, t in (("x", x), ("w_codes", w_codes), ("w_scales", w_scales)):
+        _need_cuda(name, t)
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a float16 [m, d] tensor")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.float16:
+        raise ValueError("weight codes must be uint8 and scales float16")
+    m, d = x.shape
+    k, half_d = w_codes.shape
+    if half_d * 2 != d or w_scales.numel() != k:
+        raise ValueError("weight codes do not match x")
+    s = _signs(signs, d, x.device)
+    y = _out("out", out, (m, k), torch.float16, x.device)
+    st = load_library().rq_linear_decode_w4a8(_ptr(x), m, d, _ptr(s), _ptr(w_codes),
+                                              _ptr(w_scales), k, _ptr(y), _stream())
+    _check("rq_linear_decode_w4a8", st)
     return y
 
 

@@ -210,6 +210,21 @@ int rq_linear_decode(const uint16_t* x, int64_t m, int64_t d, const int8_t* sign
                                            static_cast<hipStream_t>(stream)));
 }
 
+int rq_linear_decode_w4a8(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                          const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
+                          void* stream) {
+  if (m < 0 || m > 4) return RQ_ERR_SHAPE;
+  if (!is_pow2(d) || d < 512 || d > 8192) return RQ_ERR_SHAPE;
+  if (k < 1 || k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_codes)) return RQ_ERR_ALIGN;
+  if (signs != nullptr && !aligned16(signs)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_linear_decode_w4a8(x, m, d, signs, w_codes, w_scales, k, y,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64_t group,
                                           int64_t seq) {
   if (batch < 1 || kv_heads < 1 || group < 1 || seq < 1) return 0;

@@ -80,4 +80,10 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t m, int64_t d, const i
                                 const uint8_t* w_codes, const uint16_t* w_scales, int64_t k,
                                 uint16_t* y, void* workspace, hipStream_t stream);
 
+// Fused W4A8 decode linear (m <= 4): rotation + per-token INT8 quantisation
+// of x as the prologue of the INT8-activation decode GEMM, one launch.
+hipError_t launch_linear_decode_w4a8(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                                     const uint8_t* w_codes, const uint16_t* w_scales, int64_t k,
+                                     uint16_t* y, hipStream_t stream);
+
 }  // namespace rq

@@ -519,7 +519,8 @@ __device__ __forceinline__ DecEpi dec_load_epi(const DecLane<RG>& t, int64_t m, 
 }
 
 // Partial sums of the 8 waves meet in LDS (wave w's RG x 64 sums start at
-// partial + w * pitch); waves 0..RG-1 finish one 16-row group each.
+// partial + w * pitch); waves 0..RG-1 finish one 16-row group each.  Row r's
+// activation scale is a_scales[r * sa_stride] (or epi's).
 template <int RG, int SHIFT = 8>
 __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* partial, int pitch,
                                                  const v4i (&acc0)[RG], const v4i (&acc1)[RG],
@@ -530,7 +531,8 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
                                                  int32_t* __restrict__ acc_out,
                                                  const uint8_t* __restrict__ a_zeros = nullptr,
                                                  const int32_t* __restrict__ w_sums = nullptr,
-                                                 const DecEpi* epi = nullptr) {
+                                                 const DecEpi* epi = nullptr,
+                                                 int64_t sa_stride = 1) {
 #pragma unroll
   for (int q = 0; q < RG; ++q) partial[t.wave * pitch + q * 64 + t.lane] = acc0[q] + acc1[q];
   __syncthreads();
@@ -546,7 +548,7 @@ __device__ __forceinline__ void dec_reduce_store(const DecLane<RG>& t, v4i* part
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 4 * t.g + e;
         if (row < m) {
-          const float sa = epi != nullptr ? epi->sa[e] : h2f(a_scales[row]);
+          const float sa = epi != nullptr ? epi->sa[e] : h2f(a_scales[row * sa_stride]);
           const int32_t z = epi != nullptr ? epi->za[e] : (a_zeros != nullptr ? (int32_t)a_zeros[row] : 0);
           epilogue_store<SHIFT>(s[e], sa, sw, row * k + col, y, acc_out, z * ws);
         }
@@ -755,18 +757,36 @@ constexpr int LD_FUSED_M = 4;
 // operands as in the one-wavefront rotation, up to the exact sign sigma,
 // and fma(u sigma, c / s, M) = fma(u, (c / s) sigma, M): codes and scales are
 // bit-identical to it.  MW = 0: one wavefront per token (row_rotate_quant).
-template <int N, bool HAS_SIGNS, int RG, int MW = 0>
+//
+// BITS = 8: the W4A8 linear (rq_fwht_quant8's per-token INT8 quantiser,
+// codes [token][n] bytes in LDS, then the INT8-activation MFMA path of the
+// decode GEMM with its epilogue); y is bit-identical to rq_fwht_quant8
+// followed by rq_w4a8_gemm.
+template <int N, bool HAS_SIGNS, int RG, int MW = 0, int BITS = 4>
 __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
     const __half* __restrict__ x, int64_t m, const int8_t* __restrict__ signs, float c32,
     const uint8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int64_t k,
     uint16_t* __restrict__ y) {
+  static_assert(BITS == 4 || BITS == 8, "INT4 or INT8 activation codes");
+  constexpr int AM = BITS == 8 ? kA8 : kA4;
+  constexpr int AW = BITS == 8 ? 2 : 1;  // activation code bytes per weight code byte
   // wl also takes the partial sums: each wave's RG x 64 sums go into the
   // staging segments that only that wave reads, once its MFMAs are done
   __shared__ __align__(16) unsigned char wl[DCHUNK * 16 * RG * DSEG];
-  __shared__ __align__(16) unsigned char acodes[LD_FUSED_M][N / 2];
-  __shared__ uint16_t ascales[LD_FUSED_M];
+  __shared__ __align__(16) unsigned char acodes[LD_FUSED_M][AW * N / 2];
   constexpr int kWavePitch = 2 * 16 * RG * DSEG / (int)sizeof(v4i);  // v4i per wave's two segments
-  static_assert(kWavePitch >= RG * 64, "the partial sums fit in a wave's own segments");
+  static_assert(kWavePitch >= RG * 64 + 1, "the partial sums and a scale fit in a wave's segments");
+  // A token's fp16 scale stays in a register of the wavefront that finished
+  // its quantisation (lane 0) until that wavefront's MFMAs are done; it then
+  // goes into the wavefront's own staging segments, after its partial sums,
+  // and the epilogue reads it there after the reduction's barrier.  (A
+  // separate LDS array would take the kernel 8 bytes past 80 KB at n = 4096
+  // with INT8 codes and two 16-row groups, and two workgroups would no
+  // longer fit on a CU.)
+  constexpr int kScaleStride = (MW > 0 ? MW : 1) * kWavePitch * (int)(sizeof(v4i) / 2);
+  uint16_t* const scale_lds = reinterpret_cast<uint16_t*>(wl + RG * 64 * sizeof(v4i));
+  bool scale_writer = false;  // uniform per wavefront
+  uint16_t my_scale = 0;      // lane 0 of a writer
   constexpr int64_t rowb = N / 2;
   const DecLane<RG> t = dec_lane<RG>(w_codes, k, rowb, wl);
 
@@ -852,10 +872,14 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
       float tmax = 0.0f;
 #pragma unroll
       for (int w = 0; w < MW; ++w) tmax = fmaxf(tmax, wmax[MW * tok + w]);
-      const uint16_t hb = scale_fp16<7>(tmax * c32);
+      constexpr float kM = BITS == 4 ? kMagic : kMagic8;
+      constexpr float kMLo = BITS == 4 ? kMagicLo : kMagic8Lo;
+      constexpr float kMHi = BITS == 4 ? kMagicHi : kMagic8Hi;
+      const uint16_t hb = scale_fp16<BITS == 4 ? 7 : 127>(tmax * c32);
       const bool subnormal = hb != 0 && hb < 0x0400u;
       const float mult = hb == 0 ? 0.0f : c32 / h2f(hb);
-      if (th == 0) ascales[tok] = hb;
+      scale_writer = part == 0;
+      my_scale = hb;
 #pragma unroll
       for (int gi = 0; gi < PGT; ++gi) {
         const int G = th + TT * gi;
@@ -863,15 +887,22 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
         const int a = G % 256, lc = G / 256;
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
-          float t0 = __builtin_fmaf(v[gi][0][j], mult, kMagic);
-          float t1 = __builtin_fmaf(v[gi][1][j], mult, kMagic);
+          float t0 = __builtin_fmaf(v[gi][0][j], mult, kM);
+          float t1 = __builtin_fmaf(v[gi][1][j], mult, kM);
           if (subnormal) {  // uniform: the scale is shared by the whole row
-            t0 = fminf(fmaxf(t0, kMagicLo), kMagicHi);
-            t1 = fminf(fmaxf(t1, kMagicLo), kMagicHi);
+            t0 = fminf(fmaxf(t0, kMLo), kMHi);
+            t1 = fminf(fmaxf(t1, kMLo), kMHi);
           }
-          // (q1 + 8) << 4 | (q0 + 8), flipped to two's complement nibbles
-          acodes[tok][256 * (lc + CPW * j) + a] =
-              (unsigned char)(((f2u(t1) << 4) | (f2u(t0) & 0xFu)) ^ 0x88u);
+          if constexpr (BITS == 4) {
+            // (q1 + 8) << 4 | (q0 + 8), flipped to two's complement nibbles
+            acodes[tok][256 * (lc + CPW * j) + a] =
+                (unsigned char)(((f2u(t1) << 4) | (f2u(t0) & 0xFu)) ^ 0x88u);
+          } else {
+            // bytes q0 + 128, q1 + 128 of elements 2a, 2a + 1, flipped to
+            // two's complement
+            *reinterpret_cast<uint16_t*>(&acodes[tok][512 * (lc + CPW * j) + 2 * a]) =
+                (uint16_t)(((f2u(t0) & 0xFFu) | ((f2u(t1) & 0xFFu) << 8)) ^ 0x8080u);
+          }
         }
       }
     }
@@ -881,25 +912,29 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
     uint4 raw[N / 512];
     load_row(raw, x + (int64_t)t.wave * N, t.lane);
     dec_issue_w(t, 0);
-    row_rotate_quant<N, HAS_SIGNS, true>(raw, sg, t.lane, make_row_lane(t.lane), c32,
-                                         acodes[t.wave], nullptr, ascales + t.wave, nullptr);
+    row_rotate_quant<N, HAS_SIGNS, true, BITS>(raw, sg, t.lane, make_row_lane(t.lane), c32,
+                                               acodes[t.wave], nullptr, &my_scale, nullptr);
+    scale_writer = true;
   } else {
     dec_issue_w(t, 0);
   }
   __syncthreads();
 
   const bool a_ok = t.r16 < m;
-  const unsigned char* a_src = acodes[a_ok ? t.r16 : 0] + 16 * t.g;
+  const unsigned char* a_src = acodes[a_ok ? t.r16 : 0] + 16 * AW * t.g;
   v4i acc0[RG], acc1[RG];
 #pragma unroll
   for (int q = 0; q < RG; ++q) acc0[q] = acc1[q] = v4i{0, 0, 0, 0};
-  dec_mma_chunk(t, wl, a_src, a_ok, 0, acc0, acc1);
+  dec_mma_chunk<RG, AM>(t, wl, a_src, a_ok, 0, acc0, acc1);
   for (int64_t c0 = DCHUNK; c0 < t.nseg; c0 += DCHUNK) {
     dec_issue_w(t, c0);
-    dec_mma_chunk(t, wl, a_src, a_ok, c0, acc0, acc1);
+    dec_mma_chunk<RG, AM>(t, wl, a_src, a_ok, c0, acc0, acc1);
   }
-  dec_reduce_store(t, reinterpret_cast<v4i*>(wl), kWavePitch, acc0, acc1, m, k, ascales,
-                   w_scales, y, nullptr);
+  // (this wavefront's LDS reads are back: its segments are free)
+  if (scale_writer && t.lane == 0) scale_lds[(int64_t)t.wave * kWavePitch * (sizeof(v4i) / 2)] = my_scale;
+  dec_reduce_store<RG, BITS == 4 ? 8 : 4>(t, reinterpret_cast<v4i*>(wl), kWavePitch, acc0, acc1,
+                                          m, k, scale_lds, w_scales, y, nullptr, nullptr, nullptr,
+                                          nullptr, kScaleStride);
 }
 #undef RQ_DMA_NT
 
@@ -1522,19 +1557,19 @@ size_t linear_decode_workspace_bytes(int64_t m, int64_t d) {
 }
 
 namespace {
-template <int N, bool HAS_SIGNS, int RG, int MW = 0>
+template <int N, bool HAS_SIGNS, int RG, int MW, int BITS>
 hipError_t launch_ld(const uint16_t* x, int64_t m, const int8_t* signs, const uint8_t* w_codes,
                      const uint16_t* w_scales, int64_t k, uint16_t* y, hipStream_t stream) {
   const float c32 = (float)(1.0 / __builtin_sqrt((double)N));
   const int64_t grid = (k + 16 * RG - 1) / (16 * RG);
   if (MW > 0 && m > DEC_WAVES / (MW > 0 ? MW : 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((w4a4_linear_decode_kernel<N, HAS_SIGNS, RG, MW>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((w4a4_linear_decode_kernel<N, HAS_SIGNS, RG, MW, BITS>), dim3((unsigned)grid),
                      dim3(64 * DEC_WAVES), 0, stream, reinterpret_cast<const __half*>(x), m, signs,
                      c32, w_codes, w_scales, k, y);
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, int BITS>
 hipError_t launch_ld_n(const uint16_t* x, int64_t m, const int8_t* signs, const uint8_t* w_codes,
                        const uint16_t* w_scales, int64_t k, uint16_t* y, hipStream_t stream) {
   // Two 16-row weight groups per workgroup when that still gives every CU a
@@ -1547,21 +1582,35 @@ hipError_t launch_ld_n(const uint16_t* x, int64_t m, const int8_t* signs, const 
   // one (the exchange and the finishing work outweigh the halved butterflies
   // once two such wavefronts share a SIMD).  The fp32 rows this takes (16 KB
   // a token) fit beside one 16-row weight group.
+  const bool sg = signs != nullptr;
   if constexpr (N == 4096) {
     if (!rg2 && m <= 2 && (k + 15) / 16 <= (int64_t)cu_count()) {
-      const bool sg = signs != nullptr;
       if (m == 1)
-        return sg ? launch_ld<N, true, 1, 8>(x, m, signs, w_codes, w_scales, k, y, stream)
-                  : launch_ld<N, false, 1, 8>(x, m, signs, w_codes, w_scales, k, y, stream);
-      return sg ? launch_ld<N, true, 1, 4>(x, m, signs, w_codes, w_scales, k, y, stream)
-                : launch_ld<N, false, 1, 4>(x, m, signs, w_codes, w_scales, k, y, stream);
+        return sg ? launch_ld<N, true, 1, 8, BITS>(x, m, signs, w_codes, w_scales, k, y, stream)
+                  : launch_ld<N, false, 1, 8, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+      return sg ? launch_ld<N, true, 1, 4, BITS>(x, m, signs, w_codes, w_scales, k, y, stream)
+                : launch_ld<N, false, 1, 4, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
     }
   }
-  if (signs != nullptr)
-    return rg2 ? launch_ld<N, true, 2>(x, m, signs, w_codes, w_scales, k, y, stream)
-               : launch_ld<N, true, 1>(x, m, signs, w_codes, w_scales, k, y, stream);
-  return rg2 ? launch_ld<N, false, 2>(x, m, signs, w_codes, w_scales, k, y, stream)
-             : launch_ld<N, false, 1>(x, m, signs, w_codes, w_scales, k, y, stream);
+  if (sg)
+    return rg2 ? launch_ld<N, true, 2, 0, BITS>(x, m, signs, w_codes, w_scales, k, y, stream)
+               : launch_ld<N, true, 1, 0, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+  return rg2 ? launch_ld<N, false, 2, 0, BITS>(x, m, signs, w_codes, w_scales, k, y, stream)
+             : launch_ld<N, false, 1, 0, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+}
+
+template <int BITS>
+hipError_t launch_ld_d(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                       const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, uint16_t* y,
+                       hipStream_t stream) {
+  switch (d) {
+    case 512: return launch_ld_n<512, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 1024: return launch_ld_n<1024, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 2048: return launch_ld_n<2048, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 4096: return launch_ld_n<4096, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+    case 8192: return launch_ld_n<8192, BITS>(x, m, signs, w_codes, w_scales, k, y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 }  // namespace
 
@@ -1578,14 +1627,14 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t m, int64_t d, const i
     if (e != hipSuccess) return e;
     return launch_w4a4_gemm(codes, scales, m, w_codes, w_scales, k, d, y, nullptr, stream);
   }
-  switch (d) {
-    case 512: return launch_ld_n<512>(x, m, signs, w_codes, w_scales, k, y, stream);
-    case 1024: return launch_ld_n<1024>(x, m, signs, w_codes, w_scales, k, y, stream);
-    case 2048: return launch_ld_n<2048>(x, m, signs, w_codes, w_scales, k, y, stream);
-    case 4096: return launch_ld_n<4096>(x, m, signs, w_codes, w_scales, k, y, stream);
-    case 8192: return launch_ld_n<8192>(x, m, signs, w_codes, w_scales, k, y, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_ld_d<4>(x, m, d, signs, w_codes, w_scales, k, y, stream);
+}
+
+hipError_t launch_linear_decode_w4a8(const uint16_t* x, int64_t m, int64_t d, const int8_t* signs,
+                                     const uint8_t* w_codes, const uint16_t* w_scales, int64_t k,
+                                     uint16_t* y, hipStream_t stream) {
+  if (m > LD_FUSED_M) return hipErrorInvalidValue;
+  return launch_ld_d<8>(x, m, d, signs, w_codes, w_scales, k, y, stream);
 }
 
 }  // namespace rq

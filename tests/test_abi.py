@@ -197,6 +197,26 @@ def test_linear_decode_argument_errors(lib):
     assert call(ws=MIS) == binding.RQ_ERR_ALIGN
 
 
+def test_linear_decode_w4a8_argument_errors(lib):
+    def call(x=A16, m=4, d=4096, signs=None, w=A16, sw=A16b, k=64, y=A16b):
+        return lib.rq_linear_decode_w4a8(x, m, d, signs, w, sw, k, y, None)
+
+    assert call(m=0) == binding.RQ_OK
+    assert call(m=5) == binding.RQ_ERR_SHAPE  # one launch holds at most 4 tokens
+    assert call(m=-1) == binding.RQ_ERR_SHAPE
+    assert call(d=256) == binding.RQ_ERR_SHAPE
+    assert call(d=3072) == binding.RQ_ERR_SHAPE
+    assert call(d=16384) == binding.RQ_ERR_SHAPE
+    assert call(k=0) == binding.RQ_ERR_SHAPE
+    assert call(x=None) == binding.RQ_ERR_NULL
+    assert call(w=None) == binding.RQ_ERR_NULL
+    assert call(sw=None) == binding.RQ_ERR_NULL
+    assert call(y=None) == binding.RQ_ERR_NULL
+    assert call(x=MIS) == binding.RQ_ERR_ALIGN
+    assert call(w=MIS) == binding.RQ_ERR_ALIGN
+    assert call(signs=MIS) == binding.RQ_ERR_ALIGN
+
+
 def test_asym_argument_errors(lib):
     f = lib.rq_fwht_quant_asym
 

@@ -183,6 +183,96 @@ def test_w4a8_decode_linear_end_to_end(rq):
                        what=f"w4a8 decode m={m} k={k}", a8=True)
 
 
+# the fused W4A8 decode linear (rq_linear_decode_w4a8): every n class, one
+# workgroup (k = 5), one and two 16-row weight groups per workgroup (k = 12300
+# and 14336 give two), no signs, and n = 4096 with one 16-row group per
+# workgroup, where 8 or 4 wavefronts rotate each token (m = 1, 2; one
+# wavefront for m = 3, 4)
+LD8_SHAPES = [(4, 5, 512, True), (3, 40, 8192, True), (2, 300, 1024, False),
+              (1, 12300, 2048, True), (4, 14336, 4096, True), (1, 5, 4096, True),
+              (2, 300, 4096, False), (3, 40, 4096, True), (4, 1000, 4096, False),
+              (1, 1000, 8192, False), (2, 4096, 4096, True)]
+
+
+@pytest.mark.parametrize("m,k,d,with_signs", LD8_SHAPES)
+def test_linear_decode_w4a8_shapes(rq, m, k, d, with_signs):
+    """y of the one-launch W4A8 linear is the two-launch path's
+    (rq_fwht_quant8 then rq_w4a8_gemm) bit for bit, into guarded outputs with
+    both sentinels; the two-launch pieces against the oracle: INT8 codes up to
+    the rounding band, accumulators exact, y within 1e-2 of the oracle's
+    epilogue on those codes."""
+    rng = np.random.default_rng(m * 11 + k + d)
+    x = (rng.standard_normal((m, d)) * np.where(rng.random(d) < 0.01, 50.0, 1.0)).astype(np.float16)
+    wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
+    signs = datagen.rademacher(rng, d) if with_signs else None
+    sd = dev(signs) if with_signs else None
+    say(f"fused w4a8 decode linear m={m} k={k} d={d} signs={with_signs}")
+    wc, wsc, _ = rq.fold_weights(dev(wt), sd)
+    ys = []
+    for sentinel in SENTINELS:
+        yo = Out((m, k), torch.float16, sentinel)
+        rq.linear_decode_w4a8(dev(x), sd, wc, wsc, out=yo.t)
+        check_all([yo], "fused w4a8 decode")
+        ys.append(yo.host())
+    assert np.array_equal(ys[0].view(np.uint16), ys[1].view(np.uint16))
+    a8, sa, xr = rq.fwht_quant8(dev(x), sd, debug=True)
+    y2, acc2 = rq.w4a8_gemm(a8, sa, wc, wsc, debug=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ys[0].view(np.uint16), host(y2).view(np.uint16))
+    check_rotation_result(x, signs, host(a8), host(sa), host(xr), what="fused w4a8 activations",
+                          bits=8)
+    check_gemm(host(a8), host(sa), host(wc), host(wsc), ys[0], host(acc2),
+               what=f"fused w4a8 {m}x{k}x{d}", a8=True)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_linear_decode_w4a8_special_tokens(rq, m):
+    """Tokens whose INT8 scale is zero or fp16-subnormal (the code clamp), a
+    token of +-65504 (every code +-127 at the largest rotated value) and an
+    ordinary one, at n = 4096 where several wavefronts rotate a token (m = 1,
+    2) or one does (m = 4): y is the two-launch path's, bit for bit."""
+    rng = np.random.default_rng(900 + m)
+    d, k = 4096, 64
+    signs = datagen.rademacher(rng, d)
+    sd = dev(signs)
+    rows = [np.zeros(d), rng.standard_normal(d) * 1e-4, 65504.0 * signs.astype(np.float64),
+            rng.standard_normal(d) * np.where(rng.random(d) < 0.01, 50.0, 1.0)]
+    x = np.stack(rows[1:2] if m == 1 else rows[:m]).astype(np.float16)
+    wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
+    say(f"fused w4a8 decode linear special tokens m={m}")
+    wc, wsc, _ = rq.fold_weights(dev(wt), sd)
+    yo = Out((m, k), torch.float16)
+    rq.linear_decode_w4a8(dev(x), sd, wc, wsc, out=yo.t)
+    check_all([yo], "fused w4a8 special")
+    a8, sa, xr = rq.fwht_quant8(dev(x), sd, debug=True)
+    y2 = rq.w4a8_gemm(a8, sa, wc, wsc)[0]
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(yo.host().view(np.uint16), host(y2).view(np.uint16))
+    check_rotation_result(x, signs, host(a8), host(sa), host(xr), what="w4a8 special", bits=8)
+    sa = host(sa).view(np.uint16)
+    if m == 1:
+        assert 0 < sa[0] < 0x0400
+    if m == 4:
+        assert sa[0] == 0 and 0 < sa[1] < 0x0400 and sa[2] < 0x7C00
+
+
+def test_linear_decode_w4a8_workload(rq):
+    """The decode-linear workload (4096 -> 4096 and 4096 -> 14336, m = 1, 2,
+    4): the one-launch W4A8 linear against the two-launch path, twice."""
+    dec = datagen.decode_linear(0)
+    s = dev(dec["signs"])
+    for k, wt in dec["wts"].items():
+        wc, wsc, _ = rq.fold_weights(dev(wt), s)
+        for m in (1, 2, 4):
+            say(f"fused w4a8 decode workload m={m} k={k}")
+            x = dev(dec["x"][:m])
+            for rep in range(2):
+                y = rq.linear_decode_w4a8(x, s, wc, wsc)
+                y_ref = rq.w4a8_linear(x, s, wc, wsc)
+                torch.cuda.synchronize()
+                assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (m, k, rep)
+
+
 def test_w4a8_linear_beats_w4a4_error(rq):
     """INT8 activations cut the linear's error against the float product (the
     reason for the variant): on the decode workload the W4A8 output is closer
