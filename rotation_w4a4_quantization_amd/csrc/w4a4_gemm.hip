@@ -963,10 +963,11 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_linear_decode_kernel(
 // A and B use the same assignment, so every code meets its partner exactly
 // once.  For 2048 x 28672 the tile gives exactly 1024 tiles, four per CU.
 constexpr int LM = 256, LN = 224, LK = 256;  // block tile (codes)
+constexpr int LN_WIDE = 256;                  // the wider tile (see wide_tiles)
 constexpr int LPK = LK / 2;                   // packed bytes per row per step
-constexpr int LBUF = (LM + LN) * LPK;         // one LDS buffer: 60 KB
 constexpr int LTHREADS = 512;
-static_assert(LN % 32 == 0 && LM == 32 * (LTHREADS / 64), "one 32-row DMA slice per wave");
+static_assert(LN % 32 == 0 && LN_WIDE % 32 == 0 && LN_WIDE <= LM, "32-row B DMA slices, one per wave");
+static_assert(LM == 32 * (LTHREADS / 64), "one 32-row A DMA slice per wave");
 
 __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); }
 
@@ -990,7 +991,7 @@ __device__ __forceinline__ int part_pos(int row, int p) { return p ^ (row & 7); 
 // group scales of its B rows (4 bytes a row, dword DMA by waves 0..3); per
 // half step every (i, j) tile's int32 sum over the group is two MFMAs from
 // zero, and it turns into fp32 with its column's group scale.
-template <int AM = kA4, bool GROUPED = false, bool GACC = false>
+template <int AM = kA4, bool GROUPED = false, bool GACC = false, int TN = LN>
 __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __restrict__ a_codes,
                                                               const uint16_t* __restrict__ a_scales,
                                                               const uint8_t* __restrict__ w_codes,
@@ -1009,17 +1010,22 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   constexpr int KSTEP = A8 ? LK / 2 : LK;       // codes per step
   constexpr int APK = A8 ? KSTEP : KSTEP / 2;   // A bytes per row per step (128)
   constexpr int BPK = KSTEP / 2;                // B bytes per row per step
-  constexpr int BUF = LM * APK + LN * BPK;      // codes of one step
+  constexpr int JT = TN / 32;                   // 16-column MFMA tiles per wave
+  constexpr int WNC = TN / 2;                   // columns per wave
+  constexpr int BUF = LM * APK + TN * BPK;      // codes of one step
   constexpr int BUFS = BUF + (GROUPED ? 4 * 256 : 0);  // + group scales: one buffer
-  constexpr int OP = 464;                       // LDS row pitch of the output tile (bytes)
-  constexpr int HR = LM / 2;                    // output rows staged at a time
+  constexpr int OP = 2 * TN + 16;               // LDS row pitch of the output tile (bytes)
+  // output rows go through LDS in NH passes of HR rows (GPP 16-row groups of
+  // every wave per pass): two passes when half the tile fits, else four
+  constexpr int NH = (A8 ? 2 * BUF + (LM / 2) * OP <= 160 * 1024 : (LM / 2) * OP <= BUF) ? 2 : 4;
+  constexpr int HR = LM / NH, GPP = 4 / NH;
   constexpr int STAGE = A8 ? 2 * BUF : 0;       // A8: the staging region after both buffers
   static_assert(APK == LPK, "A rows are 128 bytes per step");
   static_assert(A8 ? 2 * BUF + HR * OP <= 160 * 1024 : HR * OP <= BUF, "the output staging fits");
   __shared__ __align__(16) unsigned char lds[A8 ? 2 * BUF + HR * OP : 2 * BUFS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x 112
+  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves of 64 x TN / 2
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t rowa = A8 ? d : d / 2, rowb = d / 2;
   const int steps = (int)(d / KSTEP);
@@ -1038,7 +1044,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
 #define RQ_TILE(R) (by_xcd ? xcd_base + b / 8 + xcd_stride * (R) : b + nb * (R))
   if (!RQ_TILE_OK(0)) return;  // uniform per workgroup
   int64_t m0 = (int64_t)(RQ_TILE(0) % tiles_m) * LM;
-  int64_t n0 = (int64_t)(RQ_TILE(0) / tiles_m) * LN;
+  int64_t n0 = (int64_t)(RQ_TILE(0) / tiles_m) * TN;
 
   // DMA rows of this lane: row 32 wave + 8 t + lane / 8 (t = 0..3) of the A
   // tile and (waves 0..6) of the B tile, 16-byte part drp of it; rows past the
@@ -1078,7 +1084,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
     const int64_t ka_ = (int64_t)(S) * APK, kb_ = (int64_t)(S) * BPK;               \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                   \
       RQ_DMA(buf_ + (uint32_t)((32 * wave + 8 * t) * APK), (A_)[t] + ka_);          \
-    if (wave < LN / 32) {                                                           \
+    if (wave < TN / 32) {                                                           \
       _Pragma("unroll") for (int t = 0; t < NBT; ++t)                               \
         RQ_DMA(buf_ + (uint32_t)(LM * APK + (32 * wave + (A8 ? 16 : 8) * t) * BPK), \
                (B_)[t] + kb_);                                                      \
@@ -1101,45 +1107,56 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
   for (int r = 0;; ++r) {
     const bool has_next = RQ_TILE_OK(r + 1);
     const int tn = has_next ? RQ_TILE(r + 1) : 0;
-    const int64_t m0n = (int64_t)(tn % tiles_m) * LM, n0n = (int64_t)(tn / tiles_m) * LN;
+    const int64_t m0n = (int64_t)(tn % tiles_m) * LM, n0n = (int64_t)(tn / tiles_m) * TN;
 
-    v4i acc[4][7];
-    v4f facc[4][7];  // GROUPED: 256 * sum over groups of the group scale times its int32 sum
+    v4i acc[4][JT];
+    v4f facc[4][JT];  // GROUPED: 256 * sum over groups of the group scale times its int32 sum
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 7; ++j) {
+      for (int j = 0; j < JT; ++j) {
         acc[i][j] = v4i{0, 0, 0, 0};
         facc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       }
 
     for (int s = 0; s < steps; ++s) {
-      if (s + 1 < steps) {
-        RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, gsrc, s + 1);
-      } else if (has_next) {
-        const uint8_t* an[4];
-        const uint8_t* bn[NBT];
+      // The next step's loads go out at the start of the step's second half:
+      // issued together with the first half's fragment reads, their LDS
+      // writes slowed those reads (measured 2-4% on the 2048 x 8192 -> 28672
+      // prefill).  They still have half a step to land.  A8 (one half per
+      // step) and GROUPED (where the later issue costs registers it does not
+      // have: 244 bytes of spills) issue them at the start of the step.
+      constexpr bool kLateIssue = !A8 && !GROUPED;
+      auto issue_next = [&]() {
+        if (s + 1 < steps) {
+          RQ_ISSUE_FROM(par ^ 1, asrc, bsrc, gsrc, s + 1);
+        } else if (has_next) {
+          const uint8_t* an[4];
+          const uint8_t* bn[NBT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int64_t ar = m0n + dr0 + 8 * t;
-          an[t] = a_codes + (ar < m ? ar : m - 1) * rowa + drp;
-        }
+          for (int t = 0; t < 4; ++t) {
+            const int64_t ar = m0n + dr0 + 8 * t;
+            an[t] = a_codes + (ar < m ? ar : m - 1) * rowa + drp;
+          }
 #pragma unroll
-        for (int t = 0; t < NBT; ++t) {
-          const int64_t br = n0n + db0 + (A8 ? 16 : 8) * t;
-          bn[t] = w_codes + (br < k ? br : k - 1) * rowb + dbp;
+          for (int t = 0; t < NBT; ++t) {
+            const int64_t br = n0n + db0 + (A8 ? 16 : 8) * t;
+            bn[t] = w_codes + (br < k ? br : k - 1) * rowb + dbp;
+          }
+          RQ_ISSUE_FROM(par ^ 1, an, bn, RQ_GSRC(n0n), 0);
         }
-        RQ_ISSUE_FROM(par ^ 1, an, bn, RQ_GSRC(n0n), 0);
-      }
+      };
+      if constexpr (!kLateIssue) issue_next();
       const unsigned char* cur = lds + par * BUFS;
-      uint32_t sgw[7];  // GROUPED: the step's two group scales of column j
+      uint32_t sgw[JT];  // GROUPED: the step's two group scales of column j
       if constexpr (GROUPED) {
 #pragma unroll
-        for (int j = 0; j < 7; ++j)
-          sgw[j] = *reinterpret_cast<const uint32_t*>(cur + BUF + 4 * (wn * 112 + j * 16 + r16));
+        for (int j = 0; j < JT; ++j)
+          sgw[j] = *reinterpret_cast<const uint32_t*>(cur + BUF + 4 * (wn * WNC + j * 16 + r16));
       }
 #pragma unroll
       for (int u = 0; u < (A8 ? 1 : 2); ++u) {
+        if (kLateIssue && u == 1) issue_next();
         const int fo = u ? frag_off1 : frag_off0;
         v4i af[2][4];
 #pragma unroll
@@ -1160,8 +1177,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           }
         }
 #pragma unroll
-        for (int j = 0; j < 7; ++j) {
-          const uint4 q = *reinterpret_cast<const uint4*>(cur + LM * APK + (wn * 112 + j * 16) * BPK +
+        for (int j = 0; j < JT; ++j) {
+          const uint4 q = *reinterpret_cast<const uint4*>(cur + LM * APK + (wn * WNC + j * 16) * BPK +
                                                           (A8 ? frag_b8 : fo));
           const v4i b0 = widen(q.x, q.y), b1 = widen(q.z, q.w);
           if constexpr (GROUPED) {
@@ -1174,7 +1191,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
             for (int i = 0; i < 4; ++i)
               t[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], b1, t[i], 0, 0, 0);
             if constexpr (GACC) {  // debug: the exact int32 sum of group 2 s + u
-              const int64_t col = n0 + wn * 112 + j * 16 + r16;
+              const int64_t col = n0 + wn * WNC + j * 16 + r16;
               const int64_t ng = d / WG, grp = 2 * (int64_t)s + u;
 #pragma unroll
               for (int i = 0; i < 4; ++i)
@@ -1234,52 +1251,54 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
         zv[i][e] = AM == kAU4 ? (int32_t)a_zeros[arowc] : 0;
       }
     }
-    float swv[7];
-    int32_t wsv[7];  // weight code sums (asymmetric activations only)
+    float swv[JT];
+    int32_t wsv[JT];  // weight code sums (asymmetric activations only)
 #pragma unroll
-    for (int j = 0; j < 7; ++j) {
-      const int64_t col = n0 + wn * 112 + j * 16 + r16;
+    for (int j = 0; j < JT; ++j) {
+      const int64_t col = n0 + wn * WNC + j * 16 + r16;
       const int64_t colc = col < k ? col : k - 1;
       const float sw = GROUPED ? 0.0f : h2f(w_scales[colc]);
       const int32_t ws = AM == kAU4 ? w_sums[colc] : 0;
       swv[j] = col < k ? sw : 0.0f;
       wsv[j] = col < k ? ws : 0;
     }
-    const bool full = m0 + LM <= m && n0 + LN <= k;
+    const bool full = m0 + LM <= m && n0 + TN <= k;
     if (full && wide_store) {
       // The fp16 tile goes through the free buffer (A8: its own region) in
-      // two halves of 128 rows (464-byte rows) and leaves as coalesced 16-byte
-      // stores.  Half h holds row groups 2h and 2h + 1 of every wave: staging
-      // row tr is tile row (tr / 32) * 64 + 32 h + tr % 32.
+      // NH passes of HR rows (OP-byte rows) and leaves as coalesced 16-byte
+      // stores.  Pass h holds row groups GPP h .. GPP h + GPP - 1 of every
+      // wave: staging row tr is tile row (tr / (16 GPP)) * 64 + 16 GPP h +
+      // tr % (16 GPP).
       unsigned char* stg = lds + (A8 ? STAGE : (par ^ 1) * BUFS);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < NH; ++h) {
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const int i = 2 * h + i2;
+        for (int i2 = 0; i2 < GPP; ++i2) {
+          const int i = GPP * h + i2;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int tr = wm * 32 + i2 * 16 + 4 * g + e;
+            const int tr = wm * 16 * GPP + i2 * 16 + 4 * g + e;
             const float sa = sav[i][e];
             const int32_t z = zv[i][e];
 #pragma unroll
-            for (int j = 0; j < 7; ++j) {
+            for (int j = 0; j < JT; ++j) {
               // exact: the MFMA sum is 2^SHIFT * sum qa qw
               const int32_t a = (acc[i][j][e] >> SHIFT) - z * wsv[j];
-              *reinterpret_cast<uint16_t*>(stg + tr * OP + 2 * (wn * 112 + j * 16 + r16)) =
+              *reinterpret_cast<uint16_t*>(stg + tr * OP + 2 * (wn * WNC + j * 16 + r16)) =
                   GROUPED ? f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa)
                           : f2h_rn(((float)a * sa) * swv[j]);
             }
           }
         }
         __syncthreads();
-        constexpr int CPR = LN * 2 / 16;  // 16-byte chunks per output row: 28
+        constexpr int CPR = TN * 2 / 16;  // 16-byte chunks per output row
+        static_assert(HR * CPR % LTHREADS == 0, "whole store rounds");
 #pragma unroll
         for (int q = 0; q < HR * CPR / LTHREADS; ++q) {
           const int c = tid_o + LTHREADS * q;
           const int tr = c / CPR, ch = c % CPR;
           const v4u_g v = *reinterpret_cast<const v4u_g*>(stg + tr * OP + 16 * ch);
-          const int row = (tr >> 5) * 64 + 32 * h + (tr & 31);
+          const int row = (tr / (16 * GPP)) * 64 + 16 * GPP * h + tr % (16 * GPP);
           __builtin_nontemporal_store(v, reinterpret_cast<v4u_g*>(y + (m0 + row) * k + n0 + 8 * ch));
         }
         __syncthreads();
@@ -1293,10 +1312,10 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           if (!full && row >= m) continue;
           const float sa = sav[i][e];
           const int32_t z = zv[i][e];
-          const int64_t base = row * k + n0 + wn * 112 + r16;
+          const int64_t base = row * k + n0 + wn * WNC + r16;
 #pragma unroll
-          for (int j = 0; j < 7; ++j) {
-            if (full || n0 + wn * 112 + j * 16 + r16 < k) {
+          for (int j = 0; j < JT; ++j) {
+            if (full || n0 + wn * WNC + j * 16 + r16 < k) {
               if constexpr (GROUPED)
                 y[base + j * 16] = f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa);
               else
@@ -1422,21 +1441,47 @@ hipError_t launch_weight_code_sums(const uint8_t* w_codes, int64_t k, int64_t d,
 // Shapes the persistent prefill kernel takes (d: whole 256-code steps).
 bool large_shape(int64_t m, int64_t k, int64_t d) { return m >= 128 && k >= 224 && d % LK == 0; }
 
+template <int AM, bool GROUPED, bool GACC, int TN>
+hipError_t launch_large_tn(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
+                           int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
+                           const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
+                           hipStream_t stream) {
+  const int tiles_m = (int)((m + LM - 1) / LM);
+  const int64_t tiles = (int64_t)tiles_m * ((k + TN - 1) / TN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
+  // 16-byte output stores need 16-byte aligned rows and no int32 output
+  const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
+  hipLaunchKernelGGL((w4a4_large_kernel<AM, GROUPED, GACC, TN>), dim3((unsigned)grid),
+                     dim3(LTHREADS), 0, stream, a_codes, a_scales, w_codes, w_scales, m, k, d,
+                     tiles_m, (int)tiles, wide_store, y, acc, a_zeros, w_sums);
+  return hipGetLastError();
+}
+
+// Tile width: 224 columns, or 256 where that takes fewer tile rounds on the
+// CUs for the same work (rounds x width): k = 8192 gives 296 tiles of 224,
+// two rounds, but 256 tiles of 256, one round; k = 28672 gives exactly four
+// rounds of 224.  The 256-wide tile holds 128 int32 accumulators per lane;
+// the W4A8 and per-group instantiations have no registers left for it.
+bool wide_tiles(int64_t m, int64_t k) {
+  const int64_t tiles_m = (m + LM - 1) / LM, cus = cu_count();
+  const int64_t r224 = (tiles_m * ((k + LN - 1) / LN) + cus - 1) / cus;
+  const int64_t r256 = (tiles_m * ((k + LN_WIDE - 1) / LN_WIDE) + cus - 1) / cus;
+  return r256 * LN_WIDE < r224 * LN;
+}
+
 template <int AM, bool GROUPED = false, bool GACC = false>
 hipError_t launch_large(const uint8_t* a_codes, const uint16_t* a_scales, const uint8_t* a_zeros,
                         int64_t m, const uint8_t* w_codes, const uint16_t* w_scales,
                         const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
                         hipStream_t stream) {
-  const int tiles_m = (int)((m + LM - 1) / LM);
-  const int64_t tiles = (int64_t)tiles_m * ((k + LN - 1) / LN);
-  if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  const int64_t grid = tiles < cu_count() ? tiles : cu_count();  // one workgroup per CU
-  // 16-byte output stores need 16-byte aligned rows and no int32 output
-  const bool wide_store = acc == nullptr && k % 8 == 0 && ((uintptr_t)y & 15) == 0;
-  hipLaunchKernelGGL((w4a4_large_kernel<AM, GROUPED, GACC>), dim3((unsigned)grid), dim3(LTHREADS), 0, stream,
-                     a_codes, a_scales, w_codes, w_scales, m, k, d, tiles_m, (int)tiles, wide_store,
-                     y, acc, a_zeros, w_sums);
-  return hipGetLastError();
+  if constexpr (AM != kA8 && !GROUPED) {
+    if (wide_tiles(m, k))
+      return launch_large_tn<AM, GROUPED, GACC, LN_WIDE>(a_codes, a_scales, a_zeros, m, w_codes,
+                                                         w_scales, w_sums, k, d, y, acc, stream);
+  }
+  return launch_large_tn<AM, GROUPED, GACC, LN>(a_codes, a_scales, a_zeros, m, w_codes, w_scales,
+                                                w_sums, k, d, y, acc, stream);
 }
 
 hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,

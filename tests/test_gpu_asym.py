@@ -118,7 +118,7 @@ def test_weight_code_sums(rq):
 # shape (one edge tile, one step)
 ASYM_SHAPES = [(1, 1, 64), (4, 17, 256), (16, 15, 512), (16, 12300, 512), (3, 40, 8192),
                (5, 33, 192), (17, 33, 64), (130, 129, 256), (300, 260, 1024),
-               (512, 448, 512), (300, 456, 512), (128, 224, 256)]
+               (512, 448, 512), (300, 456, 512), (128, 224, 256), (300, 30000, 512)]
 
 
 @pytest.mark.parametrize("m,k,d", ASYM_SHAPES)

@@ -274,10 +274,13 @@ def test_fold_tiny_and_decode_weights(rq):
 # (512, 448, 512): only full 256 x 224 tiles with 16-byte output rows (the
 # LDS-staged epilogue); (300, 456, 512): full and edge tiles in both dimensions;
 # (16, 12300, 512): decode with two 16-row weight groups per workgroup and a
-# ragged last group; (3, 40, 8192): decode over two 2 KB chunks per row
+# ragged last group; (3, 40, 8192): decode over two 2 KB chunks per row;
+# (256, 60000, 256), (300, 30000, 512): 256-column tiles (one round of them on
+# 256 CUs against two of 224 columns), full and edge tiles, both epilogues
 GEMM_SHAPES = [(1, 1, 64), (4, 17, 128), (16, 15, 192), (16, 200, 4096), (17, 33, 64),
                (130, 129, 256), (300, 260, 1024), (129, 257, 4160), (512, 448, 512),
-               (300, 456, 512), (16, 12300, 512), (3, 40, 8192)]
+               (300, 456, 512), (16, 12300, 512), (3, 40, 8192), (256, 60000, 256),
+               (300, 30000, 512)]
 
 
 @pytest.mark.parametrize("m,k,d", GEMM_SHAPES)
