@@ -193,13 +193,13 @@ def cpu_baseline(log) -> dict:
     """The oracle (oracle/rq_oracle.py, untuned) on the GPU machine's host cores:
     fp64 rq_fwht_quant on the 4096 x 4096 workload, on every core it may use
     (rows split over worker processes, capped at 16) and on one, and the
-    oracle's W4A4 GEMM on a 32-token slice of the prefill shape; each the
+    oracle's W4A4 GEMM on a 64-token slice of the prefill shape; each the
     median of 3 runs."""
     model, nproc, avail = _host_cpu()
     procs = max(1, min(avail, 16))
     allc = _time_oracle(["fwht", "--rows", "4096", "--procs", str(procs), "--reps", "3"], 1)
     one = _time_oracle(["fwht", "--rows", "1024", "--procs", "1", "--reps", "3"], 1)
-    gemm = _time_oracle(["gemm", "--rows", "32", "--reps", "3"], procs)
+    gemm = _time_oracle(["gemm", "--rows", "64", "--reps", "3"], procs)
     gbs = allc["bytes"] / allc["median_s"] / 1e9
     gbs1 = one["bytes"] / one["median_s"] / 1e9
     tops = gemm["int_ops"] / gemm["median_s"] / 1e12
@@ -214,11 +214,11 @@ def cpu_baseline(log) -> dict:
         "single_thread": {"value": round(gbs1, 5), "unit": "GB/s", "cores": 1,
                           "sample": f"first 1024 rows, median of 3 ({one['median_s']:.2f} s)"},
         "gemm_prefill_slice": {"value": round(tops, 5), "unit": "TOP/s", "cores": procs,
-                               "sample": f"oracle W4A4 GEMM on 32 of the 2048 prefill tokens x 8192 "
+                               "sample": f"oracle W4A4 GEMM on 64 of the 2048 prefill tokens x 8192 "
                                          f"-> 28672 (exact integer product through a float64 "
                                          f"matrix product, {procs} BLAS threads), median of 3 "
                                          f"({gemm['median_s']:.2f} s); the full 2048 tokens scale "
-                                         f"x64"},
+                                         f"x32"},
     }
 
 
