@@ -191,7 +191,8 @@ int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows,
 
 /*
  * rq_linear_decode_workspace_size -- bytes of device workspace that
- * rq_linear_decode needs: m * d / 2 + 64.
+ * rq_linear_decode needs: m * d / 2 + 64 (0 for a shape rq_linear_decode
+ * rejects).
  */
 size_t rq_linear_decode_workspace_size(int64_t m, int64_t d);
 
@@ -438,7 +439,8 @@ int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64
  * fp32 record of 132 values per query head and split of the cache).  When
  * batch * kv_heads is a multiple of the device's CU count, the call runs one
  * workgroup per KV head over the whole sequence and leaves the workspace
- * untouched; it is still required.
+ * untouched; it is still required.  Returns 0 for a shape rq_decode_attention
+ * rejects or for batch == 0.
  */
 size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64_t group,
                                           int64_t seq);

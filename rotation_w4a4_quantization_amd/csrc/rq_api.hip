@@ -15,6 +15,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Rows are limited so that every grid dimension fits its hardware limit.
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
+// Token rows of the tile GEMM: 128-row tiles in a grid dimension of 65535.
+constexpr int64_t kMaxTileRows = (int64_t)65535 * 128;
+// Decode attention: one workgroup row per (batch, KV head), grid y <= 65535.
+constexpr int64_t kMaxHeads = 65535;
+
+// Shapes rq_decode_attention accepts (checked without overflow: batch and
+// kv_heads are bounded before their product is formed).
+bool attention_shape_ok(int64_t batch, int64_t kv_heads, int64_t group, int64_t seq) {
+  if (batch < 0 || batch > kMaxHeads || kv_heads < 1 || kv_heads > kMaxHeads) return false;
+  if (batch * kv_heads > kMaxHeads) return false;
+  return group >= 1 && group <= 8 && seq >= 2 && seq % 2 == 0 && seq < kMaxRows;
+}
 
 int from_hip(hipError_t e) { return e == hipSuccess ? RQ_OK : RQ_ERR_HIP; }
 
@@ -98,7 +110,7 @@ int rq_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
   (void)workspace;
   (void)workspace_bytes;
   if (m < 0 || k < 0 || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
-  if (m > 16 && (m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (m > kMaxTileRows) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
   if (k == 0) return RQ_ERR_SHAPE;
@@ -130,7 +142,7 @@ int rq_w4a8_gemm(const int8_t* a_codes, const uint16_t* a_scales, int64_t m,
                  const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                  uint16_t* y, int32_t* acc, void* stream) {
   if (m < 0 || k < 0 || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
-  if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (m > kMaxTileRows) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
   if (k == 0) return RQ_ERR_SHAPE;
@@ -147,7 +159,7 @@ int rq_w4a4_gemm_asym(const uint8_t* a_codes, const uint16_t* a_scales, const ui
                       const int32_t* w_sums, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
                       void* stream) {
   if (m < 0 || k < 0 || d < 64 || d > RQ_MAX_D || d % 64 != 0) return RQ_ERR_SHAPE;
-  if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (m > kMaxTileRows) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
   if (k == 0) return RQ_ERR_SHAPE;
@@ -176,7 +188,7 @@ int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64
                          const uint8_t* w_codes, const uint16_t* w_group_scales, int64_t k,
                          int64_t d, uint16_t* y, int32_t* acc, void* stream) {
   if (m < 0 || k < 0 || d < 128 || d > RQ_MAX_D || d % 128 != 0) return RQ_ERR_SHAPE;
-  if ((m + 127) / 128 > 65535) return RQ_ERR_SHAPE;
+  if (m > kMaxTileRows) return RQ_ERR_SHAPE;
   if (k >= kMaxRows) return RQ_ERR_SHAPE;
   if (m == 0) return RQ_OK;
   if (k == 0) return RQ_ERR_SHAPE;
@@ -189,7 +201,7 @@ int rq_w4a4_gemm_grouped(const uint8_t* a_codes, const uint16_t* a_scales, int64
 }
 
 size_t rq_linear_decode_workspace_size(int64_t m, int64_t d) {
-  if (m < 0 || m > 16 || d < 0) return 0;
+  if (m < 0 || m > 16 || !is_pow2(d) || d < 512 || d > 8192) return 0;
   return rq::linear_decode_workspace_bytes(m, d);
 }
 
@@ -227,7 +239,7 @@ int rq_linear_decode_w4a8(const uint16_t* x, int64_t m, int64_t d, const int8_t*
 
 size_t rq_decode_attention_workspace_size(int64_t batch, int64_t kv_heads, int64_t group,
                                           int64_t seq) {
-  if (batch < 1 || kv_heads < 1 || group < 1 || seq < 1) return 0;
+  if (batch < 1 || !attention_shape_ok(batch, kv_heads, group, seq)) return 0;
   return rq::decode_attention_workspace_bytes(batch, kv_heads, group, seq);
 }
 
@@ -237,10 +249,7 @@ int rq_decode_attention(const uint16_t* q, const uint8_t* k_codes, const uint16_
                         int64_t head_dim, const int8_t* signs, float sm_scale, uint16_t* out,
                         float* out_f32, void* workspace, size_t workspace_bytes, void* stream) {
   if (head_dim != 128) return RQ_ERR_SHAPE;
-  if (batch < 0 || kv_heads < 1 || kv_heads > 65535 || group < 1 || group > 8 || seq < 2 ||
-      seq % 2 != 0)
-    return RQ_ERR_SHAPE;
-  if (batch * kv_heads > 65535 || seq >= kMaxRows) return RQ_ERR_SHAPE;
+  if (!attention_shape_ok(batch, kv_heads, group, seq)) return RQ_ERR_SHAPE;
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return RQ_ERR_SHAPE;
   if (batch == 0) return RQ_OK;
   if (q == nullptr || k_codes == nullptr || k_scales == nullptr || v_codes == nullptr ||

@@ -173,6 +173,7 @@ def test_w4a8_gemm_argument_errors(lib):
     assert call(k=0) == binding.RQ_ERR_SHAPE
     assert call(m=-1) == binding.RQ_ERR_SHAPE
     assert call(m=128 * 65536) == binding.RQ_ERR_SHAPE
+    assert call(m=2 ** 63 - 1) == binding.RQ_ERR_SHAPE  # m + 127 would overflow
     assert call(a=MIS) == binding.RQ_ERR_ALIGN
     assert call(w=MIS) == binding.RQ_ERR_ALIGN
 
@@ -180,6 +181,9 @@ def test_w4a8_gemm_argument_errors(lib):
 def test_linear_decode_argument_errors(lib):
     need = lib.rq_linear_decode_workspace_size(4, 4096)
     assert need == 4 * 2048 + 64
+    # shapes the call rejects have no workspace size (and no overflowing one)
+    for m, d in ((17, 4096), (4, 4095), (4, 16384), (4, 2 ** 62), (-1, 4096)):
+        assert lib.rq_linear_decode_workspace_size(m, d) == 0, (m, d)
 
     def call(x=A16, m=4, d=4096, signs=None, w=A16, sw=A16b, k=64, y=A16b, ws=A16b,
              nbytes=need):
@@ -267,6 +271,9 @@ def test_grouped_argument_errors(lib):
 def test_decode_attention_argument_errors(lib):
     need = lib.rq_decode_attention_workspace_size(2, 8, 4, 4096)
     assert need > 0 and need % 16 == 0
+    for shape in ((65536, 1, 4, 4096), (4096, 4096, 4, 4096), (2 ** 62, 2 ** 62, 4, 4096),
+                  (2, 8, 9, 4096), (2, 8, 4, 4095), (2, 8, 4, 2 ** 40), (0, 8, 4, 4096)):
+        assert lib.rq_decode_attention_workspace_size(*shape) == 0, shape
 
     def call(q=A16, kc=A16, ks=A16b, vc=A16, vs=A16b, lens=None, B=2, H=8, G=4, S=4096, D=128,
              signs=None, sm=0.088, out=A16b, out32=None, ws=A16b, nbytes=need):
@@ -284,6 +291,7 @@ def test_decode_attention_argument_errors(lib):
     assert call(sm=float("nan")) == binding.RQ_ERR_SHAPE
     assert call(nbytes=need - 1) == binding.RQ_ERR_SHAPE
     assert call(B=65536, H=1) == binding.RQ_ERR_SHAPE
+    assert call(B=2 ** 62, H=65535) == binding.RQ_ERR_SHAPE  # the product would overflow
     assert call(q=None) == binding.RQ_ERR_NULL
     assert call(ws=None) == binding.RQ_ERR_NULL
     assert call(kc=MIS) == binding.RQ_ERR_ALIGN
