@@ -70,3 +70,45 @@ def test_noalloc_rejects_bad_arguments(rq):
     assert lib.rq_linear_decode_noalloc(ptr(x), 4, 16384, None, ptr(w), ptr(s), 8, ptr(y), None) == 2
     assert lib.rq_linear_decode_noalloc(None, 4, 512, None, ptr(w), ptr(s), 8, ptr(y), None) == 1
     assert lib.rq_linear_decode_noalloc(ptr(x), 0, 512, None, None, None, 8, None, None) == 0
+
+
+def test_noalloc_under_graph_capture(rq):
+    """The callers the entry point is for: the call captured in a HIP graph
+    (it allocates nothing, so the capture holds only its kernels), replayed
+    several times with eager work between the replays (including an eager
+    call of the same entry point on another input, which rewrites the
+    library's device array); every replay equals the eager workspace entry
+    point's result bit for bit."""
+    d, k = 4096, 1000
+    for m in (3, 12):  # one launch; rotation into the device array, then the GEMM
+        rng = np.random.default_rng(4321 + m)
+        x = (rng.standard_normal((m, d)) * np.where(rng.random(d) < 0.01, 50.0, 1.0)).astype(np.float16)
+        x2 = (rng.standard_normal((m, d)) * 3.0).astype(np.float16)
+        wt = (rng.standard_normal((k, d)) * 0.02).astype(np.float32)
+        signs = torch.from_numpy(datagen.rademacher(rng, d)).cuda()
+        xd, x2d = torch.from_numpy(x).cuda(), torch.from_numpy(x2).cuda()
+        wc, ws, _ = rq.fold_weights(torch.from_numpy(wt).cuda(), signs)
+        y_ref = rq.linear_decode(xd, signs, wc, ws)
+        y2_ref = rq.linear_decode(x2d, signs, wc, ws)
+        y = torch.empty((m, k), dtype=torch.float16, device="cuda")
+        y2 = torch.empty((m, k), dtype=torch.float16, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up outside the capture
+            rq.linear_decode_noalloc(xd, signs, wc, ws, out=y)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        say(f"noalloc graph capture m={m}")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rq.linear_decode_noalloc(xd, signs, wc, ws, out=y)
+        for rep in range(4):
+            y.fill_(float("nan"))  # a fill kernel, eager
+            rq.linear_decode_noalloc(x2d, signs, wc, ws, out=y2)  # eager, other input
+            torch.cuda.synchronize()
+            assert torch.equal(y2.view(torch.int16), y2_ref.view(torch.int16)), (m, rep)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (m, rep)
+        del g
+        torch.cuda.synchronize()
