@@ -1125,8 +1125,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
       // writes slowed those reads (measured 2-4% on the 2048 x 8192 -> 28672
       // prefill).  They still have half a step to land.  A8 (one half per
       // step) issues them after its first column tile (376 -> 364-368 us on
-      // the same prefill); GROUPED, where the later issue costs registers it
-      // does not have (244 bytes of spills), at the start of the step.
+      // the same prefill), and so does GROUPED, in the first half (491 -> 476
+      // us; at the second half it would spill 244 bytes and run 2.5x slower).
       constexpr bool kLateIssue = !A8 && !GROUPED;
       auto issue_next = [&]() {
         if (s + 1 < steps) {
@@ -1147,7 +1147,6 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           RQ_ISSUE_FROM(par ^ 1, an, bn, RQ_GSRC(n0n), 0);
         }
       };
-      if constexpr (GROUPED) issue_next();
       const unsigned char* cur = lds + par * BUFS;
       uint32_t sgw[JT];  // GROUPED: the step's two group scales of column j
       if constexpr (GROUPED) {
@@ -1179,8 +1178,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
         }
 #pragma unroll
         for (int j = 0; j < JT; ++j) {
-          if constexpr (A8) {
-            if (j == 1) issue_next();
+          if constexpr (A8 || GROUPED) {
+            if (u == 0 && j == 1) issue_next();
           }
           const uint4 q = *reinterpret_cast<const uint4*>(cur + LM * APK + (wn * WNC + j * 16) * BPK +
                                                           (A8 ? frag_b8 : fo));
