@@ -779,6 +779,44 @@ def main():
                 sec[name] = line(mm_, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
                 log(f"[bench] {name}: {sec[name]}")
                 del outm
+            # issue rates of the instruction classes the kernels are made of: does
+            # VALU work overlap MFMA work on a SIMD (kinds 0, 1, 2 at two
+            # wavefronts per SIMD, as in the prefill GEMMs), and what does a DPP
+            # lane exchange cost against a plain fp32 op (kinds 3, 4 at four
+            # wavefronts per SIMD, as in the rotation)
+            lib.rq_ceiling_issue_out_words.argtypes = [ctypes.c_int64]
+            lib.rq_ceiling_issue_out_words.restype = ctypes.c_size_t
+            lib.rq_ceiling_issue.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_void_p]
+            lib.rq_ceiling_issue.restype = ctypes.c_int64
+            issue_ns = {}
+            for name, kind, wps, per_round in (("issue_mfma8_2waves", 0, 2, 8),
+                                               ("issue_cvt_fma32_2waves", 1, 2, 64),
+                                               ("issue_mfma8_plus_cvt_fma32_2waves", 2, 2, 72),
+                                               ("issue_fmac32_4waves", 3, 4, 32),
+                                               ("issue_dpp_fmac32_4waves", 4, 4, 32)):
+                if not want_line(name):
+                    continue
+                outi = torch.empty((int(lib.rq_ceiling_issue_out_words(wps)),), dtype=torch.float32,
+                                   device=dev)
+                iters = 2048
+
+                def iss(i, outi=outi, kind=kind, wps=wps, iters=iters):
+                    assert lib.rq_ceiling_issue(_ptr(outi), kind, wps, iters, _stream()) > 0
+
+                mi = time_launches(torch, iss, 1, max(5, steps2 // 4), warm2)
+                # SIMD time per wavefront round, and per wavefront instruction
+                ns_round = mi * 1e6 / (iters * wps)
+                issue_ns[kind] = ns_round
+                extra = {"ns_per_round_per_simd": round(ns_round, 2),
+                         "ns_per_instr_per_simd": round(ns_round / per_round, 3)}
+                if kind == 2 and 0 in issue_ns and 1 in issue_ns:
+                    # 1: the VALU block hides fully under the MFMAs; 0: the two add up
+                    hid = (issue_ns[0] + issue_ns[1] - ns_round) / min(issue_ns[0], issue_ns[1])
+                    extra["overlap"] = round(hid, 3)
+                sec[name] = line(mi, **extra)
+                log(f"[bench] {name}: {sec[name]}")
+                del outi
     result["secondary"] = sec
 
     # ------------------------------------------------------- CPU baseline

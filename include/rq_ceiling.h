@@ -52,6 +52,27 @@ size_t rq_ceiling_mfma_out_words(int64_t waves_per_simd);
  */
 int64_t rq_ceiling_mfma_i8(int32_t* out, int64_t waves_per_simd, int64_t iters, void* stream);
 
+/* Floats of `out` that rq_ceiling_issue writes for this occupancy. */
+size_t rq_ceiling_issue_out_words(int64_t waves_per_simd);
+
+/*
+ * Issue-rate loop: waves_per_simd (1..8) wavefronts per SIMD on every CU
+ * each run `iters` (1..2^24) rounds of one register-only instruction block
+ * and store one float per lane to out [rq_ceiling_issue_out_words(...)]:
+ *   kind 0: 8 independent v_mfma_i32_16x16x64_i8;
+ *   kind 1: 32 independent (v_cvt_f32_i32, v_fmac_f32) pairs;
+ *   kind 2: the blocks of kinds 0 and 1 in the same round;
+ *   kind 3: 32 independent v_fmac_f32;
+ *   kind 4: 32 independent v_fmac_f32_dpp (quad_perm lane exchange).
+ * Kinds 0..2 show whether MFMA and VALU work of a SIMD overlap (the time
+ * of kind 2 against the sum of kinds 0 and 1); kinds 3 and 4 the issue cost
+ * of a lane-crossing DPP operation against a plain one.  Returns the
+ * wavefront rounds run (blocks * 4 * iters), or -1 (NULL), -2 (bad kind or
+ * size), -5 (launch failure).
+ */
+int64_t rq_ceiling_issue(float* out, int64_t kind, int64_t waves_per_simd, int64_t iters,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

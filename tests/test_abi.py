@@ -58,6 +58,18 @@ def test_ceiling_probe_argument_errors(lib):
     assert lib.rq_ceiling_mfma_i8(A16, 9, 10, None) == -2
     assert lib.rq_ceiling_mfma_i8(A16, 2, 0, None) == -2
     assert lib.rq_ceiling_mfma_out_words(0) == 0
+    lib.rq_ceiling_issue.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p]
+    lib.rq_ceiling_issue.restype = ctypes.c_int64
+    lib.rq_ceiling_issue_out_words.argtypes = [ctypes.c_int64]
+    lib.rq_ceiling_issue_out_words.restype = ctypes.c_size_t
+    assert lib.rq_ceiling_issue(None, 0, 2, 10, None) == -1
+    assert lib.rq_ceiling_issue(A16, 5, 2, 10, None) == -2
+    assert lib.rq_ceiling_issue(A16, -1, 2, 10, None) == -2
+    assert lib.rq_ceiling_issue(A16, 0, 0, 10, None) == -2
+    assert lib.rq_ceiling_issue(A16, 0, 2, 0, None) == -2
+    assert lib.rq_ceiling_issue(A16, 0, 2, (1 << 24) + 1, None) == -2
+    assert lib.rq_ceiling_issue_out_words(9) == 0
 
 
 def test_version_and_status_strings(lib):
