@@ -578,21 +578,40 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
       for (int b = 0; b < NB; ++b) xo[P * b + tid] = y[b] * c32;
     }
 
-    // 4. codes: element P b + tid is nibble (tid & 1) of byte (P / 2) b + tid / 2;
-    // the odd lane's code reaches its even neighbour by DPP
+    // 4. codes.  Every thread writes its 28 offset-binary codes (q + 8) as
+    // bytes, element P b + tid at byte P b + tid (over the fp32 row, which
+    // every thread has read): the low byte of fma(y, m, 2^23 + 8) is exactly
+    // the code, its bits 4..7 are zero.  After a barrier each thread packs 32
+    // consecutive code bytes into 16 bytes of nibble pairs (element e is
+    // nibble e & 1 of byte e / 2) and stores them.  The scale is the row's,
+    // so the subnormal clamp is a uniform branch.
+    float q[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float q = __builtin_fmaf(y[b], mult, kMagic);
-      if (subnormal) q = fminf(fmaxf(q, kMagicLo), kMagicHi);
-      const uint32_t code = f2u(q) & 0xFu;
-      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, 0xB1, 0xF, 0xF, false);
-      if (!(tid & 1)) cbuf[(P / 2) * b + (tid >> 1)] = (unsigned char)((code | (other << 4)) ^ 0x88u);
+    for (int b = 0; b < NB; ++b) q[b] = __builtin_fmaf(y[b], mult, kMagic);
+    if (__builtin_amdgcn_readfirstlane((int)subnormal)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) q[b] = fminf(fmaxf(q[b], kMagicLo), kMagicHi);
     }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cbuf[P * b + tid] = (unsigned char)f2u(q[b]);
     __syncthreads();
     uint8_t* dst = o.codes + row * (N / 2);
-    for (int c = tid; c < N / 32; c += P)
-      __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(cbuf + 16 * c),
-                                  reinterpret_cast<v4u*>(dst + 16 * c));
+    for (int c = tid; c < N / 32; c += P) {
+      const v4u lo = *reinterpret_cast<const v4u*>(cbuf + 32 * c);
+      const v4u hi = *reinterpret_cast<const v4u*>(cbuf + 32 * c + 16);
+      // bytes c0..c3 of d0 and c4..c7 of d1: d | d >> 4 holds the pairs
+      // (c0, c1), (c2, c3) in its bytes 0 and 2; one byte permute joins them
+      const auto pack8 = [](uint32_t d0, uint32_t d1) {
+        return __builtin_amdgcn_perm(d1 | (d1 >> 4), d0 | (d0 >> 4), 0x06040200u);
+      };
+      v4u out;
+      out[0] = pack8(lo[0], lo[1]);
+      out[1] = pack8(lo[2], lo[3]);
+      out[2] = pack8(hi[0], hi[1]);
+      out[3] = pack8(hi[2], hi[3]);
+      out ^= 0x88888888u;  // offset binary to two's complement nibbles
+      __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(dst + 16 * c));
+    }
     if (!more) break;
     __syncthreads();  // the next row overwrites xb
     row = next;

@@ -128,8 +128,11 @@ def test_fwht_quant_28x1024(rq, m, dtype):
         timed_fq_matches_oracle(rq, x, signs, c, s, f"n=28x1024 m={m}", fold=dtype == np.float32)
 
 
-def test_fwht_quant_28x1024_special_rows(rq):
-    n = 28672
+@pytest.mark.parametrize("n", [14336, 28672])
+def test_fwht_quant_28xP_special_rows(rq, n):
+    """Zero, one-hot, underflowing, overflowing and fp16-subnormal-scale rows
+    (the clamp the kernel takes as a uniform branch) at n = 28 * 512 and
+    28 * 1024."""
     rng = np.random.default_rng(55)
     signs = datagen.rademacher(rng, n)
     x = np.zeros((5, n), np.float32)
@@ -137,9 +140,9 @@ def test_fwht_quant_28x1024_special_rows(rq):
     x[2] = 1e-30                          # underflows the fp16 scale -> zero codes
     x[3] = rng.standard_normal(n) * 1e6   # fp16 scale overflows -> +inf, zero codes
     x[4, :4] = [4e-4, -4e-4, 1e-4, 0.0]   # fp16-subnormal scale (clamped path)
-    say("fwht_quant n=28x1024 special rows")
+    say(f"fwht_quant n={n} special rows")
     c, s, r = run_fq(rq, x, signs)
-    check_rotation_result(x, signs, c, s, r, what="28x1024 special rows")
+    check_rotation_result(x, signs, c, s, r, what=f"n={n} special rows")
     q = O.unpack_int4(c)
     assert not q[0].any() and not q[2].any() and not q[3].any()
     assert set(np.abs(q[1]).tolist()) == {7}
