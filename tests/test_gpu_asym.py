@@ -103,6 +103,28 @@ def test_fwht_quant_asym_special_rows(rq):
     assert 0 < s.view(np.uint16)[4] < 0x0400
 
 
+def test_fwht_quant_asym_clamp_rows(rq):
+    """Rows whose largest code passes 15 before the clamp (a one-hot input at
+    index 1 rotates to +-c everywhere, so hi / step sits at 7.5 and the fp16
+    rounding of the step decides), next to rows that need no clamp: random
+    rows almost never reach the clamp, so this is where it is exercised; the
+    codes match the oracle's, timed and debug launches alike."""
+    n = 4096
+    vals = np.float16(np.linspace(0.5, 4.0, 64))
+    x = np.zeros((len(vals), n), np.float16)
+    x[:, 1] = vals
+    ref = O.fwht_quant_asym(x, None, "f32")
+    unclamped = np.rint(ref["v"]) + ref["zeros"].astype(np.float64)[:, None]
+    need = (unclamped > 15).any(axis=1) | (unclamped < 0).any(axis=1)
+    assert need.any() and not need.all(), "the rows must exercise both branches"
+    say(f"fwht_quant_asym clamp rows: {int(need.sum())} of {len(vals)} need the clamp")
+    c, s, z, r = run_asym(rq, x, None)
+    check_asym_result(x, None, c, s, z, r, what="asym clamp rows")
+    c2, s2, z2, _ = run_asym(rq, x, None, debug=False)
+    assert np.array_equal(c, c2) and np.array_equal(z, z2)
+    assert (O.unpack_uint4(c)[need] == 15).any()
+
+
 def test_weight_code_sums(rq):
     rng = np.random.default_rng(10)
     for k, d in ((1, 64), (37, 512), (300, 4160), (5, 16384)):
