@@ -190,7 +190,7 @@ def _time_oracle(args, threads: int):
 
 
 def cpu_baseline(log) -> dict:
-    """The oracle (oracle/rq_oracle.py, untuned) on the GPU machine's host cores:
+    """The oracle (oracle/rq_oracle.py, untuned) on the host's CPU cores:
     fp64 rq_fwht_quant on the 4096 x 4096 workload, on every core it may use
     (rows split over worker processes, capped at 16) and on one, and the
     oracle's W4A4 GEMM on a 64-token slice of the prefill shape; each the
@@ -227,7 +227,7 @@ def main():
     args = parse()
     REPLAYS = max(1, args.replays)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the rq kernels run on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     for v in ("RANK", "WORLD_SIZE"):
