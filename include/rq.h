@@ -149,7 +149,8 @@ size_t rq_w4a4_gemm_workspace_size(int64_t m, int64_t k, int64_t d);
  * rotated activation multiplies the INT4 folded weight in a low-bit kernel).
  * INT4 codes are widened to int8 in registers and multiplied with int8 MFMA
  * into int32 accumulators (exact: |acc| <= 64 * d, see RQ_MAX_D); the epilogue is
- * fp32(acc) * sa, then * sw, rounded to fp16 half to even.
+ * t = fp32(fp32(acc) * sa), then t * sw rounded once to fp16 half to even
+ * (from the exact product, with no fp32 rounding in between).
  *
  *   a_codes  [m][d/2] uint8 activation codes (rq_fwht_quant output), 16-byte
  *            aligned; a_scales [m] fp16.

@@ -40,6 +40,26 @@ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(flo
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h_rn(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
+// fp16 of the product a * b, rounded once from the exact product (half to
+// even): v_fma_mixlo_f16 with a -0 addend (a * b + -0 is a * b, the sign of a
+// zero product included).  Measured on gfx950: this is the once-rounded
+// product, while v_mul_f32 then v_cvt_f16_f32 rounds twice (to fp32, then to
+// fp16).  The compiler emits either form for fp16(a * b) depending on the
+// code around it, so the GEMM epilogues name the instruction.  Bits 16-31 of
+// the result are unspecified.
+__device__ __forceinline__ uint32_t f16_mul_lo(float a, float b) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, neg(0)" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// fp16(a0 * b0) in bits 0-15 and fp16(a1 * b1) in bits 16-31, each rounded
+// once as above
+__device__ __forceinline__ uint32_t f16_mul_pair(float a0, float b0, float a1, float b1) {
+  uint32_t r = f16_mul_lo(a0, b0);
+  asm("v_fma_mixhi_f16 %0, %1, %2, neg(0)" : "+v"(r) : "v"(a1), "v"(b1));
+  return r;
+}
+
 // fp16_rne(xm / D) rounded once from the exact quotient (xm >= 0, finite;
 // D = 7 for INT4 codes, 127 for INT8).  The fp32 quotient is correctly
 // rounded; only when it lands exactly on an fp16 rounding midpoint can a

@@ -82,7 +82,7 @@ __device__ __forceinline__ void epilogue_store(int32_t raw, float sa, float sw, 
                                                int32_t zsum = 0) {
   const int32_t a = (raw >> SHIFT) - zsum;
   if (acc != nullptr) acc[idx] = a;
-  y[idx] = f2h_rn(((float)a * sa) * sw);
+  y[idx] = (uint16_t)f16_mul_lo((float)a * sa, sw);
 }
 
 // ---------------------------------------------------------------- tile GEMM
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void w4a4_tile_kernel(const uint8_t* __restric
         const int64_t col = n0 + wn * 64 + j * 16 + r16;
         if (col >= k) continue;
         if constexpr (GROUPED)
-          y[row * k + col] = f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa);
+          y[row * k + col] = (uint16_t)f16_mul_lo(facc[i][j][e] * (1.0f / 256.0f), sa);
         else
           epilogue_store<AM == kA4 ? 8 : 4>(acc[i][j][e], sa, h2f(w_scales[col]), row * k + col,
                                             y, acc_out, AM == kAU4 ? z * w_sums[col] : 0);
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void w4a4_decode_grouped_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = 4 * t.g + e;
-        if (row < m) y[row * k + col] = f2h_rn((sum[e] * (1.0f / 256.0f)) * epi.sa[e]);
+        if (row < m) y[row * k + col] = (uint16_t)f16_mul_lo(sum[e] * (1.0f / 256.0f), epi.sa[e]);
       }
     }
   }
@@ -1288,8 +1288,8 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
               // exact: the MFMA sum is 2^SHIFT * sum qa qw
               const int32_t a = (acc[i][j][e] >> SHIFT) - z * wsv[j];
               *reinterpret_cast<uint16_t*>(stg + tr * OP + 2 * (wn * WNC + j * 16 + r16)) =
-                  GROUPED ? f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa)
-                          : f2h_rn(((float)a * sa) * swv[j]);
+                  (uint16_t)(GROUPED ? f16_mul_lo(facc[i][j][e] * (1.0f / 256.0f), sa)
+                                     : f16_mul_lo((float)a * sa, swv[j]));
             }
           }
         }
@@ -1320,7 +1320,7 @@ __global__ __launch_bounds__(LTHREADS) void w4a4_large_kernel(const uint8_t* __r
           for (int j = 0; j < JT; ++j) {
             if (full || n0 + wn * WNC + j * 16 + r16 < k) {
               if constexpr (GROUPED)
-                y[base + j * 16] = f2h_rn((facc[i][j][e] * (1.0f / 256.0f)) * sa);
+                y[base + j * 16] = (uint16_t)f16_mul_lo(facc[i][j][e] * (1.0f / 256.0f), sa);
               else
                 epilogue_store<SHIFT>(acc[i][j][e], sa, swv[j], base + j * 16, y, acc_out,
                                       z * wsv[j]);

@@ -306,6 +306,53 @@ def test_gemm_random_codes(rq, m, k, d):
         assert np.array_equal(y2.host().view(np.uint16), yo.host().view(np.uint16))
 
 
+def epilogue_once(acc, sa, sw):
+    """The epilogue the GEMM entry points document, written out on the host:
+    t = fp32(fp32(acc) * sa), then t * sw rounded once to fp16 (the float64
+    product of two float32 is exact, and numpy rounds float64 to float16 once).
+    Also returns the twice-rounded value fp16(fp32(t * sw)) for comparison."""
+    t = acc.astype(np.float32) * sa.astype(np.float32)[:, None]
+    with np.errstate(over="ignore"):
+        once = (t.astype(np.float64) * sw.astype(np.float64)[None, :]).astype(np.float16)
+        twice = (t * sw.astype(np.float32)[None, :]).astype(np.float16)
+    return once, twice
+
+
+# decode (m <= 16), the tile kernel (16 < m < 128), and the persistent prefill
+# kernel with full tiles only and with edge tiles; each through the debug
+# launch (direct stores) and the timed launch (LDS-staged stores)
+@pytest.mark.parametrize("kind,m,k,d", [("w4a4", 8, 8000, 512), ("w4a4", 64, 1000, 1024),
+                                        ("w4a4", 256, 448, 512), ("w4a4", 300, 456, 512),
+                                        ("asym", 256, 448, 512), ("w4a8", 256, 448, 512)])
+def test_gemm_epilogue_rounds_once(rq, kind, m, k, d):
+    rng = np.random.default_rng(77 + m + k + d)
+    wc = datagen.random_codes(rng, k, d)
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k)
+    say(f"gemm epilogue rounding {kind} m={m} k={k} d={d}")
+    if kind == "w4a8":
+        ac = datagen.random_codes8(rng, m, d)
+        _, acc_ref = O.w4a8_gemm(ac, sa, wc, sw)
+        run = lambda debug: rq.w4a8_gemm(dev(ac), dev(sa), dev(wc), dev(sw), debug=debug)[0]
+    elif kind == "asym":
+        ac = datagen.random_codes(rng, m, d)
+        za = rng.integers(0, 16, m).astype(np.uint8)
+        _, acc_ref = O.w4a4_gemm_asym(ac, sa, za, wc, sw)
+        wsum = rq.weight_code_sums(dev(wc))
+        run = lambda debug: rq.w4a4_gemm_asym(dev(ac), dev(sa), dev(za), dev(wc), dev(sw), wsum,
+                                              debug=debug)[0]
+    else:
+        ac = datagen.random_codes(rng, m, d)
+        _, acc_ref = O.w4a4_gemm(ac, sa, wc, sw)
+        run = lambda debug: rq.w4a4_gemm(dev(ac), dev(sa), dev(wc), dev(sw), debug=debug)[0]
+    once, twice = epilogue_once(acc_ref, sa, sw)
+    assert (once.view(np.uint16) != twice.view(np.uint16)).any(), "no case where the roundings differ"
+    for debug in (True, False):
+        y = host(run(debug))
+        bad = y.view(np.uint16) != once.view(np.uint16)
+        assert not bad.any(), f"{kind} {m}x{k}x{d} debug={debug}: {int(bad.sum())} outputs differ"
+
+
 @pytest.mark.parametrize("m", [3, 64])
 def test_gemm_closed_form_extremes(rq, m):
     d, k = 8192, 40
