@@ -145,11 +145,20 @@ def kron28_transform(u: np.ndarray, precision: str = "f64") -> np.ndarray:
     (:func:`hadamard_transform`, ascending strides).  Step 2: for every
     position, y[b'] = sum_b H_28[b'][b] t[b] (H_28 symmetric).
     "f64": step 2 is the dense 28 x 28 product in float64.
-    "f32": step 2 in float32, in the order that the Paley structure
+    "f32": step 2 in float32, in an order that the Paley structure
     H_28 = C (x) H_2 + I (x) J_2 gives: a_i = t[2i] + t[2i+1],
-    d_i = t[2i] - t[2i+1]; then y[2j] = (sum over i != j, ascending, of
-    C[j][i] a_i) + d_j and y[2j+1] = (the same sum of C[j][i] d_i) - a_j,
-    each sum accumulated left to right (C[j][i] = +-1 is a sign flip).
+    d_i = t[2i] - t[2i+1], y[2j] = (C a)_j + d_j and y[2j+1] = (C d)_j - a_j.
+    The conference matrix products use the residue structure of C: with
+    S = v_1 + ... + v_13 and T_x = sum over the quadratic residues r of 13
+    of v_(1 + (x - r) mod 13), row 1 + x of C has +1 exactly at those
+    columns and at column 0, and -1 at the other twelve off-diagonal ones,
+    so (C v)_0 = S and (C v)_(1+x) = v_0 + T_x - (S - v_(1+x) - T_x)
+    = 2 T_x + ((v_0 - S) + v_(1+x)).  In float32: S accumulated left to
+    right over i = 1..13, w = v_0 - S, T_x left to right over the residues
+    in ascending order; then y[0] = S_a + d_0, y[1] = S_d - a_0 and, for
+    j = 1 + x, y[2j] = 2 T_x(a) + (w_a + (a_j + d_j)) and
+    y[2j+1] = 2 T_x(d) + (w_d + (d_j - a_j)) (2 T is exact, so each of
+    these last sums rounds once).
     """
     u = np.asarray(u)
     n = u.shape[-1]
@@ -165,22 +174,33 @@ def kron28_transform(u: np.ndarray, precision: str = "f64") -> np.ndarray:
         return y.reshape(lead + (n,))
     if precision != "f32":
         raise ValueError(f"precision must be 'f64' or 'f32', got {precision!r}")
-    conf = _paley_conference_14()
+    residues = sorted({(r * r) % 13 for r in range(1, 13)})
     a = t[..., 0::2, :] + t[..., 1::2, :]   # [..., 14, P]
     d = t[..., 0::2, :] - t[..., 1::2, :]
+
+    def conference_terms(v):
+        """S, w = v_0 - S and T_x (x = 0..12) of C v, in float32."""
+        s = v[..., 1, :]
+        for i in range(2, 14):
+            s = s + v[..., i, :]
+        w = v[..., 0, :] - s
+        ts = []
+        for x in range(13):
+            tx = v[..., 1 + (x - residues[0]) % 13, :]
+            for r in residues[1:]:
+                tx = tx + v[..., 1 + (x - r) % 13, :]
+            ts.append(tx)
+        return s, w, ts
+
+    s_a, w_a, t_a = conference_terms(a)
+    s_d, w_d, t_d = conference_terms(d)
     y = np.empty_like(t)
-    for j in range(14):
-        acc_a = None
-        acc_d = None
-        for i in range(14):
-            if i == j:
-                continue
-            sa = a[..., i, :] if conf[j, i] > 0 else -a[..., i, :]
-            sd = d[..., i, :] if conf[j, i] > 0 else -d[..., i, :]
-            acc_a = sa.copy() if acc_a is None else acc_a + sa
-            acc_d = sd.copy() if acc_d is None else acc_d + sd
-        y[..., 2 * j, :] = acc_a + d[..., j, :]
-        y[..., 2 * j + 1, :] = acc_d - a[..., j, :]
+    y[..., 0, :] = s_a + d[..., 0, :]
+    y[..., 1, :] = s_d - a[..., 0, :]
+    for x in range(13):
+        j = 1 + x
+        y[..., 2 * j, :] = (t_a[x] + t_a[x]) + (w_a + (a[..., j, :] + d[..., j, :]))
+        y[..., 2 * j + 1, :] = (t_d[x] + t_d[x]) + (w_d + (d[..., j, :] - a[..., j, :]))
     return y.reshape(lead + (n,)).astype(np.float32)
 
 
