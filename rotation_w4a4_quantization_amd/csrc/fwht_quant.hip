@@ -498,11 +498,15 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
   constexpr int BPW = (NB + W - 1) / W;  // blocks per wave
   constexpr int SUB = P / 512;           // 512-element sub-blocks (chunks) per block
   static_assert(P == 512 || P == 1024, "blocks of 512 or 1024 elements");
-  __shared__ __align__(16) float xb[NB][P];  // the row in fp32; then its code bytes
+  __shared__ __align__(16) float xb[NB][P];  // the row in fp32
+  // the row's code bytes, apart from xb: the next row's fp32 stores into xb
+  // need no barrier after the codes are packed (its own code bytes are
+  // written only after its absmax barrier, which every wave reaches after
+  // packing this row)
+  __shared__ __align__(16) unsigned char cbuf[NB * P];
   __shared__ float amx[W];
   const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
   const RowLane rl = make_row_lane(L);
-  unsigned char* cbuf = reinterpret_cast<unsigned char*>(&xb[0][0]);
 
   int64_t row = blockIdx.x;
   if (row >= rows) return;  // uniform per workgroup
@@ -613,8 +617,7 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
     }
 
     // 4. codes.  Every thread writes its 28 offset-binary codes (q + 8) as
-    // bytes, element P b + tid at byte P b + tid (over the fp32 row, which
-    // every thread has read): the low byte of fma(y, m, 2^23 + 8) is exactly
+    // bytes, element P b + tid at byte P b + tid: the low byte of fma(y, m, 2^23 + 8) is exactly
     // the code, its bits 4..7 are zero.  After a barrier each thread packs 32
     // consecutive code bytes into 16 bytes of nibble pairs (element e is
     // nibble e & 1 of byte e / 2) and stores them.  The scale is the row's,
@@ -647,7 +650,6 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
       __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(dst + 16 * c));
     }
     if (!more) break;
-    __syncthreads();  // the next row overwrites xb
     row = next;
   }
 }
