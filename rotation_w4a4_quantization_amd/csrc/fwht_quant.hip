@@ -380,7 +380,8 @@ __global__ __launch_bounds__(64 * kRowWaves, N <= 4096 ? 4 : 2) void fwht_row_ke
 // sub-block is one 16-byte chunk per lane through the 512-point stages of the
 // row kernel, and for P = 1024 the last stage (stride 512) combines the two
 // sub-blocks in registers.  The block goes, sign-corrected, to an fp32 LDS
-// row; the next row's chunks are loaded while the rest of the row runs.
+// row; the next row's chunks are loaded during the P-point stages (P = 1024)
+// or right after them, and arrive while the rest of the row runs.
 // After a barrier, thread t takes position t and applies H_28 across the 28
 // blocks in an order the Paley structure H_28 = C (x) H_2 + I (x) J_2 gives
 // (C the order-14 conference matrix, J_2 = [[1, -1], [-1, -1]]):
@@ -521,6 +522,15 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
                                  P * (wave + W * i) + 512 * j + 8 * L);
 
   for (;;) {
+    // P = 1024 with fp16 input (one workgroup per CU, nothing else to hide
+    // the loads behind): the next row's chunk goes out as soon as this row's
+    // is consumed, so it is in flight during the rest of this row (55.0 ->
+    // 53.8 us at 2048 x 28672).  Otherwise it is loaded after the P-point
+    // stages: at P = 512 the CU's second workgroup already overlaps it (no
+    // gain measured), and the fp32 fold would spill.
+    constexpr bool kEarlyLoad = sizeof(T) == 2 && P == 1024;
+    const int64_t next = row + gridDim.x;
+    const bool more = next < rows;
     // 1. the P-point stages of this wave's blocks, sign-corrected into LDS
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
@@ -530,6 +540,8 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
         chunk28_e0<T, HAS_SIGNS>(raw[i][j], signs, P * b + 512 * j + 8 * L, c[j]);
+        if (kEarlyLoad && more)
+          raw[i][j] = load_chunk28(static_cast<const T*>(o.x) + next * N, P * b + 512 * j + 8 * L);
         chunk512_stages(c[j], rl);
       }
       if constexpr (SUB == 2) {  // stride 512: sub-block 0 with sub-block 1
@@ -548,10 +560,7 @@ __global__ __launch_bounds__(P) void fwht28_kernel(FQOut o, int64_t rows,
           *reinterpret_cast<float2*>(&xb[b][p]) = make_float2(c[j][r] * rl.sigma, c[j][r + 1] * rl.sigma);
         }
     }
-    // the next row's chunks are in flight during the rest of this row
-    const int64_t next = row + gridDim.x;
-    const bool more = next < rows;
-    if (more) {
+    if (!kEarlyLoad && more) {
 #pragma unroll
       for (int i = 0; i < BPW; ++i)
 #pragma unroll
