@@ -237,3 +237,26 @@ def test_asym_prefill_full_size_sampled(rq):
     check_gemm_asym(ac, sa, za, wc[cols], ws[cols], y[:, cols], acc[:, cols], "asym prefill cols")
     check_gemm_asym(ac[rows], sa[rows], za[rows], wc, ws, y[rows], acc[rows], "asym prefill rows")
     check_gemm_asym(ac, sa, za, wc[cols], ws[cols], yt[:, cols], None, "asym prefill timed cols")
+
+
+@pytest.mark.parametrize("m,k,d", [(4, 300, 512), (64, 200, 1024), (256, 448, 512), (300, 456, 512)])
+def test_asym_with_zero_point_8_is_the_symmetric_gemm(rq, m, k, d):
+    """Symmetric codes q in two's complement nibbles are the unsigned codes
+    q + 8 (each nibble xor 8) with zero point 8, so the asymmetric GEMM on
+    those returns the symmetric GEMM's int32 accumulators and y bit for bit
+    (decode, tile and prefill kernels)."""
+    rng = np.random.default_rng(m + 7 * k + d)
+    ac = datagen.random_codes(rng, m, d)
+    wc = datagen.random_codes(rng, k, d)
+    sa = datagen.random_scales(rng, m)
+    sw = datagen.random_scales(rng, k)
+    say(f"asym zero point 8 vs symmetric m={m} k={k} d={d}")
+    y_s, acc_s = rq.w4a4_gemm(dev(ac), dev(sa), dev(wc), dev(sw), debug=True)
+    wsum = rq.weight_code_sums(dev(wc))
+    z8 = np.full(m, 8, np.uint8)
+    y_a, acc_a = rq.w4a4_gemm_asym(dev(ac ^ 0x88), dev(sa), dev(z8), dev(wc), dev(sw), wsum, debug=True)
+    assert np.array_equal(host(acc_a), host(acc_s))
+    assert np.array_equal(host(y_a).view(np.uint16), host(y_s).view(np.uint16))
+    y_a2, _ = rq.w4a4_gemm_asym(dev(ac ^ 0x88), dev(sa), dev(z8), dev(wc), dev(sw), wsum)
+    y_s2, _ = rq.w4a4_gemm(dev(ac), dev(sa), dev(wc), dev(sw))
+    assert np.array_equal(host(y_a2).view(np.uint16), host(y_s2).view(np.uint16))
