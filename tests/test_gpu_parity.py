@@ -353,19 +353,25 @@ def test_gemm_epilogue_rounds_once(rq, kind, m, k, d):
         assert not bad.any(), f"{kind} {m}x{k}x{d} debug={debug}: {int(bad.sum())} outputs differ"
 
 
-@pytest.mark.parametrize("m", [3, 64])
-def test_gemm_closed_form_extremes(rq, m):
-    d, k = 8192, 40
+# decode (m = 3), tile (m = 64) and prefill (m = 256, k = 224) kernels, at
+# d = 8192 and at the largest d (RQ_MAX_D = 32768, where the W4A4 MFMA sum
+# 256 * 64 * d = 2^29 is the largest the int32 path has to hold)
+@pytest.mark.parametrize("m,k,d", [(3, 40, 8192), (64, 40, 8192), (3, 40, 32768), (64, 40, 32768),
+                                   (256, 224, 32768)])
+def test_gemm_closed_form_extremes(rq, m, k, d):
     a = O.pack_int4(np.full((m, d), -8))
     w = O.pack_int4(np.full((k, d), -8))
     w[1::2] = O.pack_int4(np.full((1, d), 7))
-    say(f"gemm extremes m={m}")
+    say(f"gemm extremes m={m} k={k} d={d}")
     y, acc = rq.w4a4_gemm(dev(a), dev(np.ones(m, np.float16)), dev(w), dev(np.ones(k, np.float16)),
                           debug=True)
     acc = host(acc)
     assert (acc[:, 0::2] == 64 * d).all() and (acc[:, 1::2] == -56 * d).all()
-    # unit scales: y = fp16(acc); 524288 overflows fp16 -> inf
-    assert np.isinf(host(y)[:, 0]).all()
+    # unit scales: y = fp16(acc); 64 d >= 524288 overflows fp16 -> inf
+    assert np.isinf(host(y)[:, 0]).all() and (host(y)[:, 1] < 0).all()
+    # the launch the benchmark times gives the same y
+    y2, _ = rq.w4a4_gemm(dev(a), dev(np.ones(m, np.float16)), dev(w), dev(np.ones(k, np.float16)))
+    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
 
 
 def test_decode_linear_end_to_end(rq):
