@@ -168,13 +168,14 @@ def test_w4a4_gemm_asym_random_codes(rq, m, k, d):
         assert np.array_equal(y2.host().view(np.uint16), yo.host().view(np.uint16))
 
 
-def test_w4a4_gemm_asym_closed_form(rq):
-    m, k, d = 3, 40, 16384
+# decode and prefill kernels, up to d = 32768 (RQ_MAX_D)
+@pytest.mark.parametrize("m,k,d", [(3, 40, 16384), (3, 40, 32768), (256, 224, 32768)])
+def test_w4a4_gemm_asym_closed_form(rq, m, k, d):
     a = O._pack_uint4(np.full((m, d), 15))
     w = O.pack_int4(np.full((k, d), -8))
     w[1::2] = O.pack_int4(np.full((1, d), 7))
-    za = np.array([0, 15, 7], np.uint8)
-    say("w4a4 asym gemm closed form")
+    za = np.resize(np.array([0, 15, 7], np.uint8), m)
+    say(f"w4a4 asym gemm closed form m={m} k={k} d={d}")
     wsum = rq.weight_code_sums(dev(w))
     y, acc = rq.w4a4_gemm_asym(dev(a), dev(np.full(m, 2.0 ** -12, np.float16)), dev(za), dev(w),
                                dev(np.full(k, 2.0 ** -12, np.float16)), wsum, debug=True)

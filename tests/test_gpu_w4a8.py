@@ -151,19 +151,21 @@ def test_w4a8_gemm_random_codes(rq, m, k, d):
         assert np.array_equal(y2.host().view(np.uint16), yo.host().view(np.uint16))
 
 
-@pytest.mark.parametrize("m,k", [(3, 40), (64, 40), (256, 224)])
-def test_w4a8_gemm_closed_form_extremes(rq, m, k):
-    d = 16384
+# decode, tile and prefill kernels; d = 32768 (RQ_MAX_D) puts the MFMA sum at
+# 16 * 1024 * d = 2^29
+@pytest.mark.parametrize("m,k,d", [(3, 40, 16384), (64, 40, 16384), (256, 224, 16384),
+                                   (3, 40, 32768), (64, 40, 32768), (256, 224, 32768)])
+def test_w4a8_gemm_closed_form_extremes(rq, m, k, d):
     a = np.full((m, d), -128, np.int8)
     w = O.pack_int4(np.full((k, d), -8))
     w[1::2] = O.pack_int4(np.full((1, d), 7))
-    say(f"w4a8 gemm extremes m={m} k={k}")
+    say(f"w4a8 gemm extremes m={m} k={k} d={d}")
     y, acc = rq.w4a8_gemm(dev(a), dev(np.full(m, 2.0 ** -10, np.float16)), dev(w),
                           dev(np.full(k, 2.0 ** -10, np.float16)), debug=True)
     acc = host(acc)
     assert (acc[:, 0::2] == 1024 * d).all() and (acc[:, 1::2] == -896 * d).all()
     y = host(y).astype(np.float64)
-    assert (y[:, 0::2] == 16.0).all() and (y[:, 1::2] == -14.0).all()
+    assert (y[:, 0::2] == 1024 * d * 2.0 ** -20).all() and (y[:, 1::2] == -896 * d * 2.0 ** -20).all()
 
 
 def test_w4a8_decode_linear_end_to_end(rq):
