@@ -212,3 +212,24 @@ def test_grouped_prefill_full_size_sampled(rq):
     del yo
     check_gemm_grouped(ac, sa, wc[cols], wsg[cols], y[:, cols], "grouped prefill cols", gacc=g_cols)
     check_gemm_grouped(ac[rows], sa[rows], wc, wsg, y[rows], "grouped prefill rows", gacc=g_rows)
+
+
+# decode, tile and prefill kernels at d = 32768 (RQ_MAX_D, 256 groups)
+@pytest.mark.parametrize("m,k", [(3, 40), (64, 40), (256, 224)])
+def test_grouped_gemm_closed_form_extremes(rq, m, k):
+    d = 32768
+    a = O.pack_int4(np.full((m, d), -8))
+    w = O.pack_int4(np.full((k, d), -8))
+    w[1::2] = O.pack_int4(np.full((1, d), 7))
+    say(f"grouped gemm extremes m={m} k={k} d={d}")
+    sa = np.full(m, 2.0 ** -10, np.float16)
+    sw = np.full((k, d // 128), 2.0 ** -10, np.float16)
+    y, acc = rq.w4a4_gemm_grouped(dev(a), dev(sa), dev(w), dev(sw), debug=True)
+    acc = host(acc)
+    # every group's integer sum: 128 * 64 and 128 * -56
+    assert (acc[:, 0::2, :] == 64 * 128).all() and (acc[:, 1::2, :] == -56 * 128).all()
+    # y = sa * sum_g sw_g acc_g: powers of two, exact in fp32 and fp16
+    y = host(y).astype(np.float64)
+    assert (y[:, 0::2] == 64 * d * 2.0 ** -20).all() and (y[:, 1::2] == -56 * d * 2.0 ** -20).all()
+    y2 = host(rq.w4a4_gemm_grouped(dev(a), dev(sa), dev(w), dev(sw))).astype(np.float64)
+    assert np.array_equal(y2, y)
