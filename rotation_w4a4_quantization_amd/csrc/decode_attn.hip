@@ -136,7 +136,7 @@ __device__ __forceinline__ int qk_dim(int g, int t, int e) { return 32 * g + 8 *
 // bytes of codes each, row-major) and the 16 key then 16 value scales.
 constexpr int SLOT_K = 0, SLOT_V = AT * 64, SLOT_S = 2 * AT * 64;
 constexpr int SLOT = SLOT_S + 64;
-constexpr int NSLOT = 4;  // the tile in use and three in flight
+constexpr int NSLOT = 4;  // default ring depth: the tile in use and three in flight
 
 // The three DMA instructions of the tile at P into the slot at LDS address
 // slot: rows from p1 on re-read the split's last valid row (an L2 hit; their
@@ -203,18 +203,19 @@ __device__ __forceinline__ void finish_row(float o0, float o1, int lane,
 // sequence of its KV head (one split) and finishes the job itself: after the
 // merge of its wavefronts it normalises, rotates back and stores the output,
 // so no records and no combine kernel are needed.
-template <int GM, bool HAS_SIGNS, int NW = AW, bool FUSED = false>
+template <int GM, bool HAS_SIGNS, int NW = AW, bool FUSED = false, int NS = NSLOT>
 __global__ __launch_bounds__(64 * NW) void decode_attn_split_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
     const int32_t* __restrict__ lengths, int H, int G, int64_t S, int64_t chunk, float qscale,
     const int8_t* __restrict__ signs, float* __restrict__ part, uint16_t* __restrict__ out,
     float* __restrict__ out_f32) {
-  // ring[NW][NSLOT] tile slots, then the f16 value tiles; the queries rotate
+  // ring[NW][NS] tile slots (the tile in use and NS - 1 in flight), then the
+  // f16 value tiles; the queries rotate
   // in the value-tile space before the first tile, and after the tile loop
   // the per-wavefront records reuse the ring (FUSED: the merged records go to
   // the value-tile space)
-  constexpr int RING = NW * NSLOT * SLOT;
+  constexpr int RING = NW * NS * SLOT;
   constexpr int VT = NW * AT * VPITCH * 2;
   static_assert(NW * GM * PREC * 4 <= RING, "records fit in the ring");
   static_assert(GM * AD * 4 <= VT && GM * PREC * 4 <= VT, "queries fit in the value tiles");
@@ -257,13 +258,12 @@ __global__ __launch_bounds__(64 * NW) void decode_attn_split_kernel(
   const uint16_t* ksb = ks + bh * S;
   const uint16_t* vsb = vs + bh * S;
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem +
-                        (uint32_t)(wave * NSLOT * SLOT);
-  const unsigned char* ringp = smem + wave * NSLOT * SLOT;
+                        (uint32_t)(wave * NS * SLOT);
+  const unsigned char* ringp = smem + wave * NS * SLOT;
   constexpr int64_t kStep = AT * NW;
   const int64_t Pw = p0 + AT * wave;
-  issue_tile(ring, kb, vb, ksb, vsb, Pw, last, lane);
-  issue_tile(ring + SLOT, kb, vb, ksb, vsb, Pw + kStep, last, lane);
-  issue_tile(ring + 2 * SLOT, kb, vb, ksb, vsb, Pw + 2 * kStep, last, lane);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) issue_tile(ring + i * SLOT, kb, vb, ksb, vsb, Pw + i * kStep, last, lane);
 
   // ---- rotate the queries: (q * s) H_128 in LDS
   __syncthreads();
@@ -317,11 +317,13 @@ __global__ __launch_bounds__(64 * NW) void decode_attn_split_kernel(
   const int rpart = ring_part(r16, g);
   int slot = 0;
   for (int64_t P = Pw; P < p1; P += kStep) {
-    // the tile three steps ahead goes in flight, then this tile's loads are in
-    issue_tile(ring + ((slot + 3) & 3) * SLOT, kb, vb, ksb, vsb, P + 3 * kStep, last, lane);
-    RQA_WAIT_VM(9);
+    // the tile NS - 1 steps ahead goes in flight, then this tile's loads (three
+    // DMA instructions per tile) are in
+    issue_tile(ring + ((slot + NS - 1) % NS) * SLOT, kb, vb, ksb, vsb, P + (NS - 1) * kStep, last,
+               lane);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * (NS - 1)) : "memory");
     const unsigned char* sl = ringp + slot * SLOT;
-    slot = (slot + 1) & 3;
+    slot = (slot + 1) % NS;
     const int lim = (int)(p1 - P < AT ? p1 - P : AT);  // valid positions in the tile
 
     // keys and values: lane (position r16, group g) takes bytes 16g .. 16g + 15
@@ -524,10 +526,12 @@ void plan_splits(int64_t bh, int64_t S, int64_t* chunk, int* nsplit) {
   *nsplit = (int)((S + c - 1) / c);
 }
 
-// Wavefronts of the fused workgroup: three per SIMD, as many as the split
-// kernel's three 4-wavefront workgroups per CU (the LDS limit: 12 rings and
-// value tiles take 153 KB).
-constexpr int AW_FUSED = 12;
+// The fused workgroup: four wavefronts per SIMD, each with a two-slot ring
+// (the tile in use and one in flight); 16 rings and value tiles take 138 KB.
+// Twelve wavefronts with four-slot rings (153 KB) ran 43.8-44.4 us on the
+// 32 x 8 x 4096 cache against 41.3-42.1 us for this, and twelve with
+// two-slot rings 42.6-42.8 us.
+constexpr int AW_FUSED = 16, NS_FUSED = 2;
 
 template <int GM, bool HAS_SIGNS>
 void launch_split(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, const uint8_t* vc,
@@ -535,7 +539,7 @@ void launch_split(const uint16_t* q, const uint8_t* kc, const uint16_t* ks, cons
                   int64_t S, int64_t chunk, int nsplit, float qscale, const int8_t* signs,
                   float* part, bool fused, uint16_t* out, float* out_f32, hipStream_t stream) {
   if (fused)
-    hipLaunchKernelGGL((decode_attn_split_kernel<GM, HAS_SIGNS, AW_FUSED, true>),
+    hipLaunchKernelGGL((decode_attn_split_kernel<GM, HAS_SIGNS, AW_FUSED, true, NS_FUSED>),
                        dim3(1u, (unsigned)(B * H)), dim3(64 * AW_FUSED), 0, stream,
                        reinterpret_cast<const __half*>(q), kc, ks, vc, vs, lengths, (int)H, G, S, S,
                        qscale, signs, part, out, out_f32);
