@@ -170,6 +170,51 @@ int rq_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                  void* stream);
 
 /*
+ * rq_pack_f6 -- repack INT4 codes into F6 rows: fp6 E3M2 containers in the
+ * operand layout of the 6-bit MFMA, for rq_w4a4_gemm_f6.
+ *
+ * [RQ] "Hardware Execution and Serving Economics", part 1 (INT4 matrix
+ * arithmetic at twice the 8-bit throughput).  gfx950 has no INT4 MFMA, but
+ * every code -8..7 is exactly an OCP MX E3M2 value, and its 6-bit MFMA runs
+ * faster than the int8 one.  The layout is group-major: the 128-code group
+ * c of row r is the 96 bytes at (c * rows + r) * 96; its 32-code block b is a
+ * 192-bit little-endian word with code j (of the block) in bits 6j..6j+5,
+ * whose bytes 0..15 sit at group byte 16b and bytes 16..23 at group byte
+ * 64 + 16 * (b % 2) + 8 * (b / 2).  The E3M2 code of q is sign (bit 5)
+ * with |q| = 0, 1, 2, 3, 4, 5, 6, 7, 8 -> 0x00, 0x0C, 0x10, 0x12, 0x14,
+ * 0x15, 0x16, 0x17, 0x18.
+ *
+ *   codes    [rows][d/2] uint8 packed INT4 (code i in nibble i), 16-byte
+ *            aligned.
+ *   rows     >= 0.
+ *   d        codes per row, a multiple of 128 in [128, RQ_MAX_D].
+ *   out      [d/128][rows][96] uint8, 16-byte aligned, caller-owned.
+ */
+int rq_pack_f6(const uint8_t* codes, int64_t rows, int64_t d, uint8_t* out, void* stream);
+
+/*
+ * rq_w4a4_gemm_f6 -- rq_w4a4_gemm on F6 rows of both operands, multiplied on
+ * v_mfma_f32_16x16x128_f8f6f4.  The fp32 accumulators hold the integer
+ * accumulator exactly (products <= 64 in magnitude, sums < 2^24 for
+ * d <= RQ_MAX_D), so y and acc equal rq_w4a4_gemm's on the same codes bit
+ * for bit; the epilogue is the same.  One persistent workgroup per CU walks
+ * 256 x 224 (or 256 x 256) output tiles.
+ *
+ *   a_f6     [d/128][m][96] rq_pack_f6 of the activation codes, 16-byte aligned;
+ *            a_scales [m] fp16.
+ *   m        tokens, >= 0.
+ *   w_f6     [d/128][k][96] rq_pack_f6 of the weight codes, 16-byte aligned;
+ *            w_scales [k] fp16.
+ *   k        output channels, >= 1 when m > 0.
+ *   d        reduction length, a multiple of 128 in [128, RQ_MAX_D].
+ *   y        [m][k] fp16 output.
+ *   acc      optional [m][k] int32 output of the accumulators (debug), or NULL.
+ */
+int rq_w4a4_gemm_f6(const uint8_t* a_f6, const uint16_t* a_scales, int64_t m, const uint8_t* w_f6,
+                    const uint16_t* w_scales, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
+                    void* stream);
+
+/*
  * rq_kv_rotate_quant -- per-head rotation and INT4 packing of K and V.
  *
  * [QuaRot] "The architecture: every piece explained" (KV-cache rotation) and

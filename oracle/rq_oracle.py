@@ -330,6 +330,63 @@ def unpack_int4(codes: np.ndarray) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------- F6 layout
+# [RQ] "Hardware Execution and Serving Economics", part 1: the INT4 codes of a
+# W4A4 layer feed a 4-bit integer matrix product.  The F6 layout carries the
+# same integer codes in 6-bit OCP MX E3M2 floats, so that the product can run
+# on a 6-bit matrix unit; its values, and so every product and sum, are the
+# integers themselves.
+
+def e3m2_value(code: int) -> float:
+    """Value of a 6-bit E3M2 code (OCP Microscaling Formats v1.0): bit 5 is
+    the sign, bits 4..2 the exponent (bias 3), bits 1..0 the mantissa; the
+    exponent 0 encodes the subnormals (m / 4) * 2^(1 - 3).  No inf or NaN."""
+    code = int(code)
+    if not 0 <= code < 64:
+        raise ValueError("E3M2 codes have 6 bits")
+    sign = -1.0 if code & 0x20 else 1.0
+    e, mant = (code >> 2) & 7, code & 3
+    if e == 0:
+        return sign * (mant / 4.0) * 2.0 ** (1 - 3)
+    return sign * (1.0 + mant / 4.0) * 2.0 ** (e - 3)
+
+
+def e3m2_code(q: int) -> int:
+    """The E3M2 code whose value is the integer q, found by value among all 64
+    codes (zero takes the positive code); raises if q is not representable."""
+    hits = [c for c in range(64) if e3m2_value(c) == q and not (q == 0 and c & 0x20)]
+    if len(hits) != 1:
+        raise ValueError(f"{q} is not an E3M2 value")
+    return hits[0]
+
+
+def pack_f6(codes: np.ndarray) -> np.ndarray:
+    """rq_pack_f6: packed INT4 codes [rows][d/2] -> F6 layout [d/128][rows][96].
+
+    Block b (0..3) of the 128-code group c of a row holds the codes
+    128 c + 32 b + j, j = 0..31, as one 192-bit little-endian word with the
+    E3M2 code of code j in bits 6j..6j+5.  Word bytes 0..15 go to group bytes
+    16b..16b+15, bytes 16..23 to group bytes 64 + 16 (b % 2) + 8 (b // 2).
+    The layout is group-major: group c of row r is out[c, r]."""
+    q = unpack_int4(codes).astype(np.int64)
+    rows, d = q.shape
+    if d % 128:
+        raise ValueError("the F6 layout needs d % 128 == 0")
+    lut = np.array([e3m2_code(v) for v in range(-8, 8)], dtype=np.uint64)
+    e6 = lut[q + 8]                                     # [rows][d] E3M2 codes
+    blocks = e6.reshape(rows, d // 32, 32)
+    bits = ((blocks[..., :, None] >> np.arange(6, dtype=np.uint64)) & 1).astype(np.uint8)
+    words = np.packbits(bits.reshape(rows, d // 32, 192), axis=-1, bitorder="little")  # 24 bytes
+    out = np.zeros((d // 128, rows, 96), dtype=np.uint8)
+    for c in range(d // 128):
+        for b in range(4):
+            w = words[:, 4 * c + b, :]
+            out[c, :, 16 * b:16 * b + 16] = w[:, :16]
+            t = 64 + 16 * (b % 2) + 8 * (b // 2)
+            out[c, :, t:t + 8] = w[:, 16:]
+    return out
+
+
 def dequantize(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """q * scale in float64 (the value a code stands for)."""
     return np.asarray(q).astype(np.float64) * np.asarray(scales).astype(np.float64)[..., None]

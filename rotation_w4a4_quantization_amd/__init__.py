@@ -27,6 +27,8 @@ from .binding import (  # noqa: F401
     version,
     weight_code_sums,
     w4a4_gemm,
+    pack_f6,
+    w4a4_gemm_f6,
     w4a4_gemm_asym,
     w4a4_gemm_grouped,
     w4a4_linear,

@@ -24,6 +24,8 @@ EXPORTED = (
     "rq_fold_weights",
     "rq_w4a4_gemm_workspace_size",
     "rq_w4a4_gemm",
+    "rq_pack_f6",
+    "rq_w4a4_gemm_f6",
     "rq_kv_rotate_quant",
     "rq_linear_decode_workspace_size",
     "rq_linear_decode",
@@ -70,6 +72,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rq_w4a4_gemm_workspace_size.restype = sz
     lib.rq_w4a4_gemm.argtypes = [p, p, i64, p, p, i64, i64, p, p, p, sz, p]
     lib.rq_w4a4_gemm.restype = i32
+    lib.rq_pack_f6.argtypes = [p, i64, i64, p, p]
+    lib.rq_pack_f6.restype = i32
+    lib.rq_w4a4_gemm_f6.argtypes = [p, p, i64, p, p, i64, i64, p, p, p]
+    lib.rq_w4a4_gemm_f6.restype = i32
     lib.rq_kv_rotate_quant.argtypes = [p, p, i64, i64, p, p, p, p, p, p]
     lib.rq_kv_rotate_quant.restype = i32
     lib.rq_linear_decode_workspace_size.argtypes = [i64, i64]
@@ -244,6 +250,50 @@ def w4a4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
     st = lib.rq_w4a4_gemm(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes), _ptr(w_scales), k, d,
                           _ptr(y), _ptr(acc), _ptr(ws), ws_bytes, _stream())
     _check("rq_w4a4_gemm", st)
+    return y, acc
+
+
+def pack_f6(codes: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """rq_pack_f6: packed INT4 codes uint8 [rows, d/2] -> F6 layout uint8
+    [d/128, rows, 96] (fp6 E3M2 containers in the 6-bit MFMA operand layout,
+    group-major)."""
+    _need_cuda("codes", codes)
+    if codes.dtype != torch.uint8 or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D uint8 tensor")
+    rows, half_d = codes.shape
+    d = 2 * half_d
+    o = _out("out", out, (d // 128, rows, 96), torch.uint8, codes.device)
+    _check("rq_pack_f6", load_library().rq_pack_f6(_ptr(codes), rows, d, _ptr(o), _stream()))
+    return o
+
+
+def w4a4_gemm_f6(a_f6: torch.Tensor, a_scales: torch.Tensor, w_f6: torch.Tensor,
+                 w_scales: torch.Tensor, debug: bool = False, out: torch.Tensor | None = None,
+                 acc_out: torch.Tensor | None = None):
+    """rq_w4a4_gemm_f6 on the F6 layouts [d/128, m, 96] and [d/128, k, 96]:
+    returns (y fp16 [m, k], acc int32 [m, k] or None), equal to w4a4_gemm on
+    the same codes."""
+    for name, t in (("a_f6", a_f6), ("a_scales", a_scales), ("w_f6", w_f6),
+                    ("w_scales", w_scales)):
+        _need_cuda(name, t)
+    if a_f6.dtype != torch.uint8 or w_f6.dtype != torch.uint8:
+        raise ValueError("F6 rows must be uint8")
+    if a_scales.dtype != torch.float16 or w_scales.dtype != torch.float16:
+        raise ValueError("scales must be float16")
+    if a_f6.dim() != 3 or w_f6.dim() != 3 or a_f6.shape[2] != 96 or w_f6.shape[2] != 96:
+        raise ValueError("F6 layouts must be [d/128, rows, 96]")
+    groups, m, _ = a_f6.shape
+    groups2, k, _ = w_f6.shape
+    if groups != groups2:
+        raise ValueError("activation and weight F6 layouts differ in d")
+    if a_scales.numel() != m or w_scales.numel() != k:
+        raise ValueError("scale counts do not match the rows")
+    d = 128 * groups
+    y = _out("out", out, (m, k), torch.float16, a_f6.device)
+    acc = _out("acc_out", acc_out, (m, k), torch.int32, a_f6.device) if debug else None
+    st = load_library().rq_w4a4_gemm_f6(_ptr(a_f6), _ptr(a_scales), m, _ptr(w_f6),
+                                        _ptr(w_scales), k, d, _ptr(y), _ptr(acc), _stream())
+    _check("rq_w4a4_gemm_f6", st)
     return y, acc
 
 

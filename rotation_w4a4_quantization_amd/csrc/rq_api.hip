@@ -122,6 +122,30 @@ int rq_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, int64_t m,
                                        static_cast<hipStream_t>(stream)));
 }
 
+int rq_pack_f6(const uint8_t* codes, int64_t rows, int64_t d, uint8_t* out, void* stream) {
+  if (rows < 0 || rows >= kMaxRows || d < 128 || d > RQ_MAX_D || d % 128 != 0) return RQ_ERR_SHAPE;
+  if (rows == 0) return RQ_OK;
+  if (codes == nullptr || out == nullptr) return RQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(out)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_pack_f6(codes, rows, d, out, static_cast<hipStream_t>(stream)));
+}
+
+int rq_w4a4_gemm_f6(const uint8_t* a_f6, const uint16_t* a_scales, int64_t m, const uint8_t* w_f6,
+                    const uint16_t* w_scales, int64_t k, int64_t d, uint16_t* y, int32_t* acc,
+                    void* stream) {
+  if (m < 0 || k < 0 || d < 128 || d > RQ_MAX_D || d % 128 != 0) return RQ_ERR_SHAPE;
+  if (m > kMaxTileRows) return RQ_ERR_SHAPE;
+  if (k >= kMaxRows) return RQ_ERR_SHAPE;
+  if (m == 0) return RQ_OK;
+  if (k == 0) return RQ_ERR_SHAPE;
+  if (a_f6 == nullptr || a_scales == nullptr || w_f6 == nullptr || w_scales == nullptr ||
+      y == nullptr)
+    return RQ_ERR_NULL;
+  if (!aligned16(a_f6) || !aligned16(w_f6)) return RQ_ERR_ALIGN;
+  return from_hip(rq::launch_w4a4_gemm_f6(a_f6, a_scales, m, w_f6, w_scales, k, d, y, acc,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int rq_kv_rotate_quant(const uint16_t* k_in, const uint16_t* v_in, int64_t rows, int64_t head_dim,
                        const int8_t* signs, uint8_t* k_codes, uint16_t* k_scales,
                        uint8_t* v_codes, uint16_t* v_scales, void* stream) {

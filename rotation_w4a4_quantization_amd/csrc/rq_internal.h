@@ -37,6 +37,15 @@ hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint16_t* a_scales, in
                             const uint8_t* w_codes, const uint16_t* w_scales, int64_t k, int64_t d,
                             uint16_t* y, int32_t* acc, hipStream_t stream);
 
+// INT4 codes [rows][d/2] -> F6 rows [rows][3d/4] (fp6 E3M2 containers in
+// the operand layout of the 6-bit MFMA; d % 128 == 0), and the W4A4 GEMM on
+// F6 rows of both operands (same results as launch_w4a4_gemm).
+hipError_t launch_pack_f6(const uint8_t* codes, int64_t rows, int64_t d, uint8_t* out,
+                          hipStream_t stream);
+hipError_t launch_w4a4_gemm_f6(const uint8_t* a6, const uint16_t* a_scales, int64_t m,
+                               const uint8_t* w6, const uint16_t* w_scales, int64_t k, int64_t d,
+                               uint16_t* y, int32_t* acc, hipStream_t stream);
+
 // W4A8: y[m][k] = fp16(acc * sa * sw), acc = qa . qw over d with INT8
 // activation codes qa ([m][d] bytes) and packed INT4 weight codes.
 hipError_t launch_w4a8_gemm(const int8_t* a_codes8, const uint16_t* a_scales, int64_t m,

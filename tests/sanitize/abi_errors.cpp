@@ -116,6 +116,13 @@ int main() {
                              p<uint8_t>(A16), p<uint16_t>(A16b), p<int32_t>(A16b), k, d,
                              p<uint16_t>(A16b), nullptr, nullptr);
   };
+  auto gemm6 = [](int64_t m, int64_t k, int64_t d) {
+    return rq_w4a4_gemm_f6(p<uint8_t>(A16), p<uint16_t>(A16b), m, p<uint8_t>(A16),
+                           p<uint16_t>(A16b), k, d, p<uint16_t>(A16b), nullptr, nullptr);
+  };
+  auto pack6 = [](int64_t rows, int64_t d) {
+    return rq_pack_f6(p<uint8_t>(A16), rows, d, p<uint8_t>(A16b), nullptr);
+  };
   auto gemmg = [](int64_t m, int64_t k, int64_t d) {
     return rq_w4a4_gemm_grouped(p<uint8_t>(A16), p<uint16_t>(A16b), m, p<uint8_t>(A16),
                                 p<uint16_t>(A16b), k, d, p<uint16_t>(A16b), nullptr, nullptr);
@@ -140,6 +147,11 @@ int main() {
     CHECK(gemma(e, 64, 4096), RQ_ERR_SHAPE);
     CHECK(gemma(4, e, 4096), RQ_ERR_SHAPE);
     CHECK(gemma(4, 64, e), RQ_ERR_SHAPE);
+    CHECK(gemm6(e, 64, 4096), RQ_ERR_SHAPE);
+    CHECK(gemm6(4, e, 4096), RQ_ERR_SHAPE);
+    CHECK(gemm6(4, 64, e), RQ_ERR_SHAPE);
+    CHECK(pack6(e, 4096), RQ_ERR_SHAPE);
+    CHECK(pack6(4, e), RQ_ERR_SHAPE);
     CHECK(gemmg(e, 64, 4096), RQ_ERR_SHAPE);
     CHECK(gemmg(4, e, 4096), RQ_ERR_SHAPE);
     CHECK(gemmg(4, 64, e), RQ_ERR_SHAPE);
@@ -156,6 +168,13 @@ int main() {
           RQ_ERR_SHAPE);
   }
   CHECK(gemm8(4, 64, 96), RQ_ERR_SHAPE);
+  CHECK(gemm6(4, 64, 192), RQ_ERR_SHAPE);
+  CHECK(gemm6(4, 0, 4096), RQ_ERR_SHAPE);
+  CHECK(gemm6(0, 64, 4096), RQ_OK);
+  CHECK(pack6(0, 4096), RQ_OK);
+  CHECK(pack6(4, 4160), RQ_ERR_SHAPE);
+  CHECK(rq_pack_f6(p<uint8_t>(MIS), 4, 4096, p<uint8_t>(A16b), nullptr), RQ_ERR_ALIGN);
+  CHECK(rq_pack_f6(p<uint8_t>(A16), 4, 4096, nullptr, nullptr), RQ_ERR_NULL);
   CHECK(gemma(4, 0, 4096), RQ_ERR_SHAPE);
   CHECK(gemmg(4, 64, 192), RQ_ERR_SHAPE);
   CHECK(gemmg(0, 64, 4096), RQ_OK);

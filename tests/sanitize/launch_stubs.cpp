@@ -31,6 +31,10 @@ hipError_t launch_kv_rotate_quant(const uint16_t*, const uint16_t*, int64_t, con
 hipError_t launch_w4a4_gemm(const uint8_t*, const uint16_t*, int64_t, const uint8_t*,
                             const uint16_t*, int64_t, int64_t, uint16_t*, int32_t*, hipStream_t)
     RQ_STUB_LAUNCH
+hipError_t launch_pack_f6(const uint8_t*, int64_t, int64_t, uint8_t*, hipStream_t) RQ_STUB_LAUNCH
+hipError_t launch_w4a4_gemm_f6(const uint8_t*, const uint16_t*, int64_t, const uint8_t*,
+                               const uint16_t*, int64_t, int64_t, uint16_t*, int32_t*, hipStream_t)
+    RQ_STUB_LAUNCH
 hipError_t launch_w4a8_gemm(const int8_t*, const uint16_t*, int64_t, const uint8_t*,
                             const uint16_t*, int64_t, int64_t, uint16_t*, int32_t*, hipStream_t)
     RQ_STUB_LAUNCH

@@ -190,6 +190,36 @@ def test_w4a8_gemm_argument_errors(lib):
     assert call(w=MIS) == binding.RQ_ERR_ALIGN
 
 
+def test_f6_argument_errors(lib):
+    def gemm(a=A16, sa=A16b, m=4, w=A16, sw=A16b, k=64, d=4096, y=A16b, acc=None):
+        return lib.rq_w4a4_gemm_f6(a, sa, m, w, sw, k, d, y, acc, None)
+
+    assert gemm(m=0) == binding.RQ_OK
+    assert gemm(a=None) == binding.RQ_ERR_NULL
+    assert gemm(sw=None) == binding.RQ_ERR_NULL
+    assert gemm(y=None) == binding.RQ_ERR_NULL
+    assert gemm(d=64) == binding.RQ_ERR_SHAPE      # d % 128 != 0
+    assert gemm(d=4096 + 64) == binding.RQ_ERR_SHAPE
+    assert gemm(d=32768 + 128) == binding.RQ_ERR_SHAPE
+    assert gemm(k=0) == binding.RQ_ERR_SHAPE
+    assert gemm(m=-1) == binding.RQ_ERR_SHAPE
+    assert gemm(m=2 ** 63 - 1) == binding.RQ_ERR_SHAPE
+    assert gemm(a=MIS) == binding.RQ_ERR_ALIGN
+    assert gemm(w=MIS) == binding.RQ_ERR_ALIGN
+
+    def pack(c=A16, rows=4, d=4096, out=A16b):
+        return lib.rq_pack_f6(c, rows, d, out, None)
+
+    assert pack(rows=0) == binding.RQ_OK
+    assert pack(c=None) == binding.RQ_ERR_NULL
+    assert pack(out=None) == binding.RQ_ERR_NULL
+    assert pack(d=4096 + 64) == binding.RQ_ERR_SHAPE
+    assert pack(d=32768 + 128) == binding.RQ_ERR_SHAPE
+    assert pack(rows=-1) == binding.RQ_ERR_SHAPE
+    assert pack(rows=2 ** 31) == binding.RQ_ERR_SHAPE
+    assert pack(out=MIS) == binding.RQ_ERR_ALIGN
+
+
 def test_linear_decode_argument_errors(lib):
     need = lib.rq_linear_decode_workspace_size(4, 4096)
     assert need == 4 * 2048 + 64

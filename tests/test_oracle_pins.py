@@ -852,3 +852,52 @@ def test_rotated_int4_cache_attention_beats_unrotated():
     e_rot = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
     e_raw = np.linalg.norm(raw - ref) / np.linalg.norm(ref)
     assert e_rot < 0.5 * e_raw, (e_rot, e_raw)
+
+
+# ---------------------------------------------------------------- F6 layout
+# OCP Microscaling Formats (MX) v1.0, the FP6 E3M2 element format: exponent
+# bias 3, no inf or NaN; largest normal +-28.0 (0b0_111_11), smallest normal
+# +-0.25, largest subnormal +-0.1875, smallest subnormal +-0.0625.
+def test_e3m2_values_match_the_format_definition():
+    assert O.e3m2_value(0b011111) == 28.0 and O.e3m2_value(0b111111) == -28.0
+    assert O.e3m2_value(0b000100) == 0.25
+    assert O.e3m2_value(0b000011) == 0.1875
+    assert O.e3m2_value(0b000001) == 0.0625
+    assert O.e3m2_value(0b001100) == 1.0 and O.e3m2_value(0b101100) == -1.0
+    assert O.e3m2_value(0) == 0.0
+    values = sorted(O.e3m2_value(c) for c in range(64))
+    assert len(set(values)) == 63  # +0 and -0 compare equal; every other value once
+
+
+def test_every_int4_code_is_an_e3m2_value():
+    codes = {q: O.e3m2_code(q) for q in range(-8, 9)}
+    assert len(set(codes.values())) == 17
+    for q, c in codes.items():
+        assert O.e3m2_value(c) == q
+    for q in (9, 11, 13, 15, -9):  # 2 mantissa bits: 8, 10, 12, 14 only between 8 and 16
+        with pytest.raises(ValueError):
+            O.e3m2_code(q)
+
+
+def test_pack_f6_read_back_bit_by_bit():
+    # every code read back through the layout as it is described, with Python
+    # integers (not the packing's bit arrays), is the INT4 code itself
+    rng = np.random.default_rng(61)
+    rows, d = 5, 384
+    q = rng.integers(-8, 8, (rows, d))
+    out = O.pack_f6(O.pack_int4(q))
+    assert out.shape == (d // 128, rows, 96) and out.dtype == np.uint8
+    for r in range(rows):
+        for i in range(d):
+            c, b, j = i // 128, (i % 128) // 32, i % 32
+            grp = out[c, r]
+            tail = 64 + 16 * (b % 2) + 8 * (b // 2)
+            word = int.from_bytes(bytes(grp[16 * b:16 * b + 16]) + bytes(grp[tail:tail + 8]), "little")
+            assert O.e3m2_value((word >> (6 * j)) & 63) == q[r, i], (r, i)
+    # the 4 heads and 4 tails tile the 96 bytes of a group exactly once
+    cover = np.zeros(96, int)
+    for b in range(4):
+        cover[16 * b:16 * b + 16] += 1
+        t = 64 + 16 * (b % 2) + 8 * (b // 2)
+        cover[t:t + 8] += 1
+    assert (cover == 1).all()
