@@ -29,6 +29,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+FP6_PEAK_TOPS = 10100.0        # MI355X dense fp6 / fp4 MFMA, TFLOP/s
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 
 
@@ -423,7 +424,43 @@ def main():
             if want_line("linear_prefill_rotate_plus_gemm"):
                 msl = time_launches(torch, lin, 2, max(5, steps2 // 2), warm2)
                 sec["linear_prefill_rotate_plus_gemm"] = line(msl)
-            del wcs, wc, y
+
+            # the same GEMM on the 6-bit matrix unit: activation codes repacked
+            # into the F6 layout per call, weights repacked once (offline)
+            a6 = torch.empty((d // 128, mm, 96), dtype=torch.uint8, device=dev)
+            w6s = [rq.pack_f6(w_) for w_ in wcs]
+            del wcs, wc
+
+            def pk(i):
+                rq.pack_f6(ac, out=a6)
+
+            if want_line("pack_f6_2048x8192"):
+                msk = time_launches(torch, pk, 1, steps2, warm2)
+                b = mm * d // 2 + mm * d * 3 // 4
+                sec["pack_f6_2048x8192"] = line(msk, **{"GB/s": round(b / (msk * 1e-3) / 1e9, 1),
+                                           "hbm_frac": round(b / (msk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            pk(0)
+
+            def g6(i):
+                rq.w4a4_gemm_f6(a6, sa, w6s[i], ws, out=y)
+
+            if want_line("gemm_f6_prefill_2048x8192x28672"):
+                ms6 = time_launches(torch, g6, 2, max(5, steps2 // 2), warm2)
+                tops = 2 * mm * d * k / (ms6 * 1e-3) / 1e12
+                sec["gemm_f6_prefill_2048x8192x28672"] = line(
+                    ms6, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / FP6_PEAK_TOPS, 4),
+                            "vs_int8_peak": round(tops / INT8_PEAK_TOPS, 4)})
+                log(f"[bench] prefill gemm on fp6 MFMA: {sec['gemm_f6_prefill_2048x8192x28672']}")
+
+            def lin6(i):
+                f8(0)
+                rq.pack_f6(ac, out=a6)
+                rq.w4a4_gemm_f6(a6, sa, w6s[i], ws, out=y)
+
+            if want_line("linear_prefill_f6_rotate_pack_gemm"):
+                msl6 = time_launches(torch, lin6, 2, max(5, steps2 // 2), warm2)
+                sec["linear_prefill_f6_rotate_pack_gemm"] = line(msl6)
+            del w6s, a6, y
 
         if want("downproj"):
             # the online rotation in front of a down projection: 2048 tokens x
@@ -470,6 +507,20 @@ def main():
                     sec["gemm_downproj_2048x28672x8192"] = line(
                         msd, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
                     log(f"[bench] down projection gemm: {sec['gemm_downproj_2048x28672x8192']}")
+                    if want_line("gemm_f6_downproj_2048x28672x8192"):
+                        a6 = rq.pack_f6(ac28)
+                        w6s = [rq.pack_f6(w_) for w_ in wcs]
+
+                        def g6d(i, w6s=w6s, a6=a6, ws=ws, y=y, sa28=sa28):
+                            rq.w4a4_gemm_f6(a6, sa28, w6s[i], ws, out=y)
+
+                        ms6 = time_launches(torch, g6d, 2, max(5, steps2 // 2), warm2)
+                        tops = 2 * mm * d * k / (ms6 * 1e-3) / 1e12
+                        sec["gemm_f6_downproj_2048x28672x8192"] = line(
+                            ms6, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / FP6_PEAK_TOPS, 4),
+                                    "vs_int8_peak": round(tops / INT8_PEAK_TOPS, 4)})
+                        log(f"[bench] down projection on fp6 MFMA: {sec['gemm_f6_downproj_2048x28672x8192']}")
+                        del w6s, a6
                     del wcs, wc, y
                 del x28
 
@@ -777,6 +828,25 @@ def main():
                 mm_ = time_launches(torch, mf, 1, max(5, steps2 // 4), warm2)
                 tops = ops[0] / (mm_ * 1e-3) / 1e12
                 sec[name] = line(mm_, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4)})
+                log(f"[bench] {name}: {sec[name]}")
+                del outm
+            lib.rq_ceiling_mfma_f6.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_void_p]
+            lib.rq_ceiling_mfma_f6.restype = ctypes.c_int64
+            for wps in (2, 4):
+                name = f"fp6_mfma_loop_{wps}waves_per_simd"
+                if not want_line(name):
+                    continue
+                outm = torch.empty((int(lib.rq_ceiling_mfma_out_words(wps)),), dtype=torch.int32, device=dev)
+                ops = [0]
+
+                def mf6(i, outm=outm, wps=wps):
+                    ops[0] = lib.rq_ceiling_mfma_f6(_ptr(outm), wps, 2048, _stream())
+                    assert ops[0] > 0
+
+                mm_ = time_launches(torch, mf6, 1, max(5, steps2 // 4), warm2)
+                tops = ops[0] / (mm_ * 1e-3) / 1e12
+                sec[name] = line(mm_, **{"TOPS": round(tops, 1), "mfma_frac": round(tops / FP6_PEAK_TOPS, 4)})
                 log(f"[bench] {name}: {sec[name]}")
                 del outm
             # issue rates of the instruction classes the kernels are made of: does

@@ -52,6 +52,16 @@ size_t rq_ceiling_mfma_out_words(int64_t waves_per_simd);
  */
 int64_t rq_ceiling_mfma_i8(int32_t* out, int64_t waves_per_simd, int64_t iters, void* stream);
 
+/*
+ * The same loop on the 6-bit matrix unit: rounds of 8 independent
+ * v_mfma_f32_16x16x128_f8f6f4 with E3M2 operands holding random INT4 codes
+ * (the values rq_w4a4_gemm_f6 multiplies).  out takes
+ * rq_ceiling_mfma_out_words(waves_per_simd) int32 words.  Returns the
+ * operations issued (2 * 16 * 16 * 128 per MFMA), or a negative value on an
+ * error (-1 NULL, -2 bad size, -5 launch failure).
+ */
+int64_t rq_ceiling_mfma_f6(int32_t* out, int64_t waves_per_simd, int64_t iters, void* stream);
+
 /* Floats of `out` that rq_ceiling_issue writes for this occupancy. */
 size_t rq_ceiling_issue_out_words(int64_t waves_per_simd);
 

@@ -81,6 +81,54 @@ __global__ __launch_bounds__(256) void mfma_i8_loop_kernel(int32_t* __restrict__
   reinterpret_cast<v4i*>(out)[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The same loop on the 6-bit matrix unit: 8 independent
+// v_mfma_f32_16x16x128_f8f6f4 with E3M2 operands (format 3 for A and B),
+// each lane's six operand registers holding 32 random INT4 codes -8..7 as
+// E3M2 values (the operand values the F6 GEMM multiplies; the clock the
+// matrix unit holds depends on them).
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t loop_hash(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return x;
+}
+__global__ __launch_bounds__(256) void mfma_f6_loop_kernel(int32_t* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  // E3M2 codes of q = -8..7 (index q + 8)
+  constexpr unsigned char kE3M2[16] = {56, 55, 54, 53, 52, 50, 48, 44, 0, 12, 16, 18, 20, 21, 22, 23};
+  v6i a = {0, 0, 0, 0, 0, 0}, b = a;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t ca = kE3M2[loop_hash(lane * 977u + j * 131u + 17u) & 15u];
+    const uint32_t cb = kE3M2[loop_hash(lane * 977u + 62531u + j * 131u) & 15u];
+    const int pos = 6 * j;
+    a[pos >> 5] |= (int)(ca << (pos & 31));
+    b[pos >> 5] |= (int)(cb << (pos & 31));
+    if ((pos & 31) > 26) {
+      a[(pos >> 5) + 1] |= (int)(ca >> (32 - (pos & 31)));
+      b[(pos >> 5) + 1] |= (int)(cb >> (32 - (pos & 31)));
+    }
+  }
+  v4f c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile(
+        "v_mfma_f32_16x16x128_f8f6f4 %0, %8, %9, %0 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %1, %8, %9, %1 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %2, %8, %9, %2 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %3, %8, %9, %3 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %4, %8, %9, %4 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %5, %8, %9, %5 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %6, %8, %9, %6 cbsz:3 blgp:3\n"
+        "v_mfma_f32_16x16x128_f8f6f4 %7, %8, %9, %7 cbsz:3 blgp:3\n"
+        : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7)
+        : "v"(a), "v"(b));
+  }
+  // the results are read only after the last MFMA has written them
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+  const v4f s = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = (int32_t)(s[0] + s[1] + s[2] + s[3]);
+}
+
 // Issue-rate loops: each wavefront runs `iters` rounds of one block of
 // register-only instructions, independent of each other inside the round.
 //   KIND 0: 8 v_mfma_i32_16x16x64_i8 (eight accumulators);
@@ -215,6 +263,17 @@ int64_t rq_ceiling_mfma_i8(int32_t* out, int64_t waves_per_simd, int64_t iters, 
   if (hipGetLastError() != hipSuccess) return -5;
   // integer operations: 2 * 16 * 16 * 64 per MFMA, 8 MFMAs per round per wavefront
   return (int64_t)blocks * 4 * iters * 8 * (2 * 16 * 16 * 64);
+}
+
+int64_t rq_ceiling_mfma_f6(int32_t* out, int64_t waves_per_simd, int64_t iters, void* stream) {
+  if (out == nullptr) return -1;
+  if (waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 || iters > (1 << 24)) return -2;
+  const int blocks = rq::cu_count() * (int)waves_per_simd;  // 4 wavefronts per block
+  hipLaunchKernelGGL(mfma_f6_loop_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), out, (int)iters);
+  if (hipGetLastError() != hipSuccess) return -5;
+  // operations: 2 * 16 * 16 * 128 per MFMA, 8 MFMAs per round per wavefront
+  return (int64_t)blocks * 4 * iters * 8 * (2 * 16 * 16 * 128);
 }
 
 size_t rq_ceiling_issue_out_words(int64_t waves_per_simd) {

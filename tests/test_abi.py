@@ -54,6 +54,11 @@ def test_ceiling_probe_argument_errors(lib):
     assert lib.rq_ceiling_read(A16, 0, A16b, None) == 0
     assert lib.rq_ceiling_copy(A16, None, 16, None) == 1
     assert lib.rq_ceiling_copy(A16, MIS, 16, None) == 3
+    lib.rq_ceiling_mfma_f6.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    lib.rq_ceiling_mfma_f6.restype = ctypes.c_int64
+    assert lib.rq_ceiling_mfma_f6(None, 2, 10, None) == -1
+    assert lib.rq_ceiling_mfma_f6(A16, 0, 10, None) == -2
+    assert lib.rq_ceiling_mfma_f6(A16, 2, 0, None) == -2
     assert lib.rq_ceiling_mfma_i8(None, 2, 10, None) == -1
     assert lib.rq_ceiling_mfma_i8(A16, 9, 10, None) == -2
     assert lib.rq_ceiling_mfma_i8(A16, 2, 0, None) == -2
