@@ -351,6 +351,18 @@ def test_binding_rejects_cpu_tensors():
         binding.fwht_quant(torch.zeros(4, 16, dtype=torch.float16))
 
 
+def test_f6_binding_rejects_bad_inputs_before_launch():
+    # host tensors, wrong dtypes and F6 layouts that are not [d/128, rows, 96]
+    # raise ValueError on the host, before librq is called
+    import torch
+    with pytest.raises(ValueError):
+        binding.pack_f6(torch.zeros(4, 64, dtype=torch.uint8))
+    a6 = torch.zeros(2, 4, 96, dtype=torch.uint8)
+    s4 = torch.zeros(4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        binding.w4a4_gemm_f6(a6, s4, a6, s4)
+
+
 def test_binding_rejects_unfit_outputs_before_launch():
     """Caller-supplied outputs and workspaces are checked on the host: the
     wrong dtype, shape or layout, or a host tensor, raise ValueError (an
